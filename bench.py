@@ -1,0 +1,280 @@
+"""Benchmark of the ETA block-sparse decode step on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic batch resident in
+HBM: eta_predict_tau -> eta_screen -> eta_decode_attn (split-KV attention with
+the fused log-sum-exp combine). W untimed warm-up steps, then K timed steps
+between device synchronisations, timed with HIP events on the launch stream.
+Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from long_context_decode_predict_amd import _lib, calibrate, workloads  # noqa: E402
+from long_context_decode_predict_amd.build import ensure_built  # noqa: E402
+from long_context_decode_predict_amd.decode import DecodeStep  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "ETA decode steps/s and effective KV GB/s (% HBM peak), B=64 T=128K ~38% density"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def elem_bytes(dtype):
+    return 2 if dtype == torch.bfloat16 else 4
+
+
+def admitted_bytes(w, cnt, idx):
+    """Bytes of K and V of the admitted blocks (a partial last block counts its tokens)."""
+    eb = elem_bytes(w.kv_dtype)
+    nblk = w.nblk
+    last_tokens = w.T - (nblk - 1) * 64
+    full = int(cnt.sum()) * 64
+    if last_tokens != 64:
+        cntf = cnt.reshape(-1)
+        idxf = idx.reshape(cntf.shape[0], -1)
+        has_last = sum(int(idxf[u, c - 1] == nblk - 1) for u, c in enumerate(cntf) if c > 0)
+        full -= has_last * (64 - last_tokens)
+    return 2 * full * w.d * eb
+
+
+def meta_bytes(w):
+    return w.B * w.H * w.nblk * (w.d + 2) * 4
+
+
+def run_steps(step, data, w, meta, W, bias, n, stream, ev_pairs=None):
+    q, K, V = data["q"], data["K"], data["V"]
+    for i in range(n):
+        if ev_pairs is not None:
+            ev_pairs[i][0].record(stream)
+        step.predict(q, W, bias)
+        step.screen(q, meta, w.T)
+        if ev_pairs is not None:
+            ev_pairs[i][1].record(stream)
+        step.attend(q, K, V, w.T)
+        if ev_pairs is not None:
+            ev_pairs[i][2].record(stream)
+
+
+def time_steps(step, data, w, meta, W, bias, steps, warmup):
+    stream = torch.cuda.current_stream()
+    run_steps(step, data, w, meta, W, bias, warmup, stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    run_steps(step, data, w, meta, W, bias, steps, stream, evs)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    front_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    return total_ms / steps, float(np.mean(attn_ms)), float(np.mean(front_ms)), attn_ms
+
+
+def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=None):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload, timed on
+    the host cores: predictor + bound + screen + gated attention for the sampled units,
+    given metadata it built beforehand; scaled to steps/s of the whole workload."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as oracle_mod
+
+    O = oracle_mod.default()
+    units_total = w.B * w.H
+    n = min(max_units, units_total)
+    rng = np.random.default_rng(w.seed + 99)
+    units = np.sort(rng.choice(units_total, size=n, replace=False))
+    q = data["q"].cpu().numpy()
+    Wn = None if W is None else W.cpu().numpy()
+    bn = bias.cpu().numpy()
+
+    def host(t):
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.contiguous().cpu().numpy()
+
+    slabs = []
+    for u in units:
+        b, h = divmod(int(u), w.H)
+        slabs.append((b, h, host(data["K"][b, h, :w.T]), host(data["V"][b, h, :w.T])))
+    threads = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(threads) as ex:
+        metas = list(ex.map(lambda s: O.block_meta(s[2], w.T), slabs))
+        rows = sorted({s[0] for s in slabs})
+        taus = {}
+
+        def work(i):
+            b, h, Kh, Vh = slabs[i]
+            tau = taus[b][h]
+            r = O.unit_step(q[b, h], Kh, Vh, w.T, tau, metas[i], z=params.z,
+                            mode=params.bound_mode, beta=params.gate_beta,
+                            hard=bool(params.gate_hard))
+            return len(r["idx"])
+
+        t0 = time.perf_counter()
+        for b in rows:  # Eq. 1 once per sampled batch row
+            taus[b] = O.predict_tau(q[b:b + 1], Wn, bn)[0]
+        list(ex.map(work, range(n)))
+        dt = time.perf_counter() - t0
+    step_s = dt * units_total / n
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {units_total} (batch, head) units of the same workload, "
+                      f"{dt:.2f} s wall on {threads} threads, scaled by {units_total}/{n}",
+            "gpu_over_cpu": (1000.0 / step_gpu_ms) * step_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=list(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--split", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the step is data-parallel over (batch, head) units; see DESIGN.md for how it "
+              "would shard)", file=sys.stderr)
+        sys.exit(2)
+    ensure_built()
+    torch.cuda.set_device(0)
+    w = workloads.WORKLOADS[args.workload]
+    params = _lib.default_params(split_blocks=args.split)
+
+    log(f"[bench] generating {w.name}: B={w.B} H={w.H} d={w.d} T={w.T} {w.kv_dtype}")
+    t0 = time.time()
+    data = workloads.generate(w, "cuda")
+    W = data["W"]
+    bias = calibrate.bias_for(w, data["q"], W, z=params.z)
+    torch.cuda.synchronize()
+    log(f"[bench] generated in {time.time() - t0:.1f}s")
+
+    meta = _lib.Meta.alloc(w.B, w.H, w.d, w.T_cap)
+    append_ms = None
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if w.append:
+        T0 = w.T - w.append
+        _lib.eta_build_block_meta(data["K"], T0, meta)
+        ev0.record()
+        for t in range(T0, w.T):
+            _lib.eta_append_meta(data["K"], t, 1, meta)
+        ev1.record()
+        torch.cuda.synchronize()
+        append_ms = ev0.elapsed_time(ev1) / w.append
+    ev0.record()
+    _lib.eta_build_block_meta(data["K"], w.T, meta)
+    ev1.record()
+    torch.cuda.synchronize()
+    build_ms = ev0.elapsed_time(ev1)
+    log(f"[bench] metadata build {build_ms:.2f} ms")
+
+    step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params)
+    ms, attn_ms, front_ms, attn_all = time_steps(step, data, w, meta, W, bias, args.steps,
+                                                 args.warmup)
+    cnt = step.adm_cnt.cpu().numpy()
+    idx = step.adm_idx.cpu().numpy()
+    density = float(cnt.mean()) / w.nblk
+    kv_adm = admitted_bytes(w, cnt, idx)
+    mb = meta_bytes(w)
+    eff_gbs = (kv_adm + mb) / (ms * 1e-3) / 1e9
+    units = w.B * w.H
+    attn_alg = kv_adm + int(cnt.sum()) * 4 + units * w.d * 4 * 2 + units * 8
+    attn_gbs = attn_alg / (attn_ms * 1e-3) / 1e9
+    log(f"[bench] {ms:.3f} ms/step, density {density:.3f}, attention {attn_ms:.3f} ms "
+        f"({attn_gbs:.0f} GB/s), predict+screen {front_ms:.3f} ms, effective {eff_gbs:.0f} GB/s")
+
+    extra = {"density": density, "effective_kv_gbs": eff_gbs,
+             "effective_frac_hbm_peak": eff_gbs / HBM_PEAK_GBS,
+             "admitted_kv_bytes": kv_adm, "metadata_bytes": mb,
+             "attn_ms": attn_ms, "predict_screen_ms": front_ms, "meta_build_ms": build_ms}
+    if append_ms is not None:
+        extra["append_ms_per_token"] = append_ms
+    per_head = (cnt / w.nblk).mean(axis=0)
+    extra["per_head_density_min_max"] = [float(per_head.min()), float(per_head.max())]
+    union = None
+    if w.H > 1:
+        # union over heads of a batch row (reported, not a traffic figure under MHA)
+        nb = w.nblk
+        un = []
+        for b in range(w.B):
+            s = set()
+            for h in range(w.H):
+                s.update(idx[b, h, :cnt[b, h]].tolist())
+            un.append(len(s) / nb)
+        union = float(np.mean(un))
+        extra["union_density"] = union
+    if data["needles"] is not None:
+        nd = data["needles"].cpu().numpy()
+        hit = 0
+        for u, blk, _ in nd:
+            b, h = divmod(int(u), w.H)
+            hit += int(np.isin(blk, idx[b, h, :cnt[b, h]]))
+        extra["needle_block_recall"] = hit / len(nd)
+
+    if not args.no_dense:
+        dense_bias = torch.full((w.H,), -math.inf, device="cuda")
+        dms, dattn, _, _ = time_steps(step, data, w, meta, None, dense_bias,
+                                      max(5, args.steps // 2), 2)
+        dcnt = step.adm_cnt.cpu().numpy()
+        d_bytes = admitted_bytes(w, dcnt, step.adm_idx.cpu().numpy())
+        extra["dense_tau_neg_inf"] = {
+            "ms_per_step": dms, "steps_per_s": 1000.0 / dms,
+            "effective_kv_gbs": (d_bytes + mb) / (dms * 1e-3) / 1e9,
+            "attn_gbs": (d_bytes + units * w.d * 8) / (dattn * 1e-3) / 1e9,
+            "sparse_speedup": dms / ms}
+        log(f"[bench] dense reference {dms:.3f} ms/step")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on host cores)")
+        cpu = cpu_baseline(w, data, W, bias, ms, params)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} steps/s ({cpu['sample']})")
+
+    result = {
+        "metric": METRIC,
+        "value": 1000.0 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded clustered keys; see DESIGN.md)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "T": w.T,
+                   "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
+                   "block": 64, "target_density": w.density if not w.static_tau else "per-head",
+                   "split_blocks": params.split_blocks or 16, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "eta_decode_attn", "achieved": attn_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": attn_alg, "avg_launch_ms": attn_ms},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

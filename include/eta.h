@@ -1,0 +1,188 @@
+/*
+ * eta.h -- C ABI of the Elastic Threshold Attention (ETA) block-sparse decode
+ * step for AMD Instinct MI355X (gfx950).
+ *
+ * Method: arXiv:2609.20888, "Elastic Threshold Attention: Learned Contextual
+ * Sparsity for Long-Context Decoding". One decode step, per (batch, head) unit:
+ *   1. predict a threshold tau from the post-RoPE query (review "Methodology
+ *      Assessment", Eq. 1), or use frozen per-head constants (abstract: offline
+ *      calibration);
+ *   2. screen every 64-token KV block in O(1) against tau with a bound built
+ *      from cached per-block metadata (abstract: "geometric-probabilistic
+ *      bounds"; review "Summary": centroid / variance / max-norm);
+ *   3. skip every block whose bound is below tau (review Q&A "What is ETA?");
+ *   4. softmax attention over the admitted blocks' tokens, each logit S
+ *      multiplied by the gate sigmoid(beta*(S - tau)) (Eq. 2 and Eq. 3), so a
+ *      sub-threshold logit tends to 0, not to -inf.
+ *
+ * Conventions shared by every call
+ *   - All tensors are device pointers in HBM, row-major, densely packed, owned
+ *     and allocated by the caller. The library never allocates, frees or
+ *     synchronises; a call validates its arguments on the host and then only
+ *     enqueues kernels on `stream` (0 = the null stream).
+ *   - Argument errors are returned before anything is enqueued. A failed
+ *     launch returns ETA_ERR_HIP. No C++ exception crosses this boundary.
+ *   - The library holds no global mutable state; calls on different streams
+ *     with disjoint outputs may run concurrently.
+ *   - Multi-head attention only: one K/V head per query head.
+ *   - Layouts (unit u = b*H + h):
+ *       q         float32 [B][H][d]        post-RoPE query (RoPE is the caller's)
+ *       K, V      [B][H][T_cap][d]         float32 or bfloat16 (kv_dtype)
+ *       tau       float32 [B][H]
+ *       centroid  float32 [B][H][d][nblk_cap]   dimension-major per unit
+ *       var       float32 [B][H][nblk_cap]
+ *       maxnorm   float32 [B][H][nblk_cap]
+ *       adm_idx   int32   [B][H][nblk_cap]      ascending admitted block ids
+ *       adm_cnt   int32   [B][H]
+ *       out       float32 [B][H][d],  lse float32 [B][H]
+ *     where nblk_cap = eta_nblk_cap(T_cap) = ceil(T_cap/64) rounded up to a
+ *     multiple of 4.
+ *   - Block beta of a unit covers tokens [64*beta, min(T, 64*beta + 64)); the
+ *     last block may be partial. Tokens at or beyond T are never read.
+ */
+#ifndef ETA_H
+#define ETA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ETA_OK = 0,
+    ETA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned buffer */
+    ETA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, block != 64, bad dtype */
+    ETA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    ETA_ERR_HIP = -4          /* a kernel launch failed */
+} eta_status;
+
+typedef enum { ETA_F32 = 0, ETA_BF16 = 1 } eta_dtype;
+
+/* Bound used by the screen (see eta_screen). */
+typedef enum { ETA_BOUND_COMBINED = 0, ETA_BOUND_GEO = 1 } eta_bound_mode;
+
+typedef struct {
+    int B, H;           /* batch rows and heads (MHA)                          */
+    int d;              /* head dimension: 64 or 128                           */
+    int T;              /* tokens present in the cache (0 <= T <= T_cap)       */
+    int T_cap;          /* token capacity of the K/V layout (>= 1)             */
+    int block;          /* tokens per KV block: must be 64                     */
+    eta_dtype kv_dtype; /* element type of K and V                             */
+} eta_shape;
+
+typedef struct {
+    float *centroid;    /* [B][H][d][nblk_cap]                                 */
+    float *var;         /* [B][H][nblk_cap]                                    */
+    float *maxnorm;     /* [B][H][nblk_cap]                                    */
+    int nblk_cap;       /* must equal eta_nblk_cap(T_cap); the three pointers
+                           are 16-byte aligned                                 */
+} eta_meta;
+
+typedef struct {
+    float gate_beta;    /* gate sharpness beta of Eq. 2 (> 0); default 5       */
+    float z;            /* standard deviations in the probabilistic bound
+                           (>= 0, finite); default 4                           */
+    int gate_hard;      /* 1: gate is the step S >= tau instead of the sigmoid */
+    int bound_mode;     /* eta_bound_mode; default ETA_BOUND_COMBINED          */
+    int split_blocks;   /* admitted blocks per split-KV work item (1..4096);
+                           0 = library default (16)                            */
+} eta_params;
+
+/* Defaults: beta = 5 (the end of the 1 -> 5 anneal of Eq. 2), z = 4, soft
+ * gate, combined bound, split_blocks = 0. */
+eta_params eta_default_params(void);
+
+/* Per-unit block capacity of the metadata, admitted-list and bound arrays for
+ * a cache of T_cap tokens: ceil(T_cap / 64) rounded up to a multiple of 4
+ * (0 if T_cap < 1). */
+int eta_nblk_cap(int T_cap);
+
+/* Human-readable name of a status code (static storage). */
+const char *eta_status_string(eta_status st);
+
+/*
+ * Block metadata builder (review "Summary": cached centroid / variance /
+ * max-norm; abstract: cached bounds). For every unit and every block of the
+ * first s->T tokens: centroid = mean key; var = mean over the block's tokens
+ * and the d dimensions of (k - centroid)^2 (population); maxnorm = largest key
+ * L2 norm. fp32 accumulation. Reads K once; writes blocks [0, ceil(T/64)) of
+ * m. Errors: ETA_ERR_INVALID_ARG (null pointer, bad shape or meta),
+ * ETA_ERR_UNSUPPORTED, ETA_ERR_HIP.
+ */
+eta_status eta_build_block_meta(const eta_shape *s, const void *K, const eta_meta *m,
+                                hipStream_t stream);
+
+/*
+ * Incremental metadata update after new tokens (same definition as above).
+ * s->T is the token count BEFORE the append; the caller has already written K
+ * for tokens [s->T, s->T + n_new). Recomputes only the blocks touched by those
+ * tokens, with the same per-block code as eta_build_block_meta, so the result
+ * is bitwise equal to a rebuild at T + n_new. Requires n_new >= 1 and
+ * s->T + n_new <= s->T_cap. Errors as eta_build_block_meta.
+ */
+eta_status eta_append_meta(const eta_shape *s, int n_new, const void *K, const eta_meta *m,
+                           hipStream_t stream);
+
+/*
+ * Threshold predictor (review "Methodology Assessment", Eq. 1):
+ *   tau[b][h] = bias[h] + sum_{g<H, i<d} q[b][g][i] * W[g*d + i][h]
+ * on the concatenated post-RoPE queries of one batch row. W is float32
+ * [H*d][H]; W == NULL selects frozen per-head thresholds tau[b][h] = bias[h]
+ * (abstract: offline calibration removes the predictor). fp32 accumulation in
+ * a fixed order. Errors: ETA_ERR_INVALID_ARG, ETA_ERR_HIP.
+ */
+eta_status eta_predict_tau(int B, int H, int d, const float *q, const float *W,
+                           const float *bias, float *tau, hipStream_t stream);
+
+/*
+ * O(1) block screen (abstract: cached geometric-probabilistic bounds; review
+ * Q&A "What is ETA?": a block whose best possible score is below tau is
+ * skipped). With s = 1/sqrt(d), per block:
+ *   U_geo  = s * |q| * maxnorm                        (Cauchy-Schwarz)
+ *   U_prob = s * (q . centroid + z * |q| * sqrt(var)) (centroid + z std devs)
+ *   U = min(U_geo, U_prob)  (ETA_BOUND_COMBINED)  or  U_geo (ETA_BOUND_GEO)
+ * Block beta < ceil(T/64) is admitted iff U >= tau[b][h] (a NaN tau admits
+ * nothing). Writes the admitted ids in ascending order to adm_idx[u][0..cnt)
+ * and cnt to adm_cnt[u]; entries past cnt are left untouched. bound_out
+ * (nullable, float32 [B][H][nblk_cap]) receives U, with -inf for blocks at or
+ * beyond ceil(T/64). Deterministic: no atomics. Errors: ETA_ERR_INVALID_ARG,
+ * ETA_ERR_UNSUPPORTED, ETA_ERR_HIP.
+ */
+eta_status eta_screen(const eta_shape *s, const float *q, const float *tau, const eta_meta *m,
+                      const eta_params *p, int32_t *adm_idx, int32_t *adm_cnt,
+                      float *bound_out, hipStream_t stream);
+
+/* Bytes of device workspace eta_decode_attn needs for this shape and split
+ * size (0 on invalid arguments). The layout is private to the library. */
+size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);
+
+/*
+ * Block-sparse split-KV decode attention with the ETA gate (Eq. 2 and Eq. 3;
+ * abstract: sub-threshold logits suppressed toward zero). For every unit,
+ * over the tokens (< T) of the blocks adm_idx[u][0..adm_cnt[u]):
+ *   S = s * q.k,  S' = S * sigmoid(gate_beta * (S - tau))  (or S * [S >= tau]),
+ *   out = softmax(S') . V,  lse = log of the softmax denominator.
+ * The admitted list is cut into work items of split_blocks blocks; partial
+ * (max, sum, weighted V) triples are merged by a log-sum-exp combine inside
+ * the same kernel, in a fixed order (deterministic). A unit with adm_cnt == 0
+ * gets out = 0 and lse = -inf. lse is nullable. adm_idx entries must be valid
+ * block ids < ceil(T/64) (eta_screen writes such lists).
+ * ws: device workspace of at least eta_decode_attn_workspace_size() bytes,
+ * 256-byte aligned; its contents need no initialisation and are clobbered.
+ * Two calls that share a workspace must not overlap in time.
+ * Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_WORKSPACE,
+ * ETA_ERR_HIP.
+ */
+eta_status eta_decode_attn(const eta_shape *s, const float *q, const void *K, const void *V,
+                           const float *tau, const int32_t *adm_idx, const int32_t *adm_cnt,
+                           const eta_params *p, float *out, float *lse, void *ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ETA_H */

@@ -1,0 +1,280 @@
+"""ctypes binding of ``libeta.so`` (the C ABI in ``include/eta.h``).
+
+Argument marshalling only: every function checks the torch tensors it is
+handed (device, dtype, shape, contiguity), passes their device pointers and the
+current HIP stream to the C function of the same name, and raises ``EtaError``
+on a non-OK status. All arithmetic runs in the library's HIP kernels; there is
+no fallback, and loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+ETA_OK = 0
+ETA_ERR_INVALID_ARG = -1
+ETA_ERR_UNSUPPORTED = -2
+ETA_ERR_WORKSPACE = -3
+ETA_ERR_HIP = -4
+
+ETA_F32 = 0
+ETA_BF16 = 1
+ETA_BOUND_COMBINED = 0
+ETA_BOUND_GEO = 1
+BLOCK = 64
+
+
+class EtaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+class eta_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int),
+                ("T", ctypes.c_int), ("T_cap", ctypes.c_int), ("block", ctypes.c_int),
+                ("kv_dtype", ctypes.c_int)]
+
+
+class eta_meta(ctypes.Structure):
+    _fields_ = [("centroid", ctypes.c_void_p), ("var", ctypes.c_void_p),
+                ("maxnorm", ctypes.c_void_p), ("nblk_cap", ctypes.c_int)]
+
+
+class eta_params(ctypes.Structure):
+    _fields_ = [("gate_beta", ctypes.c_float), ("z", ctypes.c_float),
+                ("gate_hard", ctypes.c_int), ("bound_mode", ctypes.c_int),
+                ("split_blocks", ctypes.c_int)]
+
+
+_P = ctypes.POINTER
+_vp = ctypes.c_void_p
+_lib = None
+
+# (restype, argtypes) of every exported symbol of include/eta.h
+SIGNATURES = {
+    "eta_default_params": (eta_params, []),
+    "eta_nblk_cap": (ctypes.c_int, [ctypes.c_int]),
+    "eta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "eta_build_block_meta": (ctypes.c_int, [_P(eta_shape), _vp, _P(eta_meta), _vp]),
+    "eta_append_meta": (ctypes.c_int, [_P(eta_shape), ctypes.c_int, _vp, _P(eta_meta), _vp]),
+    "eta_predict_tau": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
+                                       _vp, _vp]),
+    "eta_screen": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _P(eta_meta), _P(eta_params), _vp,
+                                  _vp, _vp, _vp]),
+    "eta_decode_attn_workspace_size": (ctypes.c_size_t, [_P(eta_shape), _P(eta_params)]),
+    "eta_decode_attn": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _P(eta_params), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libeta.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "long_context_decode_predict_amd.build.build_lib()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return lib().eta_status_string(st).decode()
+
+
+def _check(fn: str, st: int):
+    if st != ETA_OK:
+        raise EtaError(fn, st, status_string(st))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kv_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return ETA_BF16
+    if dtype == torch.float32:
+        return ETA_F32
+    raise ValueError(f"K/V dtype must be bfloat16 or float32, got {dtype}")
+
+
+def nblk_cap(T_cap: int) -> int:
+    return int(lib().eta_nblk_cap(int(T_cap)))
+
+
+def make_shape(B, H, d, T, T_cap, kv_dtype: torch.dtype) -> eta_shape:
+    return eta_shape(int(B), int(H), int(d), int(T), int(T_cap), BLOCK, kv_code(kv_dtype))
+
+
+def shape_of(K: torch.Tensor, T: int) -> eta_shape:
+    """Shape descriptor of a [B,H,T_cap,d] K/V cache holding T tokens."""
+    B, H, T_cap, d = K.shape
+    return make_shape(B, H, d, T, T_cap, K.dtype)
+
+
+def default_params(**kw) -> eta_params:
+    p = lib().eta_default_params()
+    for k, v in kw.items():
+        if not hasattr(p, k):
+            raise KeyError(k)
+        setattr(p, k, v)
+    return p
+
+
+@dataclass
+class Meta:
+    """Device buffers of the cached block metadata for one [B,H,T_cap,d] cache."""
+    centroid: torch.Tensor  # [B,H,d,nblk_cap] float32
+    var: torch.Tensor       # [B,H,nblk_cap] float32
+    maxnorm: torch.Tensor   # [B,H,nblk_cap] float32
+    nblk_cap: int
+
+    @staticmethod
+    def alloc(B, H, d, T_cap, device="cuda") -> "Meta":
+        n = nblk_cap(T_cap)
+        return Meta(torch.empty((B, H, d, n), dtype=torch.float32, device=device),
+                    torch.empty((B, H, n), dtype=torch.float32, device=device),
+                    torch.empty((B, H, n), dtype=torch.float32, device=device), n)
+
+    def c(self) -> eta_meta:
+        return eta_meta(self.centroid.data_ptr(), self.var.data_ptr(), self.maxnorm.data_ptr(),
+                        self.nblk_cap)
+
+
+def _check_meta(meta: Meta, B, H, d, T_cap):
+    n = nblk_cap(T_cap)
+    _need(meta.centroid, "centroid", torch.float32, (B, H, d, n))
+    _need(meta.var, "var", torch.float32, (B, H, n))
+    _need(meta.maxnorm, "maxnorm", torch.float32, (B, H, n))
+
+
+def _check_kv(K: torch.Tensor, name="K"):
+    if K.dim() != 4:
+        raise ValueError(f"{name} must be [B,H,T_cap,d]")
+    _need(K, name)
+    kv_code(K.dtype)
+
+
+# ------------------------------------------------------------------------------------
+# The C entry points, same names
+# ------------------------------------------------------------------------------------
+def eta_build_block_meta(K: torch.Tensor, T: int, meta: Meta, stream=None):
+    _check_kv(K)
+    s = shape_of(K, T)
+    _check_meta(meta, s.B, s.H, s.d, s.T_cap)
+    m = meta.c()
+    _check("eta_build_block_meta",
+           lib().eta_build_block_meta(ctypes.byref(s), K.data_ptr(), ctypes.byref(m), _stream(stream)))
+
+
+def eta_append_meta(K: torch.Tensor, T_old: int, n_new: int, meta: Meta, stream=None):
+    _check_kv(K)
+    s = shape_of(K, T_old)
+    _check_meta(meta, s.B, s.H, s.d, s.T_cap)
+    m = meta.c()
+    _check("eta_append_meta",
+           lib().eta_append_meta(ctypes.byref(s), int(n_new), K.data_ptr(), ctypes.byref(m),
+                                 _stream(stream)))
+
+
+def eta_predict_tau(q: torch.Tensor, W, bias: torch.Tensor, tau: torch.Tensor, stream=None):
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,d]")
+    B, H, d = q.shape
+    _need(q, "q", torch.float32)
+    if W is not None:
+        _need(W, "W", torch.float32, (H * d, H))
+    _need(bias, "bias", torch.float32, (H,))
+    _need(tau, "tau", torch.float32, (B, H))
+    _check("eta_predict_tau",
+           lib().eta_predict_tau(B, H, d, q.data_ptr(), _ptr(W), bias.data_ptr(), tau.data_ptr(),
+                                 _stream(stream)))
+
+
+def eta_screen(q: torch.Tensor, tau: torch.Tensor, meta: Meta, T: int, T_cap: int,
+               params: eta_params, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
+               bound_out=None, kv_dtype=torch.bfloat16, stream=None):
+    B, H, d = q.shape
+    s = make_shape(B, H, d, T, T_cap, kv_dtype)
+    n = nblk_cap(T_cap)
+    _need(q, "q", torch.float32)
+    _need(tau, "tau", torch.float32, (B, H))
+    _check_meta(meta, B, H, d, T_cap)
+    _need(adm_idx, "adm_idx", torch.int32, (B, H, n))
+    _need(adm_cnt, "adm_cnt", torch.int32, (B, H))
+    if bound_out is not None:
+        _need(bound_out, "bound_out", torch.float32, (B, H, n))
+    m = meta.c()
+    _check("eta_screen",
+           lib().eta_screen(ctypes.byref(s), q.data_ptr(), tau.data_ptr(), ctypes.byref(m),
+                            ctypes.byref(params), adm_idx.data_ptr(), adm_cnt.data_ptr(),
+                            _ptr(bound_out), _stream(stream)))
+
+
+def eta_decode_attn_workspace_size(B, H, d, T_cap, params: eta_params,
+                                   kv_dtype=torch.bfloat16) -> int:
+    s = make_shape(B, H, d, 0, T_cap, kv_dtype)
+    return int(lib().eta_decode_attn_workspace_size(ctypes.byref(s), ctypes.byref(params)))
+
+
+def alloc_workspace(B, H, d, T_cap, params: eta_params, kv_dtype=torch.bfloat16,
+                    device="cuda") -> torch.Tensor:
+    n = eta_decode_attn_workspace_size(B, H, d, T_cap, params, kv_dtype)
+    if n == 0:
+        raise EtaError("eta_decode_attn_workspace_size", ETA_ERR_INVALID_ARG, "invalid shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def eta_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
+                    tau: torch.Tensor, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
+                    params: eta_params, out: torch.Tensor, lse, ws: torch.Tensor, stream=None):
+    _check_kv(K)
+    _check_kv(V, "V")
+    if V.shape != K.shape or V.dtype != K.dtype:
+        raise ValueError("K and V must have the same shape and dtype")
+    s = shape_of(K, T)
+    n = nblk_cap(s.T_cap)
+    _need(q, "q", torch.float32, (s.B, s.H, s.d))
+    _need(tau, "tau", torch.float32, (s.B, s.H))
+    _need(adm_idx, "adm_idx", torch.int32, (s.B, s.H, n))
+    _need(adm_cnt, "adm_cnt", torch.int32, (s.B, s.H))
+    _need(out, "out", torch.float32, (s.B, s.H, s.d))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (s.B, s.H))
+    _need(ws, "ws", torch.uint8)
+    _check("eta_decode_attn",
+           lib().eta_decode_attn(ctypes.byref(s), q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                 tau.data_ptr(), adm_idx.data_ptr(), adm_cnt.data_ptr(),
+                                 ctypes.byref(params), out.data_ptr(), _ptr(lse),
+                                 ws.data_ptr(), ws.numel(), _stream(stream)))

@@ -1,0 +1,185 @@
+// eta_api.hip -- the extern "C" boundary declared in include/eta.h.
+//
+// Every entry point validates its arguments on the host before anything is
+// enqueued (no HIP call happens on an invalid call), maps launch failures to
+// ETA_ERR_HIP, never allocates, frees or synchronises, and keeps no state.
+#include "eta.h"
+
+#include <math.h>
+
+#include "eta_launch.hpp"
+
+namespace {
+
+constexpr int kBlock = 64;
+constexpr int kDefaultSplit = 16;
+constexpr int kMaxSplit = 4096;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Per-unit capacity of the metadata, admitted-list and bound arrays.
+int nblk_cap_of(int T_cap) { return (int)(ceil_div(ceil_div(T_cap, kBlock), 4) * 4); }
+
+eta_status check_shape(const eta_shape *s) {
+    if (s == nullptr) return ETA_ERR_INVALID_ARG;
+    if (s->B < 1 || s->H < 1 || s->T < 0 || s->T_cap < 1 || s->T > s->T_cap)
+        return ETA_ERR_INVALID_ARG;
+    if (s->d != 64 && s->d != 128) return ETA_ERR_UNSUPPORTED;
+    if (s->block != kBlock) return ETA_ERR_UNSUPPORTED;
+    if (s->kv_dtype != ETA_F32 && s->kv_dtype != ETA_BF16) return ETA_ERR_UNSUPPORTED;
+    const long long units = (long long)s->B * s->H;
+    if (units > (1ll << 24)) return ETA_ERR_INVALID_ARG;  // grid-size headroom
+    return ETA_OK;
+}
+
+eta_status check_meta(const eta_shape *s, const eta_meta *m) {
+    if (m == nullptr || m->centroid == nullptr || m->var == nullptr || m->maxnorm == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (m->nblk_cap != nblk_cap_of(s->T_cap)) return ETA_ERR_INVALID_ARG;
+    if (!aligned(m->centroid, 16) || !aligned(m->var, 16) || !aligned(m->maxnorm, 16))
+        return ETA_ERR_INVALID_ARG;
+    return ETA_OK;
+}
+
+// Alignment the row loads need: one lane reads d/16 consecutive elements.
+bool kv_aligned(const eta_shape *s, const void *p) {
+    const size_t elem = s->kv_dtype == ETA_BF16 ? 2 : 4;
+    return aligned(p, elem * (size_t)(s->d / 16) >= 16 ? 16 : 8);
+}
+
+eta::Geometry geometry(const eta_shape *s, int nblk_cap) {
+    eta::Geometry g;
+    g.units = s->B * s->H;
+    g.d = s->d;
+    g.T = s->T;
+    g.T_cap = s->T_cap;
+    g.nblk = (int)ceil_div(s->T, kBlock);
+    g.nblk_cap = nblk_cap;
+    g.bf16 = s->kv_dtype == ETA_BF16;
+    return g;
+}
+
+eta_status check_params(const eta_params *p) {
+    if (p == nullptr) return ETA_ERR_INVALID_ARG;
+    if (!p->gate_hard && !(p->gate_beta > 0.f && isfinite(p->gate_beta))) return ETA_ERR_INVALID_ARG;
+    if (!(p->z >= 0.f && isfinite(p->z))) return ETA_ERR_INVALID_ARG;
+    if (p->bound_mode != ETA_BOUND_COMBINED && p->bound_mode != ETA_BOUND_GEO)
+        return ETA_ERR_INVALID_ARG;
+    if (p->split_blocks < 0 || p->split_blocks > kMaxSplit) return ETA_ERR_INVALID_ARG;
+    return ETA_OK;
+}
+
+int split_of(const eta_params *p) { return p->split_blocks == 0 ? kDefaultSplit : p->split_blocks; }
+
+eta_status from_hip(hipError_t e) { return e == hipSuccess ? ETA_OK : ETA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+eta_params eta_default_params(void) {
+    eta_params p;
+    p.gate_beta = 5.0f;
+    p.z = 4.0f;
+    p.gate_hard = 0;
+    p.bound_mode = ETA_BOUND_COMBINED;
+    p.split_blocks = 0;
+    return p;
+}
+
+int eta_nblk_cap(int T_cap) { return T_cap < 1 ? 0 : nblk_cap_of(T_cap); }
+
+const char *eta_status_string(eta_status st) {
+    switch (st) {
+        case ETA_OK: return "ETA_OK";
+        case ETA_ERR_INVALID_ARG: return "ETA_ERR_INVALID_ARG";
+        case ETA_ERR_UNSUPPORTED: return "ETA_ERR_UNSUPPORTED";
+        case ETA_ERR_WORKSPACE: return "ETA_ERR_WORKSPACE";
+        case ETA_ERR_HIP: return "ETA_ERR_HIP";
+    }
+    return "ETA_ERR_UNKNOWN";
+}
+
+eta_status eta_build_block_meta(const eta_shape *s, const void *K, const eta_meta *m,
+                                hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_meta(s, m)) != ETA_OK) return st;
+    if (K == nullptr || !kv_aligned(s, K)) return ETA_ERR_INVALID_ARG;
+    const eta::Geometry g = geometry(s, m->nblk_cap);
+    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, 0, g.nblk, stream));
+}
+
+eta_status eta_append_meta(const eta_shape *s, int n_new, const void *K, const eta_meta *m,
+                           hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_meta(s, m)) != ETA_OK) return st;
+    if (K == nullptr || !kv_aligned(s, K)) return ETA_ERR_INVALID_ARG;
+    if (n_new < 1 || (long long)s->T + n_new > s->T_cap) return ETA_ERR_INVALID_ARG;
+    eta_shape grown = *s;
+    grown.T = s->T + n_new;
+    const eta::Geometry g = geometry(&grown, m->nblk_cap);
+    const int first = s->T / kBlock;  // the block holding token T_old (maybe partial)
+    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, first, g.nblk, stream));
+}
+
+eta_status eta_predict_tau(int B, int H, int d, const float *q, const float *W,
+                           const float *bias, float *tau, hipStream_t stream) {
+    if (B < 1 || H < 1 || d < 1 || q == nullptr || bias == nullptr || tau == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if ((long long)H * d > (1ll << 30) || B > 65535 * 1024) return ETA_ERR_INVALID_ARG;
+    if ((long long)H > 65535ll * 16) return ETA_ERR_INVALID_ARG;
+    return from_hip(eta::launch_predict_tau(B, H, d, q, W, bias, tau, stream));
+}
+
+eta_status eta_screen(const eta_shape *s, const float *q, const float *tau, const eta_meta *m,
+                      const eta_params *p, int32_t *adm_idx, int32_t *adm_cnt, float *bound_out,
+                      hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_meta(s, m)) != ETA_OK) return st;
+    if ((st = check_params(p)) != ETA_OK) return st;
+    if (q == nullptr || tau == nullptr || adm_idx == nullptr || adm_cnt == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (bound_out != nullptr && !aligned(bound_out, 16)) return ETA_ERR_INVALID_ARG;
+    const eta::Geometry g = geometry(s, m->nblk_cap);
+    return from_hip(eta::launch_screen(g, q, tau, m->centroid, m->var, m->maxnorm, p->z,
+                                       p->bound_mode == ETA_BOUND_GEO, adm_idx, adm_cnt,
+                                       bound_out, stream));
+}
+
+size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p) {
+    if (check_shape(s) != ETA_OK || check_params(p) != ETA_OK) return 0;
+    const int split = split_of(p);
+    long long max_chunks = ceil_div(ceil_div(s->T_cap, kBlock), split);
+    if (max_chunks < 1) max_chunks = 1;
+    return eta::attn_workspace_layout(s->B * s->H, (int)max_chunks, s->d).bytes;
+}
+
+eta_status eta_decode_attn(const eta_shape *s, const float *q, const void *K, const void *V,
+                           const float *tau, const int32_t *adm_idx, const int32_t *adm_cnt,
+                           const eta_params *p, float *out, float *lse, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_params(p)) != ETA_OK) return st;
+    if (q == nullptr || K == nullptr || V == nullptr || tau == nullptr || adm_idx == nullptr ||
+        adm_cnt == nullptr || out == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
+    const size_t need = eta_decode_attn_workspace_size(s, p);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return ETA_ERR_WORKSPACE;
+    const int split = split_of(p);
+    long long max_chunks = ceil_div(ceil_div(s->T_cap, kBlock), split);
+    if (max_chunks < 1) max_chunks = 1;
+    if ((long long)s->B * s->H * max_chunks > 0x7fffffffll) return ETA_ERR_INVALID_ARG;
+    const eta::Geometry g = geometry(s, nblk_cap_of(s->T_cap));
+    return from_hip(eta::launch_decode_attn(g, q, K, V, tau, adm_idx, adm_cnt, p->gate_beta,
+                                            p->gate_hard != 0, split, (int)max_chunks, out, lse,
+                                            ws, stream));
+}
+
+}  // extern "C"

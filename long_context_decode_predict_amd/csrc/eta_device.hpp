@@ -1,0 +1,114 @@
+// eta_device.hpp -- device helpers shared by the ETA kernels (gfx950, wave64).
+//
+// Lane layout used by every kernel that walks key or value rows: a wave64 is
+// four 16-lane DPP rows; row r of the wave owns one token, and lane c of the
+// row owns the EPL = d/16 consecutive elements [EPL*c, EPL*c + EPL) of it.
+// One wave load instruction therefore covers four whole token rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eta {
+
+constexpr int kWave = 64;
+constexpr int kBlockTokens = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- bfloat16 -> float32: exact widening of the upper half of a binary32 ----
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---- DPP helpers (row = 16 lanes) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over the 16 lanes of each row; every lane of the row receives the sum.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp_mov<kQuadXor1>(x);
+    x += dpp_mov<kQuadXor2>(x);
+    x += dpp_mov<kRowHalfMirror>(x);
+    x += dpp_mov<kRowMirror>(x);
+    return x;
+}
+
+// Max over the 16 lanes of each row; every lane of the row receives it.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp_mov<kQuadXor1>(x));
+    x = fmaxf(x, dpp_mov<kQuadXor2>(x));
+    x = fmaxf(x, dpp_mov<kRowHalfMirror>(x));
+    x = fmaxf(x, dpp_mov<kRowMirror>(x));
+    return x;
+}
+
+// Combine the four rows of the wave (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float xrow_sum(float x) {
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+__device__ __forceinline__ float xrow_max(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16, kWave));
+    x = fmaxf(x, __shfl_xor(x, 32, kWave));
+    return x;
+}
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// ---- row loads: EPL elements of one token row, widened to float ----
+// KV = float or uint16_t (bfloat16 bits). EPL = d / 16.
+template <typename KV, int EPL>
+struct RowLoad;
+
+template <>
+struct RowLoad<uint16_t, 8> {  // d = 128, bf16: 16 bytes per lane
+    uint4 raw;
+    __device__ __forceinline__ void load(const uint16_t *p) { raw = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void widen(float (&x)[8]) const {
+        x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x);
+        x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
+        x[4] = bf16_lo(raw.z); x[5] = bf16_hi(raw.z);
+        x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
+    }
+};
+
+template <>
+struct RowLoad<uint16_t, 4> {  // d = 64, bf16: 8 bytes per lane
+    uint2 raw;
+    __device__ __forceinline__ void load(const uint16_t *p) { raw = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ void widen(float (&x)[4]) const {
+        x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x);
+        x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
+    }
+};
+
+template <>
+struct RowLoad<float, 8> {  // d = 128, fp32: 32 bytes per lane
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void widen(float (&x)[8]) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+
+template <>
+struct RowLoad<float, 4> {  // d = 64, fp32: 16 bytes per lane
+    float4 a;
+    __device__ __forceinline__ void load(const float *p) { a = *reinterpret_cast<const float4 *>(p); }
+    __device__ __forceinline__ void widen(float (&x)[4]) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    }
+};
+
+}  // namespace eta

@@ -1,0 +1,45 @@
+// eta_launch.hpp -- host-side launchers behind the C ABI (internal).
+// Every launcher assumes arguments already validated by eta_api.hip and only
+// enqueues work on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace eta {
+
+struct Geometry {
+    int units;     // B * H
+    int d;         // 64 or 128
+    int T;         // tokens present
+    int T_cap;     // token capacity of K / V
+    int nblk;      // ceil(T / 64)
+    int nblk_cap;  // metadata / list capacity per unit (multiple of 4)
+    bool bf16;     // K / V element type
+};
+
+hipError_t launch_block_meta(const Geometry &g, const void *K, float *centroid, float *var,
+                             float *maxnorm, int blk_begin, int blk_end, hipStream_t st);
+
+hipError_t launch_predict_tau(int B, int H, int d, const float *q, const float *W,
+                              const float *bias, float *tau, hipStream_t st);
+
+hipError_t launch_screen(const Geometry &g, const float *q, const float *tau,
+                         const float *centroid, const float *var, const float *maxnorm,
+                         float z, bool geo_only, int32_t *adm_idx, int32_t *adm_cnt,
+                         float *bound_out, hipStream_t st);
+
+// Workspace layout of the split-KV attention for `units` units with at most
+// `max_chunks` work items each.
+struct AttnWorkspace {
+    size_t off_count, off_m, off_l, off_o, bytes;
+};
+AttnWorkspace attn_workspace_layout(int units, int max_chunks, int d);
+
+hipError_t launch_decode_attn(const Geometry &g, const float *q, const void *K, const void *V,
+                              const float *tau, const int32_t *adm_idx, const int32_t *adm_cnt,
+                              float gate_beta, bool gate_hard, int split_blocks, int max_chunks,
+                              float *out, float *lse, void *ws, hipStream_t st);
+
+}  // namespace eta

@@ -1,0 +1,46 @@
+"""One ETA decode step over a resident KV cache, as a sequence of C-ABI calls.
+
+``DecodeStep`` owns the per-step device buffers (tau, admitted lists, outputs,
+workspace) for one [B,H,T_cap,d] cache and enqueues the four library calls of
+a step on the current stream with no host synchronisation:
+eta_predict_tau -> eta_screen -> eta_decode_attn.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+class DecodeStep:
+    def __init__(self, B, H, d, T_cap, kv_dtype=torch.bfloat16, params=None, device="cuda",
+                 with_bounds=False):
+        self.B, self.H, self.d, self.T_cap = B, H, d, T_cap
+        self.kv_dtype = kv_dtype
+        self.params = params if params is not None else _lib.default_params()
+        n = _lib.nblk_cap(T_cap)
+        self.tau = torch.empty((B, H), dtype=torch.float32, device=device)
+        self.adm_idx = torch.empty((B, H, n), dtype=torch.int32, device=device)
+        self.adm_cnt = torch.empty((B, H), dtype=torch.int32, device=device)
+        self.out = torch.empty((B, H, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((B, H), dtype=torch.float32, device=device)
+        self.bounds = (torch.empty((B, H, n), dtype=torch.float32, device=device)
+                       if with_bounds else None)
+        self.ws = _lib.alloc_workspace(B, H, d, T_cap, self.params, kv_dtype, device)
+
+    def predict(self, q, W, bias, stream=None):
+        _lib.eta_predict_tau(q, W, bias, self.tau, stream)
+
+    def screen(self, q, meta, T, stream=None):
+        _lib.eta_screen(q, self.tau, meta, T, self.T_cap, self.params, self.adm_idx,
+                        self.adm_cnt, self.bounds, self.kv_dtype, stream)
+
+    def attend(self, q, K, V, T, stream=None):
+        _lib.eta_decode_attn(q, K, V, T, self.tau, self.adm_idx, self.adm_cnt, self.params,
+                             self.out, self.lse, self.ws, stream)
+
+    def __call__(self, q, K, V, T, meta, W, bias, stream=None):
+        self.predict(q, W, bias, stream)
+        self.screen(q, meta, T, stream)
+        self.attend(q, K, V, T, stream)
+        return self.out

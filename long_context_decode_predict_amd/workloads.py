@@ -1,0 +1,165 @@
+"""Seeded synthetic decode workloads shaped like the pages' long-context setting.
+
+Input generation only: this module draws random tensors and holds none of the
+method's arithmetic. Both the HIP path and the oracle are handed the bytes it
+produces (the oracle gets device-to-host copies).
+
+Recipe (per (batch, head) unit, per 64-token block): a block centroid drawn
+from N(0, 1)^d; each key = centroid + N(0, sigma^2) elementwise (clustered
+keys, sigma = 0.3 unless a per-head range is given); values ~ N(0, 1); the
+post-RoPE query ~ N(0, 1)^d; the predictor W is block-diagonal (head h reads
+only its own query slice) with entries N(0, 1/d). Optional "needle" keys: in a
+fraction of the blocks one key at a seeded slot is replaced by
+r * (0.9 * q_hat + sqrt(0.19) * u), u a random unit vector orthogonal to q_hat,
+r = sqrt(d (1 + sigma^2)) -- a key aligned with the query at cosine 0.9.
+All draws use torch generators seeded per workload on the target device.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+BLOCK = 64
+SEED_BASE = 20260916
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    d: int
+    T: int                      # tokens present at the timed step
+    kv_dtype: torch.dtype
+    sigma: float = 0.3          # in-block key spread
+    sigma_range: tuple | None = None   # per-head spread ~ U(lo, hi) instead of sigma
+    density: float = 0.38       # target mean admitted-block fraction
+    head_densities: tuple | None = None  # static per-head targets (no predictor)
+    needle_frac: float = 0.0
+    append: int = 0             # tokens appended one by one before the step
+    seed: int = SEED_BASE
+    note: str = field(default="", compare=False)
+
+    @property
+    def static_tau(self) -> bool:
+        return self.head_densities is not None
+
+    @property
+    def T_cap(self) -> int:
+        return self.T
+
+    @property
+    def nblk(self) -> int:
+        return (self.T + BLOCK - 1) // BLOCK
+
+
+WORKLOADS = {
+    "tiny_b1_h4_d64_t2k_f32": Workload(
+        "tiny_b1_h4_d64_t2k_f32", B=1, H=4, d=64, T=2048, kv_dtype=torch.float32,
+        seed=SEED_BASE + 0, note="tiny single decode step, fp32 K/V"),
+    "llama_b32_h16_d128_t32k_bf16": Workload(
+        "llama_b32_h16_d128_t32k_bf16", B=32, H=16, d=128, T=32768, kv_dtype=torch.bfloat16,
+        seed=SEED_BASE + 1, note="LLaMA-style layer decode"),
+    "headline_b64_h16_d128_t128k_bf16": Workload(
+        "headline_b64_h16_d128_t128k_bf16", B=64, H=16, d=128, T=131072,
+        kv_dtype=torch.bfloat16, needle_frac=0.01, seed=SEED_BASE + 2,
+        note="headline decode with planted needle keys"),
+    "sparse_b16_h16_d128_t512k_bf16": Workload(
+        "sparse_b16_h16_d128_t512k_bf16", B=16, H=16, d=128, T=524288,
+        kv_dtype=torch.bfloat16, density=0.16, append=128, seed=SEED_BASE + 3,
+        note="sparse long context, 128 single-token appends before the step"),
+    "static_b64_h16_d128_t64k_bf16": Workload(
+        "static_b64_h16_d128_t64k_bf16", B=64, H=16, d=128, T=65536,
+        kv_dtype=torch.bfloat16, sigma_range=(0.1, 0.6),
+        head_densities=tuple(0.1 + 0.8 * h / 15 for h in range(16)), seed=SEED_BASE + 4,
+        note="frozen per-head thresholds, per-head densities 10..90%"),
+}
+
+HEADLINE = "headline_b64_h16_d128_t128k_bf16"
+
+
+def custom(name="custom", **kw) -> Workload:
+    """A workload with explicit sizes (tests use small ragged ones)."""
+    base = dict(B=1, H=2, d=128, T=300, kv_dtype=torch.bfloat16)
+    base.update(kw)
+    return Workload(name, **base)
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def head_sigmas(w: Workload) -> torch.Tensor:
+    """Per-head in-block key spread (float32 [H], on the CPU)."""
+    if w.sigma_range is None:
+        return torch.full((w.H,), float(w.sigma), dtype=torch.float32)
+    g = _gen("cpu", w.seed + 7)
+    lo, hi = w.sigma_range
+    return (lo + (hi - lo) * torch.rand(w.H, generator=g)).to(torch.float32)
+
+
+def generate(w: Workload, device="cuda", T_cap: int | None = None) -> dict:
+    """Draw q, K, V, W for a workload on `device`.
+
+    Returns dict(q [B,H,d] f32, K, V [B,H,T_cap,d] kv_dtype, W [H*d,H] f32 or None,
+    sigmas [H], needles: LongTensor [n,3] of (unit, block, slot) or None)."""
+    T_cap = w.T_cap if T_cap is None else T_cap
+    B, H, d = w.B, w.H, w.d
+    nblk_cap = (T_cap + BLOCK - 1) // BLOCK
+    g = _gen(device, w.seed)
+    q = torch.randn((B, H, d), generator=g, device=device, dtype=torch.float32)
+    sig = head_sigmas(w).to(device)
+    K = torch.empty((B, H, T_cap, d), dtype=w.kv_dtype, device=device)
+    V = torch.empty((B, H, T_cap, d), dtype=w.kv_dtype, device=device)
+    for b in range(B):  # one batch row at a time keeps fp32 temporaries small
+        cen = torch.randn((H, nblk_cap, 1, d), generator=g, device=device, dtype=torch.float32)
+        noise = torch.randn((H, nblk_cap, BLOCK, d), generator=g, device=device,
+                            dtype=torch.float32)
+        noise.mul_(sig.view(H, 1, 1, 1)).add_(cen)
+        K[b].copy_(noise.view(H, nblk_cap * BLOCK, d)[:, :T_cap])
+        del noise, cen
+        vb = torch.randn((H, T_cap, d), generator=g, device=device, dtype=torch.float32)
+        V[b].copy_(vb)
+        del vb
+    W = None
+    if not w.static_tau:
+        W = torch.zeros((H * d, H), dtype=torch.float32, device=device)
+        wdiag = torch.randn((H, d), generator=g, device=device, dtype=torch.float32) / math.sqrt(d)
+        for h in range(H):
+            W[h * d:(h + 1) * d, h] = wdiag[h]
+    needles = None
+    if w.needle_frac > 0:
+        needles = plant_needles(w, q, K, sig, g, T_cap)
+    return {"q": q, "K": K, "V": V, "W": W, "sigmas": sig, "needles": needles}
+
+
+def plant_needles(w: Workload, q, K, sig, g, T_cap):
+    """Replace one key in a seeded fraction of each unit's blocks by a key aligned with
+    the unit's query at cosine 0.9. Returns (unit, block, slot) triples."""
+    B, H, d = w.B, w.H, w.d
+    nblk = w.nblk
+    per_unit = max(1, int(round(w.needle_frac * nblk)))
+    dev = q.device
+    units = B * H
+    # seeded distinct blocks per unit and a slot inside each
+    keys = torch.rand((units, nblk), generator=g, device=dev)
+    blocks = torch.argsort(keys, dim=1)[:, :per_unit]
+    slots = torch.randint(0, BLOCK, (units, per_unit), generator=g, device=dev)
+    tok = blocks * BLOCK + slots
+    tok = torch.minimum(tok, torch.full_like(tok, w.T - 1))
+    qf = q.reshape(units, d)
+    qhat = qf / qf.norm(dim=1, keepdim=True)
+    u = torch.randn((units, per_unit, d), generator=g, device=dev)
+    u = u - (u * qhat[:, None, :]).sum(-1, keepdim=True) * qhat[:, None, :]
+    u = u / u.norm(dim=-1, keepdim=True)
+    sig_u = sig.repeat(B)  # unit = b*H + h
+    r = torch.sqrt(d * (1.0 + sig_u ** 2))[:, None, None]
+    key = r * (0.9 * qhat[:, None, :] + math.sqrt(0.19) * u)
+    Kf = K.view(units, T_cap, d)
+    rows = torch.arange(units, device=dev)[:, None].expand_as(tok)
+    Kf[rows.reshape(-1), tok.reshape(-1)] = key.reshape(-1, d).to(K.dtype)
+    return torch.stack([rows.reshape(-1), (tok // BLOCK).reshape(-1), (tok % BLOCK).reshape(-1)], 1)

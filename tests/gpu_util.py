@@ -1,0 +1,164 @@
+"""Shared machinery of the GPU parity tests: run the HIP path through the C ABI, run
+the fp64 oracle on chosen (batch, head) units, and compare.
+
+Criteria (tolerances written here, used by every GPU test):
+  * admitted-block mask: bit-exact against the oracle for every block whose fp64
+    bound lies farther than BAND = 1e-5 from the oracle's fp64 tau; a block
+    inside the band may go either way (fp32 vs fp64 rounding of the bound);
+  * out: max-abs error <= 2e-3 for bf16 K/V, <= 1e-5 for fp32 K/V;
+  * lse: abs error <= 1e-4 (fp32 logits of magnitude <= ~15 and an fp32 sum of
+    at most 2^19 terms: the rounding error is below 1e-5; 1e-4 leaves margin);
+  * tau: abs error <= 1e-5 (fp32 dot of length H*d <= 2048 of O(0.1) terms);
+  * block metadata: centroid abs <= 1e-5, var and maxnorm rel <= 1e-5;
+  * bound: abs <= 1e-5 * max(1, |U|).
+A unit whose GPU mask differs from the oracle's inside the band is not
+compared on out/lse (its admitted set legitimately differs); the count of such
+units is returned and kept small by the callers.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from long_context_decode_predict_amd import _lib, calibrate, workloads
+from long_context_decode_predict_amd.decode import DecodeStep
+from oracle import oracle as oracle_mod
+
+BAND = 1e-5
+OUT_TOL = {torch.bfloat16: 2e-3, torch.float32: 1e-5}
+LSE_TOL = 1e-4
+TAU_TOL = 1e-5
+
+
+def kv_host(t: torch.Tensor) -> np.ndarray:
+    """A device K/V slab as numpy: float32, or the uint16 bit patterns of bf16."""
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+class Case:
+    """A workload instance on the GPU plus the library's results for one step."""
+
+    def __init__(self, w: workloads.Workload, tau_mode="predictor", params=None, T=None,
+                 T_cap=None, bias=None):
+        self.w = w
+        self.T_cap = T_cap if T_cap is not None else w.T_cap
+        self.T = T if T is not None else w.T
+        self.params = params if params is not None else _lib.default_params()
+        self.data = workloads.generate(w, "cuda", T_cap=self.T_cap)
+        d = self.data
+        self.W = d["W"] if tau_mode == "predictor" else None
+        if bias is not None:
+            self.bias = bias.to("cuda", torch.float32)
+        elif tau_mode in ("predictor", "static"):
+            self.bias = calibrate.bias_for(w, d["q"], d["W"], z=self.params.z)
+        else:
+            val = {"neg_inf": -math.inf, "pos_inf": math.inf, "nan": math.nan}[tau_mode]
+            self.bias = torch.full((w.H,), val, dtype=torch.float32, device="cuda")
+        self.meta = _lib.Meta.alloc(w.B, w.H, w.d, self.T_cap)
+        self.step = DecodeStep(w.B, w.H, w.d, self.T_cap, w.kv_dtype, self.params,
+                               with_bounds=True)
+
+    def build_meta(self):
+        _lib.eta_build_block_meta(self.data["K"], self.T, self.meta)
+
+    def run(self, build=True):
+        if build:
+            self.build_meta()
+        d = self.data
+        self.step(d["q"], d["K"], d["V"], self.T, self.meta, self.W, self.bias)
+        torch.cuda.synchronize()
+        return self
+
+    def host(self):
+        s = self.step
+        return {"tau": s.tau.cpu().numpy(), "idx": s.adm_idx.cpu().numpy(),
+                "cnt": s.adm_cnt.cpu().numpy(), "out": s.out.cpu().numpy(),
+                "lse": s.lse.cpu().numpy(), "U": s.bounds.cpu().numpy(),
+                "centroid": self.meta.centroid, "var": self.meta.var,
+                "maxnorm": self.meta.maxnorm}
+
+    def free(self):
+        for k in list(self.data):
+            self.data[k] = None
+        self.meta = None
+        self.step = None
+        torch.cuda.empty_cache()
+
+
+def check_list_properties(g: dict, nblk: int):
+    """Every unit's list is strictly ascending, in range and exactly cnt long."""
+    cnt = g["cnt"].reshape(-1)
+    idx = g["idx"].reshape(cnt.shape[0], -1)
+    assert np.all(cnt >= 0) and np.all(cnt <= nblk)
+    for u in range(cnt.shape[0]):
+        lst = idx[u, :cnt[u]]
+        assert np.all(np.diff(lst) > 0), u
+        if len(lst):
+            assert lst[0] >= 0 and lst[-1] < nblk, u
+
+
+def compare_units(case: Case, units, O=None, check_meta=True):
+    """Compare the library against the oracle on the given units; returns stats."""
+    O = O or oracle_mod.default()
+    w, T, p = case.w, case.T, case.params
+    g = case.host()
+    q = case.data["q"].cpu().numpy()
+    W = None if case.W is None else case.W.cpu().numpy()
+    bias = case.bias.cpu().numpy()
+    tau_o = O.predict_tau(q, W, bias)
+    nblk = (T + 63) // 64
+    check_list_properties(g, nblk)
+    tau_g = g["tau"]
+    fin = np.isfinite(tau_o)
+    assert np.array_equal(fin, np.isfinite(tau_g))
+    assert np.all(np.abs(tau_g[fin] - tau_o[fin]) <= TAU_TOL)
+    stats = {"units": 0, "in_band": 0, "band_mismatch_units": 0, "out_checked": 0,
+             "max_out_err": 0.0, "max_lse_err": 0.0, "density": []}
+    tol = OUT_TOL[w.kv_dtype]
+    for u in units:
+        b, h = divmod(int(u), w.H)
+        Kh = kv_host(case.data["K"][b, h])
+        Vh = kv_host(case.data["V"][b, h])
+        c, v, m = O.block_meta(Kh, T)
+        if check_meta and nblk:
+            cg = g["centroid"][b, h, :, :nblk].cpu().numpy().T
+            assert np.max(np.abs(cg - c)) <= 1e-5, np.max(np.abs(cg - c))
+            vg = g["var"][b, h, :nblk].cpu().numpy()
+            mg = g["maxnorm"][b, h, :nblk].cpu().numpy()
+            assert np.all(np.abs(vg - v) <= 1e-5 * np.maximum(v, 1e-30) + 1e-12)
+            assert np.all(np.abs(mg - m) <= 1e-5 * m + 1e-12)
+        U = O.bounds(q[b, h], c, v, m, z=p.z, mode=p.bound_mode)
+        Ug = g["U"][b, h, :nblk]
+        assert np.all(np.abs(Ug - U) <= 1e-5 * np.maximum(1.0, np.abs(U))), np.max(np.abs(Ug - U))
+        t = float(tau_o[b, h])
+        mask_o = U >= t
+        cnt = int(g["cnt"][b, h])
+        mask_g = np.zeros(nblk, bool)
+        mask_g[g["idx"][b, h, :cnt]] = True
+        outside = ~(np.abs(U - t) <= BAND)
+        assert np.array_equal(mask_g[outside], mask_o[outside]), (u, np.nonzero(mask_g != mask_o))
+        stats["units"] += 1
+        stats["in_band"] += int((~outside).sum())
+        stats["density"].append(cnt / max(nblk, 1))
+        if not np.array_equal(mask_g, mask_o):
+            stats["band_mismatch_units"] += 1
+            continue
+        idx_o = np.nonzero(mask_o)[0].astype(np.int32)
+        out_o, lse_o = O.attend(q[b, h], Kh, Vh, T, t, idx_o, beta=p.gate_beta,
+                                hard=bool(p.gate_hard))
+        out_g = g["out"][b, h]
+        lse_g = float(g["lse"][b, h])
+        err = float(np.max(np.abs(out_g - out_o)))
+        assert err <= tol, (u, err)
+        if math.isinf(lse_o):
+            assert lse_g == lse_o and np.all(out_g == 0), (u, lse_g)
+        else:
+            assert abs(lse_g - lse_o) <= LSE_TOL, (u, lse_g, lse_o)
+            stats["max_lse_err"] = max(stats["max_lse_err"], abs(lse_g - lse_o))
+        stats["out_checked"] += 1
+        stats["max_out_err"] = max(stats["max_out_err"], err)
+    return stats

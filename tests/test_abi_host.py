@@ -1,0 +1,164 @@
+"""The C-ABI library loads, exports every symbol include/eta.h declares, and rejects
+invalid arguments before anything is enqueued (CPU only: no valid call is made,
+so no kernel is ever launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_decode_predict_amd import _lib
+from long_context_decode_predict_amd.build import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # a 256-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "eta.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(eta_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, n
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_defaults_and_strings(L):
+    p = L.eta_default_params()
+    assert (p.gate_beta, p.z, p.gate_hard, p.bound_mode, p.split_blocks) == (5.0, 4.0, 0, 0, 0)
+    for st, s in [(0, "ETA_OK"), (-1, "ETA_ERR_INVALID_ARG"), (-2, "ETA_ERR_UNSUPPORTED"),
+                  (-3, "ETA_ERR_WORKSPACE"), (-4, "ETA_ERR_HIP"), (7, "ETA_ERR_UNKNOWN")]:
+        assert _lib.status_string(st) == s
+    assert [L.eta_nblk_cap(t) for t in (0, 1, 64, 65, 256, 257, 2048, 131072)] == \
+        [0, 4, 4, 4, 4, 8, 32, 2048]
+
+
+def shape(**kw):
+    s = dict(B=2, H=3, d=128, T=1000, T_cap=1024, block=64, kv_dtype=1)
+    s.update(kw)
+    return _lib.eta_shape(**s)
+
+
+def meta(T_cap=1024, **kw):
+    m = dict(centroid=FAKE, var=FAKE, maxnorm=FAKE, nblk_cap=_lib.nblk_cap(T_cap))
+    m.update(kw)
+    return _lib.eta_meta(**m)
+
+
+BY = ctypes.byref
+INV, UNS, WSP = _lib.ETA_ERR_INVALID_ARG, _lib.ETA_ERR_UNSUPPORTED, _lib.ETA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("s,st", [
+    (None, INV),
+    (dict(d=96), UNS), (dict(d=256), UNS), (dict(block=32), UNS), (dict(kv_dtype=5), UNS),
+    (dict(T=1025), INV), (dict(T=-1), INV), (dict(B=0), INV), (dict(H=0), INV),
+    (dict(T_cap=0, T=0), INV),
+])
+def test_build_meta_shape_errors(L, s, st):
+    sp = None if s is None else BY(shape(**s))
+    assert L.eta_build_block_meta(sp, FAKE, BY(meta()), None) == st
+
+
+def test_build_meta_meta_and_pointer_errors(L):
+    s = BY(shape())
+    assert L.eta_build_block_meta(s, FAKE, None, None) == INV
+    assert L.eta_build_block_meta(s, None, BY(meta()), None) == INV
+    assert L.eta_build_block_meta(s, FAKE + 2, BY(meta()), None) == INV  # misaligned K
+    assert L.eta_build_block_meta(s, FAKE, BY(meta(nblk_cap=20)), None) == INV
+    assert L.eta_build_block_meta(s, FAKE, BY(meta(centroid=FAKE + 4)), None) == INV
+    assert L.eta_build_block_meta(s, FAKE, BY(meta(var=None)), None) == INV
+
+
+def test_append_errors(L):
+    s = BY(shape(T=1000))
+    assert L.eta_append_meta(s, 0, FAKE, BY(meta()), None) == INV
+    assert L.eta_append_meta(s, 25, FAKE, BY(meta()), None) == INV  # past T_cap
+    assert L.eta_append_meta(BY(shape(d=80)), 1, FAKE, BY(meta()), None) == UNS
+
+
+def test_predict_errors(L):
+    assert L.eta_predict_tau(0, 4, 64, FAKE, FAKE, FAKE, FAKE, None) == INV
+    assert L.eta_predict_tau(1, 0, 64, FAKE, FAKE, FAKE, FAKE, None) == INV
+    assert L.eta_predict_tau(1, 4, 64, None, FAKE, FAKE, FAKE, None) == INV
+    assert L.eta_predict_tau(1, 4, 64, FAKE, FAKE, None, FAKE, None) == INV
+    assert L.eta_predict_tau(1, 4, 64, FAKE, FAKE, FAKE, None, None) == INV
+
+
+def params(**kw):
+    return _lib.default_params(**kw)
+
+
+@pytest.mark.parametrize("kw", [dict(gate_beta=0.0), dict(gate_beta=float("inf")),
+                                dict(gate_beta=float("nan")), dict(z=-1.0), dict(z=float("inf")),
+                                dict(bound_mode=2), dict(split_blocks=-1),
+                                dict(split_blocks=5000)])
+def test_screen_param_errors(L, kw):
+    p = params(**kw)
+    assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(meta()), BY(p), FAKE, FAKE, None, None) == INV
+
+
+def test_screen_other_errors(L):
+    p = BY(params())
+    assert L.eta_screen(BY(shape()), None, FAKE, BY(meta()), p, FAKE, FAKE, None, None) == INV
+    assert L.eta_screen(BY(shape()), FAKE, None, BY(meta()), p, FAKE, FAKE, None, None) == INV
+    assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(meta()), p, None, FAKE, None, None) == INV
+    assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(meta()), p, FAKE, None, None, None) == INV
+    assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(meta()), None, FAKE, FAKE, None, None) == INV
+    assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(meta()), p, FAKE, FAKE, FAKE + 4, None) == INV
+    # a hard gate does not need a finite beta
+    assert L.eta_screen(BY(shape(d=32)), FAKE, FAKE, BY(meta()), BY(params(gate_hard=1, gate_beta=0.0)),
+                        FAKE, FAKE, None, None) == UNS
+
+
+def test_workspace_size(L):
+    p = params()
+    n1 = L.eta_decode_attn_workspace_size(BY(shape(T_cap=1024)), BY(p))
+    n2 = L.eta_decode_attn_workspace_size(BY(shape(T_cap=4096, T=0)), BY(p))
+    assert n1 > 0 and n2 > n1 and n1 % 256 == 0
+    assert L.eta_decode_attn_workspace_size(BY(shape(d=7)), BY(p)) == 0
+    assert L.eta_decode_attn_workspace_size(BY(shape()), None) == 0
+    small = L.eta_decode_attn_workspace_size(BY(shape(T_cap=4096, T=0)),
+                                             BY(params(split_blocks=4096)))
+    assert 0 < small < n2
+
+
+def test_decode_attn_errors(L):
+    s = BY(shape())
+    p = params()
+    need = L.eta_decode_attn_workspace_size(s, BY(p))
+    args = lambda **kw: dict(dict(q=FAKE, K=FAKE, V=FAKE, tau=FAKE, idx=FAKE, cnt=FAKE,
+                                  out=FAKE, lse=None, ws=FAKE, ws_bytes=need), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return L.eta_decode_attn(s, a["q"], a["K"], a["V"], a["tau"], a["idx"], a["cnt"], BY(p),
+                                 a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+    assert call(ws_bytes=need - 1) == WSP
+    assert call(ws=None) == WSP
+    assert call(ws=FAKE + 128) == WSP
+    assert call(out=None) == INV
+    assert call(q=None) == INV
+    assert call(K=FAKE + 8) == INV
+    assert call(cnt=None) == INV
+    assert L.eta_decode_attn(BY(shape(d=48)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BY(p), FAKE,
+                             None, FAKE, need, None) == UNS
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros((1, 2, 64))
+    with pytest.raises(ValueError):
+        _lib.eta_predict_tau(q, None, torch.zeros(2), torch.zeros((1, 2)))
