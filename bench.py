@@ -57,24 +57,29 @@ def meta_bytes(w):
     return w.B * w.H * w.nblk * (w.d + 2) * 4
 
 
-def run_steps(step, data, w, meta, W, bias, n, stream, ev_pairs=None):
+def run_steps(step, data, w, meta, W, bias, n, stream, evs=None):
+    """n decode steps; with evs, events bracket predict+screen, the split-KV partial
+    kernel and the combine kernel of every step (all on the launch stream)."""
     q, K, V = data["q"], data["K"], data["V"]
     for i in range(n):
-        if ev_pairs is not None:
-            ev_pairs[i][0].record(stream)
+        if evs is not None:
+            evs[i][0].record(stream)
         step.predict(q, W, bias)
         step.screen(q, meta, w.T)
-        if ev_pairs is not None:
-            ev_pairs[i][1].record(stream)
-        step.attend(q, K, V, w.T)
-        if ev_pairs is not None:
-            ev_pairs[i][2].record(stream)
+        if evs is not None:
+            evs[i][1].record(stream)
+        step.attend_partial(q, K, V, w.T)
+        if evs is not None:
+            evs[i][2].record(stream)
+        step.attend_combine(K, w.T)
+        if evs is not None:
+            evs[i][3].record(stream)
 
 
 def time_steps(step, data, w, meta, W, bias, steps, warmup):
     stream = torch.cuda.current_stream()
     run_steps(step, data, w, meta, W, bias, warmup, stream)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -85,7 +90,9 @@ def time_steps(step, data, w, meta, W, bias, steps, warmup):
     total_ms = start.elapsed_time(end)
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     front_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    return total_ms / steps, float(np.mean(attn_ms)), float(np.mean(front_ms)), attn_ms
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    return (total_ms / steps, float(np.mean(attn_ms)), float(np.mean(front_ms)),
+            float(np.mean(comb_ms)))
 
 
 def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=None):
@@ -188,7 +195,7 @@ def main():
     log(f"[bench] metadata build {build_ms:.2f} ms")
 
     step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params)
-    ms, attn_ms, front_ms, attn_all = time_steps(step, data, w, meta, W, bias, args.steps,
+    ms, attn_ms, front_ms, comb_ms = time_steps(step, data, w, meta, W, bias, args.steps,
                                                  args.warmup)
     cnt = step.adm_cnt.cpu().numpy()
     idx = step.adm_idx.cpu().numpy()
@@ -199,13 +206,15 @@ def main():
     units = w.B * w.H
     attn_alg = kv_adm + int(cnt.sum()) * 4 + units * w.d * 4 * 2 + units * 8
     attn_gbs = attn_alg / (attn_ms * 1e-3) / 1e9
-    log(f"[bench] {ms:.3f} ms/step, density {density:.3f}, attention {attn_ms:.3f} ms "
-        f"({attn_gbs:.0f} GB/s), predict+screen {front_ms:.3f} ms, effective {eff_gbs:.0f} GB/s")
+    log(f"[bench] {ms:.3f} ms/step, density {density:.3f}, attention partial {attn_ms:.3f} ms "
+        f"({attn_gbs:.0f} GB/s), combine {comb_ms:.3f} ms, predict+screen {front_ms:.3f} ms, "
+        f"effective {eff_gbs:.0f} GB/s")
 
     extra = {"density": density, "effective_kv_gbs": eff_gbs,
              "effective_frac_hbm_peak": eff_gbs / HBM_PEAK_GBS,
              "admitted_kv_bytes": kv_adm, "metadata_bytes": mb,
-             "attn_ms": attn_ms, "predict_screen_ms": front_ms, "meta_build_ms": build_ms}
+             "attn_partial_ms": attn_ms, "combine_ms": comb_ms, "predict_screen_ms": front_ms,
+             "meta_build_ms": build_ms}
     if append_ms is not None:
         extra["append_ms_per_token"] = append_ms
     per_head = (cnt / w.nblk).mean(axis=0)
@@ -266,7 +275,7 @@ def main():
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",
                    "split_blocks": params.split_blocks or 16, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "eta_decode_attn", "achieved": attn_gbs,
+        "roofline": {"bound": "hbm", "kernel": "attn_partial_kernel", "achieved": attn_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
                      "traffic": None,
                      "algorithmic_bytes_per_launch": attn_alg, "avg_launch_ms": attn_ms},

@@ -69,7 +69,8 @@ typedef struct {
     int B, H;           /* batch rows and heads (MHA)                          */
     int d;              /* head dimension: 64 or 128                           */
     int T;              /* tokens present in the cache (0 <= T <= T_cap)       */
-    int T_cap;          /* token capacity of the K/V layout (>= 1)             */
+    int T_cap;          /* token capacity of the K/V layout: a positive
+                           multiple of 64 (whole blocks)                       */
     int block;          /* tokens per KV block: must be 64                     */
     eta_dtype kv_dtype; /* element type of K and V                             */
 } eta_shape;
@@ -156,7 +157,7 @@ eta_status eta_screen(const eta_shape *s, const float *q, const float *tau, cons
                       const eta_params *p, int32_t *adm_idx, int32_t *adm_cnt,
                       float *bound_out, hipStream_t stream);
 
-/* Bytes of device workspace eta_decode_attn needs for this shape and split
+/* Bytes of device workspace the attention calls need for this shape and split
  * size (0 on invalid arguments). The layout is private to the library. */
 size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);
 
@@ -166,14 +167,15 @@ size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);
  * over the tokens (< T) of the blocks adm_idx[u][0..adm_cnt[u]):
  *   S = s * q.k,  S' = S * sigmoid(gate_beta * (S - tau))  (or S * [S >= tau]),
  *   out = softmax(S') . V,  lse = log of the softmax denominator.
- * The admitted list is cut into work items of split_blocks blocks; partial
- * (max, sum, weighted V) triples are merged by a log-sum-exp combine inside
- * the same kernel, in a fixed order (deterministic). A unit with adm_cnt == 0
- * gets out = 0 and lse = -inf. lse is nullable. adm_idx entries must be valid
- * block ids < ceil(T/64) (eta_screen writes such lists).
+ * The admitted list is cut into work items of split_blocks blocks. This call
+ * is eta_decode_attn_partial followed by eta_decode_attn_combine on the same
+ * stream. A unit with adm_cnt == 0 gets out = 0 and lse = -inf. lse is
+ * nullable. adm_idx entries must be valid ascending block ids < ceil(T/64)
+ * (eta_screen writes such lists); an id out of range is skipped.
  * ws: device workspace of at least eta_decode_attn_workspace_size() bytes,
- * 256-byte aligned; its contents need no initialisation and are clobbered.
- * Two calls that share a workspace must not overlap in time.
+ * 256-byte aligned; it needs no initialisation and is clobbered. Calls that
+ * share a workspace must not overlap in time. Deterministic for a fixed
+ * split size; results for different split sizes agree to fp32 rounding.
  * Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_WORKSPACE,
  * ETA_ERR_HIP.
  */
@@ -181,6 +183,31 @@ eta_status eta_decode_attn(const eta_shape *s, const float *q, const void *K, co
                            const float *tau, const int32_t *adm_idx, const int32_t *adm_cnt,
                            const eta_params *p, float *out, float *lse, void *ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * First phase of eta_decode_attn: every work item's online-softmax partial
+ * (running max, sum of weights, weighted sum of V) over its blocks. Units
+ * whose list fits one work item (or is empty) receive their final out / lse
+ * here; the others' partials go to ws for eta_decode_attn_combine. Same
+ * arguments, conventions and errors as eta_decode_attn.
+ */
+eta_status eta_decode_attn_partial(const eta_shape *s, const float *q, const void *K,
+                                   const void *V, const float *tau, const int32_t *adm_idx,
+                                   const int32_t *adm_cnt, const eta_params *p, float *out,
+                                   float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Second phase of eta_decode_attn: for every unit with more than one work
+ * item, merges the partials left in ws by eta_decode_attn_partial (same
+ * shape, parameters and adm_cnt) with a log-sum-exp combine in item order:
+ * M = max_i m_i, l = sum_i l_i e^(m_i - M), out = sum_i o_i e^(m_i - M) / l,
+ * lse = M + log(l). Must follow the partial call on the same stream.
+ * Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_WORKSPACE,
+ * ETA_ERR_HIP.
+ */
+eta_status eta_decode_attn_combine(const eta_shape *s, const int32_t *adm_cnt,
+                                   const eta_params *p, float *out, float *lse, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -70,6 +70,11 @@ SIGNATURES = {
     "eta_decode_attn_workspace_size": (ctypes.c_size_t, [_P(eta_shape), _P(eta_params)]),
     "eta_decode_attn": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp, _vp,
                                        _P(eta_params), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "eta_decode_attn_partial": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _P(eta_params), _vp, _vp, _vp, ctypes.c_size_t,
+                                               _vp]),
+    "eta_decode_attn_combine": (ctypes.c_int, [_P(eta_shape), _vp, _P(eta_params), _vp, _vp, _vp,
+                                               ctypes.c_size_t, _vp]),
 }
 
 
@@ -256,9 +261,7 @@ def alloc_workspace(B, H, d, T_cap, params: eta_params, kv_dtype=torch.bfloat16,
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def eta_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
-                    tau: torch.Tensor, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
-                    params: eta_params, out: torch.Tensor, lse, ws: torch.Tensor, stream=None):
+def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws):
     _check_kv(K)
     _check_kv(V, "V")
     if V.shape != K.shape or V.dtype != K.dtype:
@@ -273,8 +276,43 @@ def eta_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
     if lse is not None:
         _need(lse, "lse", torch.float32, (s.B, s.H))
     _need(ws, "ws", torch.uint8)
+    return s
+
+
+def eta_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
+                    tau: torch.Tensor, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
+                    params: eta_params, out: torch.Tensor, lse, ws: torch.Tensor, stream=None):
+    s = _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws)
     _check("eta_decode_attn",
            lib().eta_decode_attn(ctypes.byref(s), q.data_ptr(), K.data_ptr(), V.data_ptr(),
                                  tau.data_ptr(), adm_idx.data_ptr(), adm_cnt.data_ptr(),
                                  ctypes.byref(params), out.data_ptr(), _ptr(lse),
                                  ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def eta_decode_attn_partial(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
+                            tau: torch.Tensor, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
+                            params: eta_params, out: torch.Tensor, lse, ws: torch.Tensor,
+                            stream=None):
+    s = _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws)
+    _check("eta_decode_attn_partial",
+           lib().eta_decode_attn_partial(ctypes.byref(s), q.data_ptr(), K.data_ptr(),
+                                         V.data_ptr(), tau.data_ptr(), adm_idx.data_ptr(),
+                                         adm_cnt.data_ptr(), ctypes.byref(params),
+                                         out.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel(),
+                                         _stream(stream)))
+
+
+def eta_decode_attn_combine(K: torch.Tensor, T: int, adm_cnt: torch.Tensor, params: eta_params,
+                            out: torch.Tensor, lse, ws: torch.Tensor, stream=None):
+    _check_kv(K)
+    s = shape_of(K, T)
+    _need(adm_cnt, "adm_cnt", torch.int32, (s.B, s.H))
+    _need(out, "out", torch.float32, (s.B, s.H, s.d))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (s.B, s.H))
+    _need(ws, "ws", torch.uint8)
+    _check("eta_decode_attn_combine",
+           lib().eta_decode_attn_combine(ctypes.byref(s), adm_cnt.data_ptr(),
+                                         ctypes.byref(params), out.data_ptr(), _ptr(lse),
+                                         ws.data_ptr(), ws.numel(), _stream(stream)))

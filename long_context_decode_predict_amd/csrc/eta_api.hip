@@ -26,6 +26,7 @@ eta_status check_shape(const eta_shape *s) {
     if (s == nullptr) return ETA_ERR_INVALID_ARG;
     if (s->B < 1 || s->H < 1 || s->T < 0 || s->T_cap < 1 || s->T > s->T_cap)
         return ETA_ERR_INVALID_ARG;
+    if (s->T_cap % kBlock != 0) return ETA_ERR_INVALID_ARG;  // whole blocks of capacity
     if (s->d != 64 && s->d != 128) return ETA_ERR_UNSUPPORTED;
     if (s->block != kBlock) return ETA_ERR_UNSUPPORTED;
     if (s->kv_dtype != ETA_F32 && s->kv_dtype != ETA_BF16) return ETA_ERR_UNSUPPORTED;
@@ -74,6 +75,24 @@ eta_status check_params(const eta_params *p) {
 int split_of(const eta_params *p) { return p->split_blocks == 0 ? kDefaultSplit : p->split_blocks; }
 
 eta_status from_hip(hipError_t e) { return e == hipSuccess ? ETA_OK : ETA_ERR_HIP; }
+
+// Shared validation of the attention calls; fills the geometry and item count.
+eta_status check_attn(const eta_shape *s, const eta_params *p, const int32_t *adm_cnt,
+                      const float *out, void *ws, size_t ws_bytes, eta::Geometry *g,
+                      int *max_chunks) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_params(p)) != ETA_OK) return st;
+    if (adm_cnt == nullptr || out == nullptr) return ETA_ERR_INVALID_ARG;
+    const size_t need = eta_decode_attn_workspace_size(s, p);
+    if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return ETA_ERR_WORKSPACE;
+    long long mc = ceil_div(ceil_div(s->T_cap, kBlock), split_of(p));
+    if (mc < 1) mc = 1;
+    if ((long long)s->B * s->H * mc > 0x7fffffffll) return ETA_ERR_INVALID_ARG;
+    *g = geometry(s, nblk_cap_of(s->T_cap));
+    *max_chunks = (int)mc;
+    return ETA_OK;
+}
 
 }  // namespace
 
@@ -159,27 +178,41 @@ size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p) {
     return eta::attn_workspace_layout(s->B * s->H, (int)max_chunks, s->d).bytes;
 }
 
+eta_status eta_decode_attn_partial(const eta_shape *s, const float *q, const void *K,
+                                   const void *V, const float *tau, const int32_t *adm_idx,
+                                   const int32_t *adm_cnt, const eta_params *p, float *out,
+                                   float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+    eta::Geometry g;
+    int max_chunks = 0;
+    eta_status st = check_attn(s, p, adm_cnt, out, ws, ws_bytes, &g, &max_chunks);
+    if (st != ETA_OK) return st;
+    if (q == nullptr || K == nullptr || V == nullptr || tau == nullptr || adm_idx == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
+    return from_hip(eta::launch_attn_partial(g, q, K, V, tau, adm_idx, adm_cnt, p->gate_beta,
+                                             p->gate_hard != 0, split_of(p), max_chunks, out, lse,
+                                             ws, stream));
+}
+
+eta_status eta_decode_attn_combine(const eta_shape *s, const int32_t *adm_cnt,
+                                   const eta_params *p, float *out, float *lse, void *ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+    eta::Geometry g;
+    int max_chunks = 0;
+    eta_status st = check_attn(s, p, adm_cnt, out, ws, ws_bytes, &g, &max_chunks);
+    if (st != ETA_OK) return st;
+    return from_hip(eta::launch_attn_combine(g, adm_cnt, split_of(p), max_chunks, out, lse, ws,
+                                             stream));
+}
+
 eta_status eta_decode_attn(const eta_shape *s, const float *q, const void *K, const void *V,
                            const float *tau, const int32_t *adm_idx, const int32_t *adm_cnt,
                            const eta_params *p, float *out, float *lse, void *ws,
                            size_t ws_bytes, hipStream_t stream) {
-    eta_status st = check_shape(s);
+    eta_status st = eta_decode_attn_partial(s, q, K, V, tau, adm_idx, adm_cnt, p, out, lse, ws,
+                                            ws_bytes, stream);
     if (st != ETA_OK) return st;
-    if ((st = check_params(p)) != ETA_OK) return st;
-    if (q == nullptr || K == nullptr || V == nullptr || tau == nullptr || adm_idx == nullptr ||
-        adm_cnt == nullptr || out == nullptr)
-        return ETA_ERR_INVALID_ARG;
-    if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
-    const size_t need = eta_decode_attn_workspace_size(s, p);
-    if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return ETA_ERR_WORKSPACE;
-    const int split = split_of(p);
-    long long max_chunks = ceil_div(ceil_div(s->T_cap, kBlock), split);
-    if (max_chunks < 1) max_chunks = 1;
-    if ((long long)s->B * s->H * max_chunks > 0x7fffffffll) return ETA_ERR_INVALID_ARG;
-    const eta::Geometry g = geometry(s, nblk_cap_of(s->T_cap));
-    return from_hip(eta::launch_decode_attn(g, q, K, V, tau, adm_idx, adm_cnt, p->gate_beta,
-                                            p->gate_hard != 0, split, (int)max_chunks, out, lse,
-                                            ws, stream));
+    return eta_decode_attn_combine(s, adm_cnt, p, out, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

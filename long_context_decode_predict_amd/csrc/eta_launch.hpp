@@ -33,13 +33,18 @@ hipError_t launch_screen(const Geometry &g, const float *q, const float *tau,
 // Workspace layout of the split-KV attention for `units` units with at most
 // `max_chunks` work items each.
 struct AttnWorkspace {
-    size_t off_count, off_m, off_l, off_o, bytes;
+    size_t off_m, off_l, off_o, bytes;
 };
 AttnWorkspace attn_workspace_layout(int units, int max_chunks, int d);
 
-hipError_t launch_decode_attn(const Geometry &g, const float *q, const void *K, const void *V,
-                              const float *tau, const int32_t *adm_idx, const int32_t *adm_cnt,
-                              float gate_beta, bool gate_hard, int split_blocks, int max_chunks,
-                              float *out, float *lse, void *ws, hipStream_t st);
+// Split-KV partials (writes out/lse directly for units with a single item).
+hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K, const void *V,
+                               const float *tau, const int32_t *adm_idx, const int32_t *adm_cnt,
+                               float gate_beta, bool gate_hard, int split_blocks, int max_chunks,
+                               float *out, float *lse, void *ws, hipStream_t st);
+
+// Log-sum-exp merge of the partials of units with more than one item.
+hipError_t launch_attn_combine(const Geometry &g, const int32_t *adm_cnt, int split_blocks,
+                               int max_chunks, float *out, float *lse, void *ws, hipStream_t st);
 
 }  // namespace eta

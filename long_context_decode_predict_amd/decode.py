@@ -3,7 +3,8 @@
 ``DecodeStep`` owns the per-step device buffers (tau, admitted lists, outputs,
 workspace) for one [B,H,T_cap,d] cache and enqueues the four library calls of
 a step on the current stream with no host synchronisation:
-eta_predict_tau -> eta_screen -> eta_decode_attn.
+eta_predict_tau -> eta_screen -> eta_decode_attn (= eta_decode_attn_partial followed
+by eta_decode_attn_combine).
 """
 from __future__ import annotations
 
@@ -38,6 +39,14 @@ class DecodeStep:
     def attend(self, q, K, V, T, stream=None):
         _lib.eta_decode_attn(q, K, V, T, self.tau, self.adm_idx, self.adm_cnt, self.params,
                              self.out, self.lse, self.ws, stream)
+
+    def attend_partial(self, q, K, V, T, stream=None):
+        _lib.eta_decode_attn_partial(q, K, V, T, self.tau, self.adm_idx, self.adm_cnt,
+                                     self.params, self.out, self.lse, self.ws, stream)
+
+    def attend_combine(self, K, T, stream=None):
+        _lib.eta_decode_attn_combine(K, T, self.adm_cnt, self.params, self.out, self.lse,
+                                     self.ws, stream)
 
     def __call__(self, q, K, V, T, meta, W, bias, stream=None):
         self.predict(q, W, bias, stream)

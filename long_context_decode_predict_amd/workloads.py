@@ -48,7 +48,8 @@ class Workload:
 
     @property
     def T_cap(self) -> int:
-        return self.T
+        """Cache capacity: T rounded up to whole 64-token blocks (at least one)."""
+        return max(BLOCK, (self.T + BLOCK - 1) // BLOCK * BLOCK)
 
     @property
     def nblk(self) -> int:

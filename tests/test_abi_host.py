@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
@@ -65,7 +65,7 @@ INV, UNS, WSP = _lib.ETA_ERR_INVALID_ARG, _lib.ETA_ERR_UNSUPPORTED, _lib.ETA_ERR
     (None, INV),
     (dict(d=96), UNS), (dict(d=256), UNS), (dict(block=32), UNS), (dict(kv_dtype=5), UNS),
     (dict(T=1025), INV), (dict(T=-1), INV), (dict(B=0), INV), (dict(H=0), INV),
-    (dict(T_cap=0, T=0), INV),
+    (dict(T_cap=0, T=0), INV), (dict(T_cap=1000, T=900), INV),
 ])
 def test_build_meta_shape_errors(L, s, st):
     sp = None if s is None else BY(shape(**s))

@@ -27,7 +27,7 @@ def gpu():
 def sample_units(w, n=N_SAMPLE):
     rng = np.random.default_rng(w.seed)
     units = {0, w.B * w.H - 1}
-    units |= set(rng.choice(w.B * w.H, size=n, replace=False).tolist())
+    units |= set(rng.choice(w.B * w.H, size=min(n, w.B * w.H), replace=False).tolist())
     return sorted(units)
 
 

@@ -38,9 +38,9 @@ SMALL = [
     # name, workload, tau mode, params, T_cap override
     ("tiny_config", W["tiny_b1_h4_d64_t2k_f32"], "predictor", {}, None),
     ("bf16_d128_ragged", workloads.custom("r1", B=2, H=3, d=128, T=1000, kv_dtype=torch.bfloat16,
-                                          seed=11), "predictor", {}, 1100),
+                                          seed=11), "predictor", {}, 1152),
     ("f32_d128_ragged", workloads.custom("r2", B=1, H=2, d=128, T=777, kv_dtype=torch.float32,
-                                         seed=12), "predictor", {}, 800),
+                                         seed=12), "predictor", {}, 832),
     ("bf16_d64_one_token_tail", workloads.custom("r3", B=2, H=2, d=64, T=513,
                                                  kv_dtype=torch.bfloat16, seed=13),
      "predictor", {}, None),
