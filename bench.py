@@ -147,6 +147,26 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=N
             "gpu_over_cpu": (1000.0 / step_gpu_ms) * step_s}
 
 
+def copy_probe(gib: float, reps: int):
+    """Time torch's device-to-device copy of `gib` GiB (read + write bytes counted)."""
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * n * 4
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "ms_per_copy": ms, "gbs_read_plus_write": nbytes / (ms * 1e-3) / 1e9}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,12 +176,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
+                    help="only time a plain device copy of GIB GiB (HBM reference and the "
+                         "scale for counter-based traffic) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the step is data-parallel over (batch, head) units; see DESIGN.md for how it "
               "would shard)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe, args.steps)
+        return
     ensure_built()
     torch.cuda.set_device(0)
     w = workloads.WORKLOADS[args.workload]

@@ -7,9 +7,13 @@
 // absorbs the tokens that coarse block selection lets in (abstract).
 //
 // Work decomposition. A unit's ascending admitted list is cut into work items
-// of `split` blocks; the grid is (item index) x (unit), item-major, and an
-// item past a unit's list exits at once. A workgroup of four waves takes one
-// item; wave w walks the item's blocks w, w+4, ... in tiles of TS tokens:
+// of `split` blocks. A one-workgroup plan kernel scans the per-unit item counts
+// into a compacted item list (and settles empty units directly); a persistent
+// grid of a few workgroups per CU then takes items from the list through a
+// device-scope ticket counter, so no workgroup is launched for an absent item
+// and the load balances itself whatever the per-unit densities. A workgroup of
+// four waves processes one item at a time; wave w walks the item's blocks
+// w, w+4, ... in tiles of TS tokens:
 //   - row r of the wave owns one token and lane c of the row the EPL = d/16
 //     elements [EPL*c, EPL*c + EPL) of it, so one 16-byte load per lane covers
 //     four whole token rows; every load is a uniform block base plus a fixed
@@ -35,6 +39,7 @@ namespace eta {
 namespace {
 
 constexpr int kAttnWaves = 4;
+constexpr int kWorkersPerCU = 4;  // persistent workgroups launched per CU
 
 struct AttnArgs {
     int units, T, T_cap, nblk, nblk_cap, split, ws_chunks;
@@ -50,6 +55,8 @@ struct AttnArgs {
     float *ws_m;
     float *ws_l;
     float *ws_o;
+    int *ws_hdr;     // [0] = number of items, [1] = ticket counter
+    int2 *ws_items;  // compacted (unit, item index) list
 };
 
 // Zero the raw bits of a row held in registers (used for rows past T).
@@ -67,29 +74,26 @@ __device__ __forceinline__ void zero_row<float, 8>(RowLoad<float, 8> &r) {
 template <>
 __device__ __forceinline__ void zero_row<float, 4>(RowLoad<float, 4> &r) { r.a = make_float4(0.f, 0.f, 0.f, 0.f); }
 
+template <int D>
+struct AttnShared {
+    float m[kAttnWaves];
+    float l[kAttnWaves];
+    float o[kAttnWaves][D];
+    int ticket;
+};
+
+// One work item (unit u, item `chunk`) by the whole workgroup. Ends with the
+// workgroup merge (one barrier); the caller barriers before LDS is reused.
 template <typename KV, int D, int TS, bool HARD>
-__global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
+                                          AttnShared<D> &sm) {
     constexpr int EPL = D / 16;
     constexpr int L = TS / 4;                 // row loads per lane per tile
     constexpr int TPB = kBlockTokens / TS;    // tiles per block
     constexpr int ROW = D;                    // elements per token row
-    __shared__ float sm_m[kAttnWaves];
-    __shared__ float sm_l[kAttnWaves];
-    __shared__ float sm_o[kAttnWaves][D];
-
-    const int u = blockIdx.x % a.units;
-    const int chunk = blockIdx.x / a.units;
     const int c = a.cnt[u];
     const int nchunks = (c + a.split - 1) / a.split;
-    if (chunk >= (nchunks > 1 ? nchunks : 1)) return;
-
     const int tid = threadIdx.x;
-    if (c <= 0) {  // nothing admitted: out = 0, lse = -inf
-        for (int i = tid; i < D; i += blockDim.x) a.out[(size_t)u * D + i] = 0.f;
-        if (tid == 0 && a.lse) a.lse[u] = -INFINITY;
-        return;
-    }
-
     const int wave = tid / kWave;
     const int lane = tid & (kWave - 1);
     const int row = lane >> 4;
@@ -199,30 +203,30 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = xrow_sum(o[e]);
     if (lane == 0) {
-        sm_m[wave] = m_run;
-        sm_l[wave] = l_w;
+        sm.m[wave] = m_run;
+        sm.l[wave] = l_w;
     }
     if (lane < 16) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) sm_o[wave][lane * EPL + e] = o[e];
+        for (int e = 0; e < EPL; ++e) sm.o[wave][lane * EPL + e] = o[e];
     }
     __syncthreads();
 
     // merge the waves of the workgroup
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm_m[w]);
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.m[w]);
     float Lsum = 0.f;
     float wgt[kAttnWaves];
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
-        wgt[w] = fast_exp(sm_m[w] - M);  // a wave without blocks has m = -inf: weight 0
-        Lsum += sm_l[w] * wgt[w];
+        wgt[w] = fast_exp(sm.m[w] - M);  // a wave without blocks has m = -inf: weight 0
+        Lsum += sm.l[w] * wgt[w];
     }
     if (tid < D) {
         float O = 0.f;
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) O += sm_o[w][tid] * wgt[w];
+        for (int w = 0; w < kAttnWaves; ++w) O += sm.o[w][tid] * wgt[w];
         if (nchunks == 1) {
             a.out[(size_t)u * D + tid] = O / Lsum;
         } else {
@@ -241,25 +245,125 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
     }
 }
 
+// Persistent workers: each workgroup takes item tickets until the list is done.
+template <typename KV, int D, int TS, bool HARD>
+__global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArgs a) {
+    __shared__ AttnShared<D> sm;
+    const int total = a.ws_hdr[0];
+    if (threadIdx.x == 0) sm.ticket = atomicAdd(&a.ws_hdr[1], 1);
+    __syncthreads();
+    int ticket = sm.ticket;
+    while (ticket < total) {
+        const int2 it = a.ws_items[ticket];
+        int next = 0;
+        if (threadIdx.x == 0) next = atomicAdd(&a.ws_hdr[1], 1);  // fetched early
+        attn_item<KV, D, TS, HARD>(a, it.x, it.y, sm);
+        if (threadIdx.x == 0) sm.ticket = next;
+        __syncthreads();
+        ticket = sm.ticket;
+    }
+}
+
+// Compacted item list: items of unit u are (u, 0 .. ceil(cnt[u]/split) - 1),
+// units in order. Units with nothing admitted get out = 0, lse = -inf here.
+// One workgroup; the per-unit counts are scanned kPlanThreads at a time.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int D) {
+    __shared__ int wave_sum[kPlanThreads / kWave];
+    __shared__ int carry;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base < a.units; base += kPlanThreads) {
+        const int u = base + tid;
+        const int c = u < a.units ? a.cnt[u] : 0;
+        const int n = (c + a.split - 1) / a.split;
+        if (u < a.units && c <= 0) {
+            for (int i = 0; i < D; ++i) a.out[(size_t)u * D + i] = 0.f;
+            if (a.lse) a.lse[u] = -INFINITY;
+        }
+        // inclusive scan of n inside the wave, then across waves
+        int x = n;
+#pragma unroll
+        for (int k = 1; k < kWave; k <<= 1) {
+            const int y = __shfl_up(x, k, kWave);
+            if (lane >= k) x += y;
+        }
+        if (lane == kWave - 1) wave_sum[wave] = x;
+        __syncthreads();
+        int before = carry;
+        for (int w = 0; w < wave; ++w) before += wave_sum[w];
+        const int off = before + x - n;  // exclusive offset of this unit's items
+        for (int j = 0; j < n; ++j) a.ws_items[off + j] = make_int2(u, j);
+        __syncthreads();
+        if (tid == kPlanThreads - 1) carry = before + x;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.ws_hdr[0] = carry;
+        a.ws_hdr[1] = 0;
+    }
+}
+
 // Log-sum-exp merge of the partials of every unit that has more than one item.
+// One workgroup per unit: the item maxima, weights and sums are reduced across
+// the workgroup, and thread t accumulates output dimension t % D over the items
+// i = t / D, t / D + R, ... (R = threads / D), in a fixed order; the R partial
+// sums are then added in LDS in a fixed order (deterministic).
+constexpr int kCombineThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
+    constexpr int R = kCombineThreads / D;
+    constexpr int NW = kCombineThreads / kWave;
+    __shared__ float red[NW];
+    __shared__ float part[R][D];
     const int u = blockIdx.x;
     const int c = a.cnt[u];
     const int nchunks = (c + a.split - 1) / a.split;
     if (nchunks <= 1) return;
-    const size_t s0 = (size_t)u * a.ws_chunks;
-    float M = -INFINITY;
-    for (int i = 0; i < nchunks; ++i) M = fmaxf(M, a.ws_m[s0 + i]);
-    float Lsum = 0.f, O = 0.f;
     const int tid = threadIdx.x;
-    for (int i = 0; i < nchunks; ++i) {
-        const float w = fast_exp(a.ws_m[s0 + i] - M);
-        Lsum += a.ws_l[s0 + i] * w;
-        O += a.ws_o[(s0 + i) * D + tid] * w;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const float *wm = a.ws_m + (size_t)u * a.ws_chunks;
+    const float *wl = a.ws_l + (size_t)u * a.ws_chunks;
+    const float *wo = a.ws_o + (size_t)u * a.ws_chunks * D;
+
+    float mx = -INFINITY;
+    for (int i = tid; i < nchunks; i += kCombineThreads) mx = fmaxf(mx, wm[i]);
+    mx = xrow_max(row_max16(mx));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();  // red is reused below
+
+    float ls = 0.f;
+    for (int i = tid; i < nchunks; i += kCombineThreads) ls += wl[i] * fast_exp(wm[i] - M);
+    ls = xrow_sum(row_sum16(ls));
+    if (lane == 0) red[wave] = ls;
+
+    const int dim = tid % D;
+    const int r = tid / D;
+    float O = 0.f;
+#pragma unroll 4
+    for (int i = r; i < nchunks; i += R) O += wo[(size_t)i * D + dim] * fast_exp(wm[i] - M);
+    part[r][dim] = O;
+    __syncthreads();
+    if (tid < D) {
+        float Lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) Lsum += red[w];
+        float Ot = 0.f;
+#pragma unroll
+        for (int k = 0; k < R; ++k) Ot += part[k][tid];
+        a.out[(size_t)u * D + tid] = Ot / Lsum;
+        if (tid == 0 && a.lse) a.lse[u] = M + __logf(Lsum);
     }
-    a.out[(size_t)u * D + tid] = O / Lsum;
-    if (tid == 0 && a.lse) a.lse[u] = M + __logf(Lsum);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -291,12 +395,14 @@ AttnArgs make_args(const Geometry &g, const float *q, const void *K, const void 
     a.ws_m = reinterpret_cast<float *>(base + w.off_m);
     a.ws_l = reinterpret_cast<float *>(base + w.off_l);
     a.ws_o = reinterpret_cast<float *>(base + w.off_o);
+    a.ws_hdr = reinterpret_cast<int *>(base + w.off_hdr);
+    a.ws_items = reinterpret_cast<int2 *>(base + w.off_items);
     return a;
 }
 
 template <typename KV, int D, int TS>
-hipError_t launch_partial_t(const AttnArgs &a, bool hard, int grid_chunks, hipStream_t st) {
-    const dim3 grid((unsigned)((long long)a.units * grid_chunks));
+hipError_t launch_partial_t(const AttnArgs &a, bool hard, int workers, hipStream_t st) {
+    const dim3 grid((unsigned)workers);
     if (hard) {
         hipLaunchKernelGGL((attn_partial_kernel<KV, D, TS, true>), grid, dim3(kAttnWaves * kWave), 0,
                            st, a);
@@ -312,7 +418,9 @@ hipError_t launch_partial_t(const AttnArgs &a, bool hard, int grid_chunks, hipSt
 AttnWorkspace attn_workspace_layout(int units, int max_chunks, int d) {
     AttnWorkspace w;
     const size_t slots = (size_t)units * (size_t)max_chunks;
-    w.off_m = 0;
+    w.off_hdr = 0;
+    w.off_items = align256(w.off_hdr + 2 * sizeof(int));
+    w.off_m = align256(w.off_items + 2 * sizeof(int) * slots);
     w.off_l = align256(w.off_m + sizeof(float) * slots);
     w.off_o = align256(w.off_l + sizeof(float) * slots);
     w.bytes = align256(w.off_o + sizeof(float) * slots * (size_t)d);
@@ -326,15 +434,24 @@ hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K,
     if (g.units == 0) return hipSuccess;
     const AttnArgs a = make_args(g, q, K, V, tau, adm_idx, adm_cnt, gate_beta, split_blocks,
                                  max_chunks, out, lse, ws);
-    // items needed at the current length (at least one per unit for the empty list)
-    int grid_chunks = (g.nblk + split_blocks - 1) / split_blocks;
-    if (grid_chunks < 1) grid_chunks = 1;
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a, g.d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // persistent workers: a few per CU, never more than the largest possible item count
+    int dev = 0, cus = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return e;
+    long long workers = (long long)cus * kWorkersPerCU;
+    const long long most = (long long)g.units * ((g.nblk + split_blocks - 1) / split_blocks);
+    if (workers > most) workers = most > 0 ? most : 1;
+    const int wk = (int)workers;
     if (g.bf16) {
-        return g.d == 128 ? launch_partial_t<uint16_t, 128, 64>(a, gate_hard, grid_chunks, st)
-                          : launch_partial_t<uint16_t, 64, 64>(a, gate_hard, grid_chunks, st);
+        return g.d == 128 ? launch_partial_t<uint16_t, 128, 64>(a, gate_hard, wk, st)
+                          : launch_partial_t<uint16_t, 64, 64>(a, gate_hard, wk, st);
     }
-    return g.d == 128 ? launch_partial_t<float, 128, 32>(a, gate_hard, grid_chunks, st)
-                      : launch_partial_t<float, 64, 64>(a, gate_hard, grid_chunks, st);
+    return g.d == 128 ? launch_partial_t<float, 128, 32>(a, gate_hard, wk, st)
+                      : launch_partial_t<float, 64, 64>(a, gate_hard, wk, st);
 }
 
 hipError_t launch_attn_combine(const Geometry &g, const int32_t *adm_cnt, int split_blocks,
@@ -343,9 +460,11 @@ hipError_t launch_attn_combine(const Geometry &g, const int32_t *adm_cnt, int sp
     const AttnArgs a = make_args(g, nullptr, nullptr, nullptr, nullptr, nullptr, adm_cnt, 1.f,
                                  split_blocks, max_chunks, out, lse, ws);
     if (g.d == 128) {
-        hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((unsigned)g.units), dim3(128), 0, st, a);
+        hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((unsigned)g.units),
+                           dim3(kCombineThreads), 0, st, a);
     } else {
-        hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((unsigned)g.units), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((unsigned)g.units),
+                           dim3(kCombineThreads), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -33,7 +33,7 @@ hipError_t launch_screen(const Geometry &g, const float *q, const float *tau,
 // Workspace layout of the split-KV attention for `units` units with at most
 // `max_chunks` work items each.
 struct AttnWorkspace {
-    size_t off_m, off_l, off_o, bytes;
+    size_t off_hdr, off_items, off_m, off_l, off_o, bytes;
 };
 AttnWorkspace attn_workspace_layout(int units, int max_chunks, int d);
 
