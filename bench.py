@@ -28,6 +28,8 @@ from long_context_decode_predict_amd.build import ensure_built  # noqa: E402
 from long_context_decode_predict_amd.decode import DecodeStep  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+ATTN_SOURCES = ("eta_attn.hip", "eta_device.hpp")
 METRIC = "ETA decode steps/s and effective KV GB/s (% HBM peak), B=64 T=128K ~38% density"
 
 
@@ -51,6 +53,37 @@ def admitted_bytes(w, cnt, idx):
         has_last = sum(int(idxf[u, c - 1] == nblk - 1) for u, c in enumerate(cntf) if c > 0)
         full -= has_last * (64 - last_tokens)
     return 2 * full * w.d * eb
+
+
+def attn_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "long_context_decode_predict_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3 counter
+    summary of this workload, or None if there is none or the kernel changed since."""
+    path = os.path.join(PROFILES, f"attn_partial_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch",
+                                                      "attn_source_sha256"):
+                k, v = line.split(":", 1)
+                vals[k] = v.strip()
+    if vals.get("attn_source_sha256") != attn_source_sha():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def meta_bytes(w):
@@ -303,7 +336,7 @@ def main():
                    "split_blocks": params.split_blocks or 16, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "attn_partial_kernel", "achieved": attn_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
-                     "traffic": None,
+                     "traffic": counter_traffic(w.name),
                      "algorithmic_bytes_per_launch": attn_alg, "avg_launch_ms": attn_ms},
         "cpu_baseline": cpu,
         "extra": extra,

@@ -266,45 +266,62 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
 
 // Compacted item list: items of unit u are (u, 0 .. ceil(cnt[u]/split) - 1),
 // units in order. Units with nothing admitted get out = 0, lse = -inf here.
-// One workgroup; the per-unit counts are scanned kPlanThreads at a time.
-constexpr int kPlanThreads = 1024;
+// Each workgroup owns kPlanUnits consecutive units: it first sums the item
+// counts of all earlier units itself (a few KiB of reads, no cross-workgroup
+// communication), scans its own units in one wave, and then writes each unit's
+// items with one wave per unit on consecutive list entries. The last workgroup
+// stores the item total; workgroup 0 resets the ticket counter.
+constexpr int kPlanThreads = 256;
+constexpr int kPlanUnits = 64;
 
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int D) {
-    __shared__ int wave_sum[kPlanThreads / kWave];
-    __shared__ int carry;
+    __shared__ int red[kPlanThreads / kWave];
+    __shared__ int excl[kPlanUnits];
+    __shared__ int tile_total;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    if (tid == 0) carry = 0;
-    __syncthreads();
-    for (int base = 0; base < a.units; base += kPlanThreads) {
-        const int u = base + tid;
-        const int c = u < a.units ? a.cnt[u] : 0;
-        const int n = (c + a.split - 1) / a.split;
-        if (u < a.units && c <= 0) {
-            for (int i = 0; i < D; ++i) a.out[(size_t)u * D + i] = 0.f;
-            if (a.lse) a.lse[u] = -INFINITY;
-        }
-        // inclusive scan of n inside the wave, then across waves
-        int x = n;
+    const int u0 = blockIdx.x * kPlanUnits;
+    auto items_of = [&](int u) { return (a.cnt[u] + a.split - 1) / a.split; };
+
+    int before = 0;  // items of units [0, u0)
+    for (int u = tid; u < u0; u += kPlanThreads) before += items_of(u);
+#pragma unroll
+    for (int k = 1; k < kWave; k <<= 1) before += __shfl_xor(before, k, kWave);
+    if (lane == 0) red[wave] = before;
+    if (wave == 0) {
+        const int u = u0 + lane;
+        const int n = u < a.units ? items_of(u) : 0;
+        int x = n;  // inclusive scan over the tile's units
 #pragma unroll
         for (int k = 1; k < kWave; k <<= 1) {
             const int y = __shfl_up(x, k, kWave);
             if (lane >= k) x += y;
         }
-        if (lane == kWave - 1) wave_sum[wave] = x;
-        __syncthreads();
-        int before = carry;
-        for (int w = 0; w < wave; ++w) before += wave_sum[w];
-        const int off = before + x - n;  // exclusive offset of this unit's items
-        for (int j = 0; j < n; ++j) a.ws_items[off + j] = make_int2(u, j);
-        __syncthreads();
-        if (tid == kPlanThreads - 1) carry = before + x;
-        __syncthreads();
+        excl[lane] = x - n;
+        if (lane == kWave - 1) tile_total = x;
+    }
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanThreads / kWave; ++w) base += red[w];
+
+    for (int t = wave; t < kPlanUnits; t += kPlanThreads / kWave) {
+        const int u = u0 + t;
+        if (u >= a.units) break;
+        const int c = a.cnt[u];
+        if (c <= 0) {
+            for (int i = lane; i < D; i += kWave) a.out[(size_t)u * D + i] = 0.f;
+            if (lane == 0 && a.lse) a.lse[u] = -INFINITY;
+            continue;
+        }
+        const int n = (c + a.split - 1) / a.split;
+        const int off = base + excl[t];
+        for (int j = lane; j < n; j += kWave) a.ws_items[off + j] = make_int2(u, j);
     }
     if (tid == 0) {
-        a.ws_hdr[0] = carry;
-        a.ws_hdr[1] = 0;
+        if (blockIdx.x == gridDim.x - 1) a.ws_hdr[0] = base + tile_total;
+        if (blockIdx.x == 0) a.ws_hdr[1] = 0;
     }
 }
 
@@ -434,7 +451,8 @@ hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K,
     if (g.units == 0) return hipSuccess;
     const AttnArgs a = make_args(g, q, K, V, tau, adm_idx, adm_cnt, gate_beta, split_blocks,
                                  max_chunks, out, lse, ws);
-    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a, g.d);
+    hipLaunchKernelGGL(attn_plan_kernel, dim3((unsigned)((g.units + kPlanUnits - 1) / kPlanUnits)),
+                       dim3(kPlanThreads), 0, st, a, g.d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // persistent workers: a few per CU, never more than the largest possible item count

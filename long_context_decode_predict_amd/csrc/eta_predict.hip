@@ -21,7 +21,7 @@ constexpr int kPredHeads = 16;
 
 __global__ __launch_bounds__(kPredThreads) void predict_tau_kernel(
     int H, int HD, const float *__restrict__ q, const float *__restrict__ W,
-    const float *__restrict__ bias, float *__restrict__ tau) {
+    const float *__restrict__ bias, float *__restrict__ tau, int vec) {
     __shared__ float part[kPredThreads / kWave][kPredHeads];
     const int b = blockIdx.x;
     const int h0 = blockIdx.y * kPredHeads;
@@ -38,12 +38,29 @@ __global__ __launch_bounds__(kPredThreads) void predict_tau_kernel(
 #pragma unroll
     for (int j = 0; j < kPredHeads; ++j) acc[j] = 0.f;
     const float *qb = q + (size_t)b * HD;
-    for (int k = threadIdx.x; k < HD; k += kPredThreads) {
-        const float qv = qb[k];
-        const float *wr = W + (size_t)k * H + h0;
+    if (vec && nh == kPredHeads) {
+        // 16 whole heads and 16-byte aligned rows: four float4 loads per row slice
+#pragma unroll 4
+        for (int k = threadIdx.x; k < HD; k += kPredThreads) {
+            const float qv = qb[k];
+            const float4 *wr = reinterpret_cast<const float4 *>(W + (size_t)k * H + h0);
 #pragma unroll
-        for (int j = 0; j < kPredHeads; ++j)
-            if (j < nh) acc[j] += qv * wr[j];
+            for (int j4 = 0; j4 < kPredHeads / 4; ++j4) {
+                const float4 w4 = wr[j4];
+                acc[4 * j4 + 0] += qv * w4.x;
+                acc[4 * j4 + 1] += qv * w4.y;
+                acc[4 * j4 + 2] += qv * w4.z;
+                acc[4 * j4 + 3] += qv * w4.w;
+            }
+        }
+    } else {
+        for (int k = threadIdx.x; k < HD; k += kPredThreads) {
+            const float qv = qb[k];
+            const float *wr = W + (size_t)k * H + h0;
+#pragma unroll
+            for (int j = 0; j < kPredHeads; ++j)
+                if (j < nh) acc[j] += qv * wr[j];
+        }
     }
 #pragma unroll
     for (int j = 0; j < kPredHeads; ++j) {
@@ -65,8 +82,9 @@ __global__ __launch_bounds__(kPredThreads) void predict_tau_kernel(
 hipError_t launch_predict_tau(int B, int H, int d, const float *q, const float *W,
                               const float *bias, float *tau, hipStream_t st) {
     const dim3 grid((unsigned)B, (unsigned)((H + kPredHeads - 1) / kPredHeads));
+    const int vec = (H % 4 == 0) && (reinterpret_cast<uintptr_t>(W) % 16 == 0);
     hipLaunchKernelGGL(predict_tau_kernel, grid, dim3(kPredThreads), 0, st, H, H * d, q, W,
-                       bias, tau);
+                       bias, tau, vec);
     return hipGetLastError();
 }
 
