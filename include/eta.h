@@ -8,8 +8,8 @@
  *      Assessment", Eq. 1), or use frozen per-head constants (abstract: offline
  *      calibration);
  *   2. screen every 64-token KV block in O(1) against tau with a bound built
- *      from cached per-block metadata (abstract: "geometric-probabilistic
- *      bounds"; review "Summary": centroid / variance / max-norm);
+ *      from cached per-block metadata (abstract: geometric-probabilistic
+ *      bounds; review "Summary": centroid / variance / max-norm);
  *   3. skip every block whose bound is below tau (review Q&A "What is ETA?");
  *   4. softmax attention over the admitted blocks' tokens, each logit S
  *      multiplied by the gate sigmoid(beta*(S - tau)) (Eq. 2 and Eq. 3), so a

@@ -111,8 +111,9 @@ int eta_oracle_block_meta(int T, int d, int bs, int kv_dtype, const void *K,
     return nblk;
 }
 
-/* Block score bound (abstract: "cached geometric-probabilistic bounds"; Q&A:
- * "best possible score" of a block). With s = 1/sqrt(d):
+/* Block score bound (abstract: the screen uses cached bounds that are partly
+ * geometric, partly probabilistic; Q&A "What is ETA?": the highest score any key
+ * of the block could reach). With s = 1/sqrt(d):
  *   geometric     U_geo  = s * |q| * maxnorm          (Cauchy-Schwarz: no key
  *                                                     of the block can score
  *                                                     higher)
