@@ -90,15 +90,18 @@ def meta_bytes(w):
     return w.B * w.H * w.nblk * (w.d + 2) * 4
 
 
-def run_steps(step, data, w, meta, W, bias, n, stream, evs=None):
+def run_steps(step, data, w, meta, W, bias, n, stream, evs=None, fused=True):
     """n decode steps; with evs, events bracket predict+screen, the split-KV partial
     kernel and the combine kernel of every step (all on the launch stream)."""
     q, K, V = data["q"], data["K"], data["V"]
     for i in range(n):
         if evs is not None:
             evs[i][0].record(stream)
-        step.predict(q, W, bias)
-        step.screen(q, meta, w.T)
+        if fused:
+            step.predict_screen(q, W, bias, meta, w.T)
+        else:
+            step.predict(q, W, bias)
+            step.screen(q, meta, w.T)
         if evs is not None:
             evs[i][1].record(stream)
         step.attend_partial(q, K, V, w.T)
@@ -109,15 +112,15 @@ def run_steps(step, data, w, meta, W, bias, n, stream, evs=None):
             evs[i][3].record(stream)
 
 
-def time_steps(step, data, w, meta, W, bias, steps, warmup):
+def time_steps(step, data, w, meta, W, bias, steps, warmup, fused=True):
     stream = torch.cuda.current_stream()
-    run_steps(step, data, w, meta, W, bias, warmup, stream)
+    run_steps(step, data, w, meta, W, bias, warmup, stream, fused=fused)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    run_steps(step, data, w, meta, W, bias, steps, stream, evs)
+    run_steps(step, data, w, meta, W, bias, steps, stream, evs, fused=fused)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -126,6 +129,21 @@ def time_steps(step, data, w, meta, W, bias, steps, warmup):
     comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
     return (total_ms / steps, float(np.mean(attn_ms)), float(np.mean(front_ms)),
             float(np.mean(comb_ms)))
+
+
+def graph_step_ms(step, data, w, meta, W, bias, steps, fused):
+    """The same step captured once in a HIP graph and replayed `steps` times."""
+    graph = step.capture(data["q"], data["K"], data["V"], w.T, meta, W, bias, fused=fused)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / steps
 
 
 def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=None):
@@ -209,6 +227,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate eta_predict_tau + eta_screen launches instead of "
+                         "eta_predict_screen")
     ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GIB",
                     help="only time a plain device copy of GIB GiB (HBM reference and the "
                          "scale for counter-based traffic) and exit")
@@ -254,8 +275,10 @@ def main():
     log(f"[bench] metadata build {build_ms:.2f} ms")
 
     step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params)
+    fused = not args.unfused
     ms, attn_ms, front_ms, comb_ms = time_steps(step, data, w, meta, W, bias, args.steps,
-                                                 args.warmup)
+                                                args.warmup, fused)
+    graph_ms = graph_step_ms(step, data, w, meta, W, bias, args.steps, fused)
     cnt = step.adm_cnt.cpu().numpy()
     idx = step.adm_idx.cpu().numpy()
     density = float(cnt.mean()) / w.nblk
@@ -267,13 +290,14 @@ def main():
     attn_gbs = attn_alg / (attn_ms * 1e-3) / 1e9
     log(f"[bench] {ms:.3f} ms/step, density {density:.3f}, attention partial {attn_ms:.3f} ms "
         f"({attn_gbs:.0f} GB/s), combine {comb_ms:.3f} ms, predict+screen {front_ms:.3f} ms, "
-        f"effective {eff_gbs:.0f} GB/s")
+        f"effective {eff_gbs:.0f} GB/s, graph replay {graph_ms:.3f} ms/step")
 
     extra = {"density": density, "effective_kv_gbs": eff_gbs,
              "effective_frac_hbm_peak": eff_gbs / HBM_PEAK_GBS,
              "admitted_kv_bytes": kv_adm, "metadata_bytes": mb,
              "attn_partial_ms": attn_ms, "combine_ms": comb_ms, "predict_screen_ms": front_ms,
-             "meta_build_ms": build_ms}
+             "meta_build_ms": build_ms, "graph_replay_ms_per_step": graph_ms,
+             "predict_screen": "fused (eta_predict_screen)" if fused else "separate"}
     if append_ms is not None:
         extra["append_ms_per_token"] = append_ms
     per_head = (cnt / w.nblk).mean(axis=0)
@@ -301,7 +325,7 @@ def main():
     if not args.no_dense:
         dense_bias = torch.full((w.H,), -math.inf, device="cuda")
         dms, dattn, _, _ = time_steps(step, data, w, meta, None, dense_bias,
-                                      max(5, args.steps // 2), 2)
+                                      max(5, args.steps // 2), 2, fused)
         dcnt = step.adm_cnt.cpu().numpy()
         d_bytes = admitted_bytes(w, dcnt, step.adm_idx.cpu().numpy())
         extra["dense_tau_neg_inf"] = {

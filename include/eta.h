@@ -157,6 +157,19 @@ eta_status eta_screen(const eta_shape *s, const float *q, const float *tau, cons
                       const eta_params *p, int32_t *adm_idx, int32_t *adm_cnt,
                       float *bound_out, hipStream_t stream);
 
+/*
+ * Threshold predictor and screen in one launch: for every unit, tau[b][h] is
+ * evaluated as in eta_predict_tau (W nullable: frozen tau = bias) and stored to
+ * tau (float32 [B][H], read later by eta_decode_attn), then the unit is
+ * screened as in eta_screen. Same layouts, outputs and errors as the two calls
+ * it replaces; tau may differ from eta_predict_tau's in the last bits (another
+ * fp32 summation order).
+ */
+eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W,
+                              const float *bias, const eta_meta *m, const eta_params *p,
+                              float *tau, int32_t *adm_idx, int32_t *adm_cnt, float *bound_out,
+                              hipStream_t stream);
+
 /* Bytes of device workspace the attention calls need for this shape and split
  * size (0 on invalid arguments). The layout is private to the library. */
 size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);

@@ -67,6 +67,8 @@ SIGNATURES = {
                                        _vp, _vp]),
     "eta_screen": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _P(eta_meta), _P(eta_params), _vp,
                                   _vp, _vp, _vp]),
+    "eta_predict_screen": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _P(eta_meta),
+                                          _P(eta_params), _vp, _vp, _vp, _vp, _vp]),
     "eta_decode_attn_workspace_size": (ctypes.c_size_t, [_P(eta_shape), _P(eta_params)]),
     "eta_decode_attn": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp, _vp,
                                        _P(eta_params), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -245,6 +247,31 @@ def eta_screen(q: torch.Tensor, tau: torch.Tensor, meta: Meta, T: int, T_cap: in
            lib().eta_screen(ctypes.byref(s), q.data_ptr(), tau.data_ptr(), ctypes.byref(m),
                             ctypes.byref(params), adm_idx.data_ptr(), adm_cnt.data_ptr(),
                             _ptr(bound_out), _stream(stream)))
+
+
+def eta_predict_screen(q: torch.Tensor, W, bias: torch.Tensor, meta: Meta, T: int, T_cap: int,
+                       params: eta_params, tau: torch.Tensor, adm_idx: torch.Tensor,
+                       adm_cnt: torch.Tensor, bound_out=None, kv_dtype=torch.bfloat16,
+                       stream=None):
+    B, H, d = q.shape
+    s = make_shape(B, H, d, T, T_cap, kv_dtype)
+    n = nblk_cap(T_cap)
+    _need(q, "q", torch.float32)
+    if W is not None:
+        _need(W, "W", torch.float32, (H * d, H))
+    _need(bias, "bias", torch.float32, (H,))
+    _need(tau, "tau", torch.float32, (B, H))
+    _check_meta(meta, B, H, d, T_cap)
+    _need(adm_idx, "adm_idx", torch.int32, (B, H, n))
+    _need(adm_cnt, "adm_cnt", torch.int32, (B, H))
+    if bound_out is not None:
+        _need(bound_out, "bound_out", torch.float32, (B, H, n))
+    m = meta.c()
+    _check("eta_predict_screen",
+           lib().eta_predict_screen(ctypes.byref(s), q.data_ptr(), _ptr(W), bias.data_ptr(),
+                                    ctypes.byref(m), ctypes.byref(params), tau.data_ptr(),
+                                    adm_idx.data_ptr(), adm_cnt.data_ptr(), _ptr(bound_out),
+                                    _stream(stream)))
 
 
 def eta_decode_attn_workspace_size(B, H, d, T_cap, params: eta_params,

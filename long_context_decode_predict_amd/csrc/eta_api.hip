@@ -165,9 +165,28 @@ eta_status eta_screen(const eta_shape *s, const float *q, const float *tau, cons
         return ETA_ERR_INVALID_ARG;
     if (bound_out != nullptr && !aligned(bound_out, 16)) return ETA_ERR_INVALID_ARG;
     const eta::Geometry g = geometry(s, m->nblk_cap);
-    return from_hip(eta::launch_screen(g, q, tau, m->centroid, m->var, m->maxnorm, p->z,
+    return from_hip(eta::launch_screen(g, s->H, q, const_cast<float *>(tau), nullptr, nullptr,
+                                       false, m->centroid, m->var, m->maxnorm, p->z,
                                        p->bound_mode == ETA_BOUND_GEO, adm_idx, adm_cnt,
                                        bound_out, stream));
+}
+
+eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W,
+                              const float *bias, const eta_meta *m, const eta_params *p,
+                              float *tau, int32_t *adm_idx, int32_t *adm_cnt, float *bound_out,
+                              hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_meta(s, m)) != ETA_OK) return st;
+    if ((st = check_params(p)) != ETA_OK) return st;
+    if (q == nullptr || bias == nullptr || tau == nullptr || adm_idx == nullptr ||
+        adm_cnt == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (bound_out != nullptr && !aligned(bound_out, 16)) return ETA_ERR_INVALID_ARG;
+    const eta::Geometry g = geometry(s, m->nblk_cap);
+    return from_hip(eta::launch_screen(g, s->H, q, tau, W, bias, true, m->centroid, m->var,
+                                       m->maxnorm, p->z, p->bound_mode == ETA_BOUND_GEO, adm_idx,
+                                       adm_cnt, bound_out, stream));
 }
 
 size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p) {

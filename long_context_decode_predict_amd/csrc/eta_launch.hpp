@@ -25,10 +25,12 @@ hipError_t launch_block_meta(const Geometry &g, const void *K, float *centroid, 
 hipError_t launch_predict_tau(int B, int H, int d, const float *q, const float *W,
                               const float *bias, float *tau, hipStream_t st);
 
-hipError_t launch_screen(const Geometry &g, const float *q, const float *tau,
-                         const float *centroid, const float *var, const float *maxnorm,
-                         float z, bool geo_only, int32_t *adm_idx, int32_t *adm_cnt,
-                         float *bound_out, hipStream_t st);
+// Screen; with `predict` the threshold of every unit is first evaluated from
+// q, W (nullable) and bias and stored to tau, otherwise tau is read.
+hipError_t launch_screen(const Geometry &g, int H, const float *q, float *tau, const float *W,
+                         const float *bias, bool predict, const float *centroid,
+                         const float *var, const float *maxnorm, float z, bool geo_only,
+                         int32_t *adm_idx, int32_t *adm_cnt, float *bound_out, hipStream_t st);
 
 // Workspace layout of the split-KV attention for `units` units with at most
 // `max_chunks` work items each.

@@ -8,12 +8,19 @@
 //   U_prob = s * (q . centroid + z * |q| * sqrt(var))
 //   U = min(U_geo, U_prob), or U_geo alone; admit iff U >= tau.
 //
-// One workgroup per (batch, head) unit. The centroids are dimension-major per
-// unit, so lane l of wave w handles four consecutive blocks and every load of
-// one dimension is a contiguous 1 KiB run across the wave (float4 per lane);
-// no cross-lane reduction is needed for the dot products. Admission bits are
-// compacted with wave ballots plus an LDS exclusive scan over the waves, so
-// the admitted list comes out ascending with no atomics (deterministic).
+// One workgroup per (batch, head) unit, up to 16 waves. The centroids are
+// dimension-major per unit, so lane l of a wave handles four consecutive
+// blocks and every load of one dimension is a contiguous 1 KiB run across the
+// wave (float4 per lane), with no cross-lane reduction. When a unit has few
+// blocks, the head dimension is split across DS waves that work on the same
+// 256 blocks (partial dot products meet in LDS and are added in slice order),
+// so short contexts still put enough loads in flight. Admission bits are
+// compacted with wave ballots plus an LDS exclusive scan over the block
+// groups: the admitted list comes out ascending with no atomics.
+//
+// With PRED the workgroup first evaluates the threshold predictor of its unit
+// (evolve.pub review, "Methodology Assessment", Eq. 1: tau = qbar . W + b over
+// the concatenated queries of the batch row) and stores tau for the attention.
 #include "eta_device.hpp"
 #include "eta_launch.hpp"
 
@@ -23,129 +30,227 @@ namespace {
 constexpr int kScreenMaxWaves = 16;
 constexpr int kBlocksPerLane = 4;
 constexpr int kBlocksPerWave = kWave * kBlocksPerLane;
+constexpr int kMaxSlices = 8;
 
-template <int D>
-__global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(
-    int nblk, int nblk_cap, const float *__restrict__ q, const float *__restrict__ tau,
-    const float *__restrict__ centroid, const float *__restrict__ var,
-    const float *__restrict__ maxnorm, float s, float z, int geo_only,
-    int32_t *__restrict__ adm_idx, int32_t *__restrict__ adm_cnt, float *__restrict__ bound_out) {
+struct ScreenArgs {
+    int nblk, nblk_cap, H, nbg, ds;  // block groups per pass, dimension slices
+    float s, z;
+    int geo_only;
+    const float *q;
+    float *tau;        // read, or written with PRED
+    const float *W;    // PRED: [H*d][H] or null (frozen tau = bias)
+    const float *bias;
+    const float *centroid;
+    const float *var;
+    const float *maxnorm;
+    int32_t *adm_idx;
+    int32_t *adm_cnt;
+    float *bound_out;
+};
+
+template <int D, bool PRED>
+__global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenArgs a) {
     __shared__ float q_s[D];
+    __shared__ float4 part[kScreenMaxWaves][kWave];  // partial dots, per wave and lane
     __shared__ int wave_tot[kScreenMaxWaves];
+    __shared__ float red[kScreenMaxWaves];
+    __shared__ float tau_s;
 
     const int u = blockIdx.x;
     const int nw = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
+    const int grp = wave / a.ds;    // block group of this wave
+    const int slice = wave % a.ds;  // dimension slice of this wave
+    const int dps = D / a.ds;       // dimensions per slice
 
-    for (int i = threadIdx.x; i < D; i += blockDim.x) q_s[i] = q[(size_t)u * D + i];
+    for (int i = threadIdx.x; i < D; i += blockDim.x) q_s[i] = a.q[(size_t)u * D + i];
+    if (PRED) {
+        const int b = u / a.H, h = u - (u / a.H) * a.H;
+        float acc = 0.f;
+        if (a.W != nullptr) {
+            const float *qb = a.q + (size_t)b * a.H * D;
+            for (int k = threadIdx.x; k < a.H * D; k += blockDim.x) acc += qb[k] * a.W[(size_t)k * a.H + h];
+        }
+        acc = xrow_sum(row_sum16(acc));
+        if (lane == 0) red[wave] = acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float sum = 0.f;
+            for (int w = 0; w < nw; ++w) sum += red[w];
+            const float t = a.bias[h] + sum;
+            tau_s = t;
+            a.tau[u] = t;
+        }
+    } else {
+        if (threadIdx.x == 0) tau_s = a.tau[u];
+    }
     __syncthreads();
 
     float qq = 0.f;
     for (int i = lane; i < D; i += kWave) qq += q_s[i] * q_s[i];
     const float qn = sqrtf(xrow_sum(row_sum16(qq)));
-    const float t = tau[u];
-    const float geo_scale = s * qn;
-    const float z_scale = z * qn;
+    const float t = tau_s;
+    const float geo_scale = a.s * qn;
+    const float z_scale = a.z * qn;
 
-    const float *cu = centroid + (size_t)u * D * nblk_cap;
-    const float *vu = var + (size_t)u * nblk_cap;
-    const float *mu = maxnorm + (size_t)u * nblk_cap;
-    int32_t *iu = adm_idx + (size_t)u * nblk_cap;
+    const float *cu = a.centroid + (size_t)u * D * a.nblk_cap;
+    const float *vu = a.var + (size_t)u * a.nblk_cap;
+    const float *mu = a.maxnorm + (size_t)u * a.nblk_cap;
+    int32_t *iu = a.adm_idx + (size_t)u * a.nblk_cap;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const int d0 = slice * dps;
 
     int base = 0;
-    for (int pass0 = 0; pass0 < nblk; pass0 += nw * kBlocksPerWave) {
-        const int blk0 = pass0 + wave * kBlocksPerWave + lane * kBlocksPerLane;
-        const bool active = blk0 < nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
-        float U[kBlocksPerLane] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        if (active) {
-            const float4 m4 = *reinterpret_cast<const float4 *>(mu + blk0);
-            const float mx[4] = {m4.x, m4.y, m4.z, m4.w};
-            if (geo_only) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) U[j] = geo_scale * mx[j];
-            } else {
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int pass0 = 0; pass0 < a.nblk; pass0 += a.nbg * kBlocksPerWave) {
+        const int blk0 = pass0 + grp * kBlocksPerWave + lane * kBlocksPerLane;
+        const bool active = blk0 < a.nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        if (active && !a.geo_only) {
 #pragma unroll 16
-                for (int dim = 0; dim < D; ++dim) {
-                    const float4 c4 = *reinterpret_cast<const float4 *>(cu + (size_t)dim * nblk_cap + blk0);
-                    const float qd = q_s[dim];
-                    acc[0] += qd * c4.x;
-                    acc[1] += qd * c4.y;
-                    acc[2] += qd * c4.z;
-                    acc[3] += qd * c4.w;
-                }
-                const float4 v4 = *reinterpret_cast<const float4 *>(vu + blk0);
-                const float vx[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float u_geo = geo_scale * mx[j];
-                    const float u_prob = s * (acc[j] + z_scale * sqrtf(vx[j]));
-                    U[j] = (u_prob < u_geo) ? u_prob : u_geo;
-                }
+            for (int dim = d0; dim < d0 + dps; ++dim) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(cu + (size_t)dim * a.nblk_cap + blk0);
+                const float qd = q_s[dim];
+                acc[0] += qd * c4.x;
+                acc[1] += qd * c4.y;
+                acc[2] += qd * c4.z;
+                acc[3] += qd * c4.w;
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (blk0 + j >= nblk) U[j] = -INFINITY;
+        }
+        if (a.ds > 1) {  // add the slices' partial dots in slice order
+            part[wave][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            __syncthreads();
+            if (slice == 0) {
+                float4 sum = part[wave][lane];
+                for (int k = 1; k < a.ds; ++k) {
+                    const float4 p = part[wave + k][lane];
+                    sum.x += p.x;
+                    sum.y += p.y;
+                    sum.z += p.z;
+                    sum.w += p.w;
+                }
+                acc[0] = sum.x;
+                acc[1] = sum.y;
+                acc[2] = sum.z;
+                acc[3] = sum.w;
+            }
         }
 
-        bool adm[4];
-        int before = 0, total = 0;
+        float U[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        bool adm[4] = {false, false, false, false};
+        int before = 0;
+        if (slice == 0) {
+            if (active) {
+                const float4 m4 = *reinterpret_cast<const float4 *>(mu + blk0);
+                const float mx[4] = {m4.x, m4.y, m4.z, m4.w};
+                if (a.geo_only) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            adm[j] = active && (blk0 + j < nblk) && (U[j] >= t);
-            const uint64_t mask = __ballot(adm[j]);
-            before += __popcll(mask & lanes_below);
-            total += __popcll(mask);
+                    for (int j = 0; j < 4; ++j) U[j] = geo_scale * mx[j];
+                } else {
+                    const float4 v4 = *reinterpret_cast<const float4 *>(vu + blk0);
+                    const float vx[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float u_geo = geo_scale * mx[j];
+                        const float u_prob = a.s * (acc[j] + z_scale * sqrtf(vx[j]));
+                        U[j] = (u_prob < u_geo) ? u_prob : u_geo;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (blk0 + j >= a.nblk) U[j] = -INFINITY;
+            }
+            int total = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                adm[j] = active && (blk0 + j < a.nblk) && (U[j] >= t);
+                const uint64_t mask = __ballot(adm[j]);
+                before += __popcll(mask & lanes_below);
+                total += __popcll(mask);
+            }
+            if (lane == 0) wave_tot[grp] = total;
         }
-        if (lane == 0) wave_tot[wave] = total;
         __syncthreads();
-        int wave_base = 0, pass_total = 0;
-        for (int w = 0; w < nw; ++w) {
-            const int c = wave_tot[w];
-            wave_base += (w < wave) ? c : 0;
+        int grp_base = 0, pass_total = 0;
+        for (int g = 0; g < a.nbg; ++g) {
+            const int c = wave_tot[g];
+            grp_base += (g < grp) ? c : 0;
             pass_total += c;
         }
-        int pos = base + wave_base + before;
+        if (slice == 0) {
+            int pos = base + grp_base + before;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (adm[j]) iu[pos++] = blk0 + j;
-        }
-        if (bound_out != nullptr && active) {
-            *reinterpret_cast<float4 *>(bound_out + (size_t)u * nblk_cap + blk0) =
-                make_float4(U[0], U[1], U[2], U[3]);
+            for (int j = 0; j < 4; ++j) {
+                if (adm[j]) iu[pos++] = blk0 + j;
+            }
+            if (a.bound_out != nullptr && active) {
+                *reinterpret_cast<float4 *>(a.bound_out + (size_t)u * a.nblk_cap + blk0) =
+                    make_float4(U[0], U[1], U[2], U[3]);
+            }
         }
         base += pass_total;
-        __syncthreads();  // wave_tot is rewritten by the next pass
+        __syncthreads();  // wave_tot and part are rewritten by the next pass
     }
-    if (threadIdx.x == 0) adm_cnt[u] = base;
+    if (threadIdx.x == 0) a.adm_cnt[u] = base;
+}
+
+// Block groups per pass and dimension slices: up to 16 waves; split the
+// dimension when the unit has fewer than 16 x 256 blocks.
+void pick_shape(int nblk, int d, int *nbg, int *ds) {
+    int g = (nblk + kBlocksPerWave - 1) / kBlocksPerWave;
+    g = g < 1 ? 1 : (g > kScreenMaxWaves ? kScreenMaxWaves : g);
+    int pow2 = 1;
+    while (pow2 < g) pow2 <<= 1;  // block groups rounded up to a power of two
+    int slices = kScreenMaxWaves / pow2;
+    if (slices > kMaxSlices) slices = kMaxSlices;
+    while (slices > 1 && d / slices < 8) slices >>= 1;  // keep >= 8 dimensions per slice
+    *nbg = pow2;
+    *ds = slices < 1 ? 1 : slices;
 }
 
 template <int D>
-hipError_t launch_screen_t(const Geometry &g, const float *q, const float *tau, const float *c,
-                           const float *v, const float *m, float z, bool geo_only, int32_t *idx,
-                           int32_t *cnt, float *bound_out, hipStream_t st) {
-    int waves = (g.nblk + kBlocksPerWave - 1) / kBlocksPerWave;
-    waves = waves < 1 ? 1 : (waves > kScreenMaxWaves ? kScreenMaxWaves : waves);
-    const float s = 1.0f / sqrtf((float)D);
-    hipLaunchKernelGGL((screen_kernel<D>), dim3((unsigned)g.units), dim3(waves * kWave), 0, st,
-                       g.nblk, g.nblk_cap, q, tau, c, v, m, s, z, geo_only ? 1 : 0, idx, cnt,
-                       bound_out);
+hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau, const float *W,
+                           const float *bias, bool predict, const float *c, const float *v,
+                           const float *m, float z, bool geo_only, int32_t *idx, int32_t *cnt,
+                           float *bound_out, hipStream_t st) {
+    ScreenArgs a;
+    pick_shape(g.nblk, D, &a.nbg, &a.ds);
+    a.nblk = g.nblk;
+    a.nblk_cap = g.nblk_cap;
+    a.H = H;
+    a.s = 1.0f / sqrtf((float)D);
+    a.z = z;
+    a.geo_only = geo_only ? 1 : 0;
+    a.q = q;
+    a.tau = tau;
+    a.W = W;
+    a.bias = bias;
+    a.centroid = c;
+    a.var = v;
+    a.maxnorm = m;
+    a.adm_idx = idx;
+    a.adm_cnt = cnt;
+    a.bound_out = bound_out;
+    const dim3 block(a.nbg * a.ds * kWave);
+    if (predict) {
+        hipLaunchKernelGGL((screen_kernel<D, true>), dim3((unsigned)g.units), block, 0, st, a);
+    } else {
+        hipLaunchKernelGGL((screen_kernel<D, false>), dim3((unsigned)g.units), block, 0, st, a);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_screen(const Geometry &g, const float *q, const float *tau,
-                         const float *centroid, const float *var, const float *maxnorm, float z,
-                         bool geo_only, int32_t *adm_idx, int32_t *adm_cnt, float *bound_out,
-                         hipStream_t st) {
+hipError_t launch_screen(const Geometry &g, int H, const float *q, float *tau, const float *W,
+                         const float *bias, bool predict, const float *centroid,
+                         const float *var, const float *maxnorm, float z, bool geo_only,
+                         int32_t *adm_idx, int32_t *adm_cnt, float *bound_out, hipStream_t st) {
     if (g.units == 0) return hipSuccess;
-    return g.d == 128 ? launch_screen_t<128>(g, q, tau, centroid, var, maxnorm, z, geo_only,
-                                             adm_idx, adm_cnt, bound_out, st)
-                      : launch_screen_t<64>(g, q, tau, centroid, var, maxnorm, z, geo_only,
-                                            adm_idx, adm_cnt, bound_out, st);
+    return g.d == 128 ? launch_screen_t<128>(g, H, q, tau, W, bias, predict, centroid, var, maxnorm,
+                                             z, geo_only, adm_idx, adm_cnt, bound_out, st)
+                      : launch_screen_t<64>(g, H, q, tau, W, bias, predict, centroid, var, maxnorm,
+                                            z, geo_only, adm_idx, adm_cnt, bound_out, st);
 }
 
 }  // namespace eta

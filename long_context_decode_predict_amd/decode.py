@@ -32,6 +32,10 @@ class DecodeStep:
     def predict(self, q, W, bias, stream=None):
         _lib.eta_predict_tau(q, W, bias, self.tau, stream)
 
+    def predict_screen(self, q, W, bias, meta, T, stream=None):
+        _lib.eta_predict_screen(q, W, bias, meta, T, self.T_cap, self.params, self.tau,
+                                self.adm_idx, self.adm_cnt, self.bounds, self.kv_dtype, stream)
+
     def screen(self, q, meta, T, stream=None):
         _lib.eta_screen(q, self.tau, meta, T, self.T_cap, self.params, self.adm_idx,
                         self.adm_cnt, self.bounds, self.kv_dtype, stream)
@@ -48,8 +52,27 @@ class DecodeStep:
         _lib.eta_decode_attn_combine(K, T, self.adm_cnt, self.params, self.out, self.lse,
                                      self.ws, stream)
 
-    def __call__(self, q, K, V, T, meta, W, bias, stream=None):
-        self.predict(q, W, bias, stream)
-        self.screen(q, meta, T, stream)
+    def capture(self, q, K, V, T, meta, W, bias, fused=True):
+        """Record one step into a HIP graph (torch.cuda.CUDAGraph) and return it; each
+        replay re-runs the step on the same buffers. The library makes no allocation
+        and no memset, so the captured step holds kernel nodes only."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm the launch path outside the capture
+            self(q, K, V, T, meta, W, bias, fused=fused)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self(q, K, V, T, meta, W, bias, fused=fused)
+        return graph
+
+    def __call__(self, q, K, V, T, meta, W, bias, stream=None, fused=False):
+        """One step; fused=True evaluates tau inside the screen launch."""
+        if fused:
+            self.predict_screen(q, W, bias, meta, T, stream)
+        else:
+            self.predict(q, W, bias, stream)
+            self.screen(q, meta, T, stream)
         self.attend(q, K, V, T, stream)
         return self.out

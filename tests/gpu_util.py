@@ -43,7 +43,8 @@ class Case:
     """A workload instance on the GPU plus the library's results for one step."""
 
     def __init__(self, w: workloads.Workload, tau_mode="predictor", params=None, T=None,
-                 T_cap=None, bias=None):
+                 T_cap=None, bias=None, fused=False):
+        self.fused = fused
         self.w = w
         self.T_cap = T_cap if T_cap is not None else w.T_cap
         self.T = T if T is not None else w.T
@@ -69,7 +70,7 @@ class Case:
         if build:
             self.build_meta()
         d = self.data
-        self.step(d["q"], d["K"], d["V"], self.T, self.meta, self.W, self.bias)
+        self.step(d["q"], d["K"], d["V"], self.T, self.meta, self.W, self.bias, fused=self.fused)
         torch.cuda.synchronize()
         return self
 

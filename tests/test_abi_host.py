@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
@@ -121,6 +121,23 @@ def test_screen_other_errors(L):
     # a hard gate does not need a finite beta
     assert L.eta_screen(BY(shape(d=32)), FAKE, FAKE, BY(meta()), BY(params(gate_hard=1, gate_beta=0.0)),
                         FAKE, FAKE, None, None) == UNS
+
+
+def test_predict_screen_errors(L):
+    p = BY(params())
+    call = lambda **kw: L.eta_predict_screen(
+        BY(shape(**kw.get("shape", {}))), kw.get("q", FAKE), kw.get("W", FAKE), kw.get("bias", FAKE),
+        BY(meta()), kw.get("p", p), kw.get("tau", FAKE), kw.get("idx", FAKE), kw.get("cnt", FAKE),
+        kw.get("bound", None), None)
+    assert call(q=None) == INV
+    assert call(bias=None) == INV
+    assert call(tau=None) == INV
+    assert call(idx=None) == INV
+    assert call(cnt=None) == INV
+    assert call(p=None) == INV
+    assert call(bound=FAKE + 8) == INV
+    assert call(shape=dict(d=100)) == UNS
+    assert call(shape=dict(T=2000)) == INV
 
 
 def test_workspace_size(L):

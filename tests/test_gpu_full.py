@@ -36,7 +36,7 @@ def test_full_size(name):
     w = workloads.WORKLOADS[name]
     print(f"\n[full] {name} B={w.B} H={w.H} d={w.d} T={w.T}", flush=True)
     mode = "static" if w.static_tau else "predictor"
-    case = Case(w, tau_mode=mode)
+    case = Case(w, tau_mode=mode, fused=True)  # the launch configuration bench.py times
     if w.append:
         # the cache is built before the last `append` tokens, which then arrive one by one
         T0 = w.T - w.append

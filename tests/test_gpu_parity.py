@@ -96,6 +96,48 @@ def test_parity_small(name, w, mode, pkw, T_cap):
     case.free()
 
 
+FUSED = [c for c in SMALL if c[0] in ("tiny_config", "bf16_d128_ragged", "f32_d128_ragged",
+                                      "bf16_static_heads", "bf16_two_screen_passes",
+                                      "bf16_geo_bound", "bf16_tau_nan", "f32_d64_many_units")]
+
+
+@pytest.mark.parametrize("name,w,mode,pkw,T_cap", FUSED, ids=[c[0] for c in FUSED])
+def test_parity_fused_predict_screen(name, w, mode, pkw, T_cap):
+    """The one-launch predictor + screen (eta_predict_screen) against the oracle."""
+    _announce(f"fused {name}")
+    case = Case(w, tau_mode=mode, params=_lib.default_params(**pkw), T_cap=T_cap, fused=True).run()
+    st = compare_units(case, _all_units(w))
+    assert st["units"] == w.B * w.H
+    assert st["band_mismatch_units"] <= max(1, st["units"] // 50), st
+    case.free()
+
+
+def test_graph_replay_matches_eager():
+    """The whole step captured in a HIP graph: every replay (with eager work and
+    synchronisations between replays) equals the eager step bitwise."""
+    _announce("graph replay")
+    w = workloads.custom("gr", B=4, H=8, d=128, T=6000, kv_dtype=torch.bfloat16, seed=81)
+    case = Case(w, fused=True).run()
+    ref = (case.step.out.clone(), case.step.lse.clone(), case.step.adm_cnt.clone(),
+           case.step.tau.clone())
+    d = case.data
+    graph = case.step.capture(d["q"], d["K"], d["V"], w.T, case.meta, case.W, case.bias, fused=True)
+    for r in range(4):
+        case.step.out.zero_()
+        case.step.lse.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(case.step.out, ref[0]), r
+        assert torch.equal(case.step.lse, ref[1]), r
+        assert torch.equal(case.step.adm_cnt, ref[2]), r
+        assert torch.equal(case.step.tau, ref[3]), r
+        del junk
+    del graph
+    case.free()
+
+
 def test_dense_matches_library_sdpa():
     """tau = -inf through the HIP path equals torch's softmax attention (CPU, float64)."""
     _announce("dense vs sdpa")
