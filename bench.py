@@ -87,7 +87,7 @@ def counter_traffic(workload: str):
 
 
 def meta_bytes(w):
-    return w.B * w.H * w.nblk * (w.d + 2) * 4
+    return w.B * w.kv_heads * w.nblk * (w.d + 2) * 4
 
 
 def run_steps(step, data, w, meta, W, bias, n, stream, evs=None, fused=True):
@@ -148,17 +148,19 @@ def graph_step_ms(step, data, w, meta, W, bias, steps, fused):
 
 def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=None):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload, timed on
-    the host cores: predictor + bound + screen + gated attention for the sampled units,
-    given metadata it built beforehand; scaled to steps/s of the whole workload."""
+    the host cores: predictor + bound + screen (+ union for grouped heads) + gated
+    attention for the sampled key/value units' query heads, given metadata it built
+    beforehand; scaled to steps/s of the whole workload."""
     from concurrent.futures import ThreadPoolExecutor
 
     from oracle import oracle as oracle_mod
 
     O = oracle_mod.default()
-    units_total = w.B * w.H
-    n = min(max_units, units_total)
+    G = w.G
+    kv_total = w.B * w.kv_heads
+    n = max(1, min(max_units // G, kv_total))
     rng = np.random.default_rng(w.seed + 99)
-    units = np.sort(rng.choice(units_total, size=n, replace=False))
+    units = np.sort(rng.choice(kv_total, size=n, replace=False))
     q = data["q"].cpu().numpy()
     Wn = None if W is None else W.cpu().numpy()
     bn = bias.cpu().numpy()
@@ -170,8 +172,8 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=N
 
     slabs = []
     for u in units:
-        b, h = divmod(int(u), w.H)
-        slabs.append((b, h, host(data["K"][b, h, :w.T]), host(data["V"][b, h, :w.T])))
+        b, k = divmod(int(u), w.kv_heads)
+        slabs.append((b, k, host(data["K"][b, k, :w.T]), host(data["V"][b, k, :w.T])))
     threads = threads or min(16, os.cpu_count() or 1)
     with ThreadPoolExecutor(threads) as ex:
         metas = list(ex.map(lambda s: O.block_meta(s[2], w.T), slabs))
@@ -179,22 +181,29 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=N
         taus = {}
 
         def work(i):
-            b, h, Kh, Vh = slabs[i]
-            tau = taus[b][h]
-            r = O.unit_step(q[b, h], Kh, Vh, w.T, tau, metas[i], z=params.z,
-                            mode=params.bound_mode, beta=params.gate_beta,
-                            hard=bool(params.gate_hard))
-            return len(r["idx"])
+            b, k, Kh, Vh = slabs[i]
+            lists = []
+            for j in range(G):
+                h = k * G + j
+                U = O.bounds(q[b, h], *metas[i], z=params.z, mode=params.bound_mode)
+                lists.append(O.screen(U, taus[b][h]))
+            adm = lists[0] if G == 1 else O.union(lists, w.nblk)
+            for j in range(G):
+                h = k * G + j
+                O.attend(q[b, h], Kh, Vh, w.T, taus[b][h], adm, beta=params.gate_beta,
+                         hard=bool(params.gate_hard))
+            return len(adm)
 
         t0 = time.perf_counter()
         for b in rows:  # Eq. 1 once per sampled batch row
             taus[b] = O.predict_tau(q[b:b + 1], Wn, bn)[0]
         list(ex.map(work, range(n)))
         dt = time.perf_counter() - t0
-    step_s = dt * units_total / n
+    step_s = dt * kv_total / n
+    what = "(batch, head)" if G == 1 else f"(batch, key/value head) units of {G} query heads,"
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {units_total} (batch, head) units of the same workload, "
-                      f"{dt:.2f} s wall on {threads} threads, scaled by {units_total}/{n}",
+            "sample": f"{n} of {kv_total} {what} units of the same workload, "
+                      f"{dt:.2f} s wall on {threads} threads, scaled by {kv_total}/{n}",
             "gpu_over_cpu": (1000.0 / step_gpu_ms) * step_s}
 
 
@@ -255,7 +264,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] generated in {time.time() - t0:.1f}s")
 
-    meta = _lib.Meta.alloc(w.B, w.H, w.d, w.T_cap)
+    meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, w.T_cap)
     append_ms = None
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if w.append:
@@ -274,19 +283,21 @@ def main():
     build_ms = ev0.elapsed_time(ev1)
     log(f"[bench] metadata build {build_ms:.2f} ms")
 
-    step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params)
+    step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params, H_kv=w.kv_heads)
     fused = not args.unfused
     ms, attn_ms, front_ms, comb_ms = time_steps(step, data, w, meta, W, bias, args.steps,
                                                 args.warmup, fused)
     graph_ms = graph_step_ms(step, data, w, meta, W, bias, args.steps, fused)
-    cnt = step.adm_cnt.cpu().numpy()
+    cnt = step.adm_cnt.cpu().numpy()      # per query head
     idx = step.adm_idx.cpu().numpy()
+    ucnt = step.uni_cnt.cpu().numpy()     # per key/value head (the loaded blocks)
+    uidx = step.uni_idx.cpu().numpy()
     density = float(cnt.mean()) / w.nblk
-    kv_adm = admitted_bytes(w, cnt, idx)
+    kv_adm = admitted_bytes(w, ucnt, uidx)
     mb = meta_bytes(w)
     eff_gbs = (kv_adm + mb) / (ms * 1e-3) / 1e9
     units = w.B * w.H
-    attn_alg = kv_adm + int(cnt.sum()) * 4 + units * w.d * 4 * 2 + units * 8
+    attn_alg = kv_adm + int(ucnt.sum()) * 4 + units * w.d * 4 * 2 + units * 8
     attn_gbs = attn_alg / (attn_ms * 1e-3) / 1e9
     log(f"[bench] {ms:.3f} ms/step, density {density:.3f}, attention partial {attn_ms:.3f} ms "
         f"({attn_gbs:.0f} GB/s), combine {comb_ms:.3f} ms, predict+screen {front_ms:.3f} ms, "
@@ -303,7 +314,10 @@ def main():
     per_head = (cnt / w.nblk).mean(axis=0)
     extra["per_head_density_min_max"] = [float(per_head.min()), float(per_head.max())]
     union = None
-    if w.H > 1:
+    if w.G > 1:
+        extra["union_density"] = float(ucnt.mean()) / w.nblk
+        extra["union_scope"] = f"blocks loaded per key/value head ({w.G} query heads each)"
+    elif w.H > 1:
         # union over heads of a batch row (reported, not a traffic figure under MHA)
         nb = w.nblk
         un = []
@@ -326,8 +340,8 @@ def main():
         dense_bias = torch.full((w.H,), -math.inf, device="cuda")
         dms, dattn, _, _ = time_steps(step, data, w, meta, None, dense_bias,
                                       max(5, args.steps // 2), 2, fused)
-        dcnt = step.adm_cnt.cpu().numpy()
-        d_bytes = admitted_bytes(w, dcnt, step.adm_idx.cpu().numpy())
+        dcnt = step.uni_cnt.cpu().numpy()
+        d_bytes = admitted_bytes(w, dcnt, step.uni_idx.cpu().numpy())
         extra["dense_tau_neg_inf"] = {
             "ms_per_step": dms, "steps_per_s": 1000.0 / dms,
             "effective_kv_gbs": (d_bytes + mb) / (dms * 1e-3) / 1e9,
@@ -354,7 +368,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded clustered keys; see DESIGN.md)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "T": w.T,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
+                   "T": w.T,
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",
                    "split_blocks": params.split_blocks or 16, "parallelism": "single GPU"},

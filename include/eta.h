@@ -24,16 +24,20 @@
  *     launch returns ETA_ERR_HIP. No C++ exception crosses this boundary.
  *   - The library holds no global mutable state; calls on different streams
  *     with disjoint outputs may run concurrently.
- *   - Multi-head attention only: one K/V head per query head.
- *   - Layouts (unit u = b*H + h):
+ *   - Heads: H query heads; H_kv key/value heads (H_kv = 0 means H_kv = H,
+ *     multi-head attention). With grouped heads, query head h reads key/value
+ *     head h / G, G = H / H_kv.
+ *   - Layouts (query unit u = b*H + h, key/value unit k = b*H_kv + h/G):
  *       q         float32 [B][H][d]        post-RoPE query (RoPE is the caller's)
- *       K, V      [B][H][T_cap][d]         float32 or bfloat16 (kv_dtype)
+ *       K, V      [B][H_kv][T_cap][d]      float32 or bfloat16 (kv_dtype)
  *       tau       float32 [B][H]
- *       centroid  float32 [B][H][d][nblk_cap]   dimension-major per unit
- *       var       float32 [B][H][nblk_cap]
- *       maxnorm   float32 [B][H][nblk_cap]
- *       adm_idx   int32   [B][H][nblk_cap]      ascending admitted block ids
+ *       centroid  float32 [B][H_kv][d][nblk_cap]   dimension-major per unit
+ *       var       float32 [B][H_kv][nblk_cap]
+ *       maxnorm   float32 [B][H_kv][nblk_cap]
+ *       adm_idx   int32   [B][H][nblk_cap]  per query head (eta_screen)
  *       adm_cnt   int32   [B][H]
+ *       uni_idx   int32   [B][H_kv][nblk_cap]  per key/value head (eta_admit_union)
+ *       uni_cnt   int32   [B][H_kv]
  *       out       float32 [B][H][d],  lse float32 [B][H]
  *     where nblk_cap = eta_nblk_cap(T_cap) = ceil(T_cap/64) rounded up to a
  *     multiple of 4.
@@ -73,6 +77,8 @@ typedef struct {
                            multiple of 64 (whole blocks)                       */
     int block;          /* tokens per KV block: must be 64                     */
     eta_dtype kv_dtype; /* element type of K and V                             */
+    int H_kv;           /* key/value heads: 0 or H = multi-head; a divisor of H
+                           with H / H_kv in {1, 2, 4, 8} = grouped heads       */
 } eta_shape;
 
 typedef struct {
@@ -170,14 +176,28 @@ eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W
                               float *tau, int32_t *adm_idx, int32_t *adm_cnt, float *bound_out,
                               hipStream_t stream);
 
+/*
+ * Grouped heads: union, per key/value head, of the admitted lists of its G
+ * query heads (the pages' "union density" is the share of blocks loaded this
+ * way; abstract: tokens co-admitted by coarse block selection are absorbed by
+ * the gate's floor). uni_idx[k] = ascending union of adm_idx[k*G + j][0..cnt)
+ * over j < G, uni_cnt[k] its length. Deterministic. With G = 1 it copies the
+ * lists. Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_HIP.
+ */
+eta_status eta_admit_union(const eta_shape *s, const int32_t *adm_idx, const int32_t *adm_cnt,
+                           int32_t *uni_idx, int32_t *uni_cnt, hipStream_t stream);
+
 /* Bytes of device workspace the attention calls need for this shape and split
  * size (0 on invalid arguments). The layout is private to the library. */
 size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);
 
 /*
  * Block-sparse split-KV decode attention with the ETA gate (Eq. 2 and Eq. 3;
- * abstract: sub-threshold logits suppressed toward zero). For every unit,
- * over the tokens (< T) of the blocks adm_idx[u][0..adm_cnt[u]):
+ * abstract: sub-threshold logits suppressed toward zero). adm_idx / adm_cnt
+ * are lists per key/value unit ([B][H_kv][nblk_cap], [B][H_kv]): the
+ * eta_screen lists for multi-head attention, the eta_admit_union lists for
+ * grouped heads. Every query head h of key/value unit k attends, with its own
+ * q and tau, over the tokens (< T) of the blocks adm_idx[k][0..adm_cnt[k]):
  *   S = s * q.k,  S' = S * sigmoid(gate_beta * (S - tau))  (or S * [S >= tau]),
  *   out = softmax(S') . V,  lse = log of the softmax denominator.
  * The admitted list is cut into work items of split_blocks blocks. This call

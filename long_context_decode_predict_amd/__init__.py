@@ -6,7 +6,7 @@ the seeded synthetic workloads (``workloads``), the closed-form threshold bias
 (``calibrate``) and the in-tree build (``build``).
 """
 from . import _lib  # noqa: F401
-from ._lib import (EtaError, Meta, default_params, eta_append_meta,  # noqa: F401
+from ._lib import (EtaError, Meta, default_params, eta_admit_union, eta_append_meta,  # noqa: F401
                    eta_build_block_meta, eta_decode_attn, eta_decode_attn_combine,
                    eta_decode_attn_partial, eta_decode_attn_workspace_size, eta_predict_screen,
                    eta_predict_tau, eta_screen)

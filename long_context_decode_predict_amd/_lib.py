@@ -38,7 +38,7 @@ class EtaError(RuntimeError):
 class eta_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int),
                 ("T", ctypes.c_int), ("T_cap", ctypes.c_int), ("block", ctypes.c_int),
-                ("kv_dtype", ctypes.c_int)]
+                ("kv_dtype", ctypes.c_int), ("H_kv", ctypes.c_int)]
 
 
 class eta_meta(ctypes.Structure):
@@ -69,6 +69,7 @@ SIGNATURES = {
                                   _vp, _vp, _vp]),
     "eta_predict_screen": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _P(eta_meta),
                                           _P(eta_params), _vp, _vp, _vp, _vp, _vp]),
+    "eta_admit_union": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp]),
     "eta_decode_attn_workspace_size": (ctypes.c_size_t, [_P(eta_shape), _P(eta_params)]),
     "eta_decode_attn": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp, _vp,
                                        _P(eta_params), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -140,8 +141,9 @@ def nblk_cap(T_cap: int) -> int:
     return int(lib().eta_nblk_cap(int(T_cap)))
 
 
-def make_shape(B, H, d, T, T_cap, kv_dtype: torch.dtype) -> eta_shape:
-    return eta_shape(int(B), int(H), int(d), int(T), int(T_cap), BLOCK, kv_code(kv_dtype))
+def make_shape(B, H, d, T, T_cap, kv_dtype: torch.dtype, H_kv: int = 0) -> eta_shape:
+    return eta_shape(int(B), int(H), int(d), int(T), int(T_cap), BLOCK, kv_code(kv_dtype),
+                     int(H_kv))
 
 
 def shape_of(K: torch.Tensor, T: int) -> eta_shape:
@@ -231,13 +233,15 @@ def eta_predict_tau(q: torch.Tensor, W, bias: torch.Tensor, tau: torch.Tensor, s
 
 def eta_screen(q: torch.Tensor, tau: torch.Tensor, meta: Meta, T: int, T_cap: int,
                params: eta_params, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
-               bound_out=None, kv_dtype=torch.bfloat16, stream=None):
+               bound_out=None, kv_dtype=torch.bfloat16, stream=None, H_kv: int = 0):
+    """Per query head lists; with grouped heads (H_kv < H) each query head screens
+    the metadata of its key/value head."""
     B, H, d = q.shape
-    s = make_shape(B, H, d, T, T_cap, kv_dtype)
+    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv)
     n = nblk_cap(T_cap)
     _need(q, "q", torch.float32)
     _need(tau, "tau", torch.float32, (B, H))
-    _check_meta(meta, B, H, d, T_cap)
+    _check_meta(meta, B, H_kv or H, d, T_cap)
     _need(adm_idx, "adm_idx", torch.int32, (B, H, n))
     _need(adm_cnt, "adm_cnt", torch.int32, (B, H))
     if bound_out is not None:
@@ -252,16 +256,16 @@ def eta_screen(q: torch.Tensor, tau: torch.Tensor, meta: Meta, T: int, T_cap: in
 def eta_predict_screen(q: torch.Tensor, W, bias: torch.Tensor, meta: Meta, T: int, T_cap: int,
                        params: eta_params, tau: torch.Tensor, adm_idx: torch.Tensor,
                        adm_cnt: torch.Tensor, bound_out=None, kv_dtype=torch.bfloat16,
-                       stream=None):
+                       stream=None, H_kv: int = 0):
     B, H, d = q.shape
-    s = make_shape(B, H, d, T, T_cap, kv_dtype)
+    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv)
     n = nblk_cap(T_cap)
     _need(q, "q", torch.float32)
     if W is not None:
         _need(W, "W", torch.float32, (H * d, H))
     _need(bias, "bias", torch.float32, (H,))
     _need(tau, "tau", torch.float32, (B, H))
-    _check_meta(meta, B, H, d, T_cap)
+    _check_meta(meta, B, H_kv or H, d, T_cap)
     _need(adm_idx, "adm_idx", torch.int32, (B, H, n))
     _need(adm_cnt, "adm_cnt", torch.int32, (B, H))
     if bound_out is not None:
@@ -274,18 +278,41 @@ def eta_predict_screen(q: torch.Tensor, W, bias: torch.Tensor, meta: Meta, T: in
                                     _stream(stream)))
 
 
+def eta_admit_union(adm_idx: torch.Tensor, adm_cnt: torch.Tensor, uni_idx: torch.Tensor,
+                    uni_cnt: torch.Tensor, T: int, T_cap: int, d: int, kv_dtype=torch.bfloat16,
+                    stream=None):
+    """Union of each key/value head's query-head lists ([B,H,n] -> [B,H_kv,n])."""
+    B, H, n = adm_idx.shape
+    H_kv = uni_idx.shape[1]
+    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv)
+    _need(adm_idx, "adm_idx", torch.int32, (B, H, nblk_cap(T_cap)))
+    _need(adm_cnt, "adm_cnt", torch.int32, (B, H))
+    _need(uni_idx, "uni_idx", torch.int32, (B, H_kv, nblk_cap(T_cap)))
+    _need(uni_cnt, "uni_cnt", torch.int32, (B, H_kv))
+    _check("eta_admit_union",
+           lib().eta_admit_union(ctypes.byref(s), adm_idx.data_ptr(), adm_cnt.data_ptr(),
+                                 uni_idx.data_ptr(), uni_cnt.data_ptr(), _stream(stream)))
+
+
 def eta_decode_attn_workspace_size(B, H, d, T_cap, params: eta_params,
-                                   kv_dtype=torch.bfloat16) -> int:
-    s = make_shape(B, H, d, 0, T_cap, kv_dtype)
+                                   kv_dtype=torch.bfloat16, H_kv: int = 0) -> int:
+    s = make_shape(B, H, d, 0, T_cap, kv_dtype, H_kv)
     return int(lib().eta_decode_attn_workspace_size(ctypes.byref(s), ctypes.byref(params)))
 
 
 def alloc_workspace(B, H, d, T_cap, params: eta_params, kv_dtype=torch.bfloat16,
-                    device="cuda") -> torch.Tensor:
-    n = eta_decode_attn_workspace_size(B, H, d, T_cap, params, kv_dtype)
+                    device="cuda", H_kv: int = 0) -> torch.Tensor:
+    n = eta_decode_attn_workspace_size(B, H, d, T_cap, params, kv_dtype, H_kv)
     if n == 0:
         raise EtaError("eta_decode_attn_workspace_size", ETA_ERR_INVALID_ARG, "invalid shape")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_shape(q: torch.Tensor, K: torch.Tensor, T: int) -> eta_shape:
+    """Shape of an attention call: H query heads from q, H_kv key/value heads from K."""
+    B, H_kv, T_cap, d = K.shape
+    H = q.shape[1]
+    return make_shape(B, H, d, T, T_cap, K.dtype, H_kv if H_kv != H else 0)
 
 
 def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws):
@@ -293,12 +320,15 @@ def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws):
     _check_kv(V, "V")
     if V.shape != K.shape or V.dtype != K.dtype:
         raise ValueError("K and V must have the same shape and dtype")
-    s = shape_of(K, T)
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,d]")
+    s = attn_shape(q, K, T)
     n = nblk_cap(s.T_cap)
+    H_kv = K.shape[1]
     _need(q, "q", torch.float32, (s.B, s.H, s.d))
     _need(tau, "tau", torch.float32, (s.B, s.H))
-    _need(adm_idx, "adm_idx", torch.int32, (s.B, s.H, n))
-    _need(adm_cnt, "adm_cnt", torch.int32, (s.B, s.H))
+    _need(adm_idx, "adm_idx", torch.int32, (s.B, H_kv, n))
+    _need(adm_cnt, "adm_cnt", torch.int32, (s.B, H_kv))
     _need(out, "out", torch.float32, (s.B, s.H, s.d))
     if lse is not None:
         _need(lse, "lse", torch.float32, (s.B, s.H))
@@ -333,8 +363,10 @@ def eta_decode_attn_partial(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T
 def eta_decode_attn_combine(K: torch.Tensor, T: int, adm_cnt: torch.Tensor, params: eta_params,
                             out: torch.Tensor, lse, ws: torch.Tensor, stream=None):
     _check_kv(K)
-    s = shape_of(K, T)
-    _need(adm_cnt, "adm_cnt", torch.int32, (s.B, s.H))
+    if out.dim() != 3:
+        raise ValueError("out must be [B,H,d]")
+    s = attn_shape(out, K, T)
+    _need(adm_cnt, "adm_cnt", torch.int32, (s.B, K.shape[1]))
     _need(out, "out", torch.float32, (s.B, s.H, s.d))
     if lse is not None:
         _need(lse, "lse", torch.float32, (s.B, s.H))

@@ -48,7 +48,8 @@ def _bisect(f, target: float, lo=-50.0, hi=50.0, iters=200) -> float:
 def bias_for(w: Workload, q: torch.Tensor, W, z: float = 4.0, device="cuda") -> torch.Tensor:
     """float32 [H] bias: frozen per-head thresholds for a workload without a predictor,
     else one predictor bias shared by all heads."""
-    sig = head_sigmas(w).tolist()
+    sig_kv = head_sigmas(w).tolist()
+    sig = [sig_kv[h // w.G] for h in range(w.H)]  # spread of each query head's keys
     qd = q.detach().to("cpu", torch.float64)
     B, H, d = qd.shape
     r = (qd.norm(dim=2) / math.sqrt(d)).tolist()  # [B][H]

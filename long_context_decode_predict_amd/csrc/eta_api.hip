@@ -32,8 +32,16 @@ eta_status check_shape(const eta_shape *s) {
     if (s->kv_dtype != ETA_F32 && s->kv_dtype != ETA_BF16) return ETA_ERR_UNSUPPORTED;
     const long long units = (long long)s->B * s->H;
     if (units > (1ll << 24)) return ETA_ERR_INVALID_ARG;  // grid-size headroom
+    if (s->H_kv < 0) return ETA_ERR_INVALID_ARG;
+    if (s->H_kv > 0) {
+        if (s->H % s->H_kv != 0) return ETA_ERR_INVALID_ARG;
+        const int G = s->H / s->H_kv;
+        if (G != 1 && G != 2 && G != 4 && G != 8) return ETA_ERR_UNSUPPORTED;
+    }
     return ETA_OK;
 }
+
+int kv_heads(const eta_shape *s) { return s->H_kv > 0 ? s->H_kv : s->H; }
 
 eta_status check_meta(const eta_shape *s, const eta_meta *m) {
     if (m == nullptr || m->centroid == nullptr || m->var == nullptr || m->maxnorm == nullptr)
@@ -53,6 +61,8 @@ bool kv_aligned(const eta_shape *s, const void *p) {
 eta::Geometry geometry(const eta_shape *s, int nblk_cap) {
     eta::Geometry g;
     g.units = s->B * s->H;
+    g.kv_units = s->B * kv_heads(s);
+    g.G = s->H / kv_heads(s);
     g.d = s->d;
     g.T = s->T;
     g.T_cap = s->T_cap;
@@ -187,6 +197,16 @@ eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W
     return from_hip(eta::launch_screen(g, s->H, q, tau, W, bias, true, m->centroid, m->var,
                                        m->maxnorm, p->z, p->bound_mode == ETA_BOUND_GEO, adm_idx,
                                        adm_cnt, bound_out, stream));
+}
+
+eta_status eta_admit_union(const eta_shape *s, const int32_t *adm_idx, const int32_t *adm_cnt,
+                           int32_t *uni_idx, int32_t *uni_cnt, hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if (adm_idx == nullptr || adm_cnt == nullptr || uni_idx == nullptr || uni_cnt == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    const eta::Geometry g = geometry(s, nblk_cap_of(s->T_cap));
+    return from_hip(eta::launch_union(g, adm_idx, adm_cnt, uni_idx, uni_cnt, stream));
 }
 
 size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p) {

@@ -42,7 +42,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kWorkersPerCU = 4;  // persistent workgroups launched per CU
 
 struct AttnArgs {
-    int units, T, T_cap, nblk, nblk_cap, split, ws_chunks;
+    int units, G, T, T_cap, nblk, nblk_cap, split, ws_chunks;  // units: key/value units
     float s, nbl2e;  // 1/sqrt(d), -beta*log2(e)
     const float *q;
     const void *K;
@@ -74,19 +74,22 @@ __device__ __forceinline__ void zero_row<float, 8>(RowLoad<float, 8> &r) {
 template <>
 __device__ __forceinline__ void zero_row<float, 4>(RowLoad<float, 4> &r) { r.a = make_float4(0.f, 0.f, 0.f, 0.f); }
 
-template <int D>
+template <int D, int G>
 struct AttnShared {
-    float m[kAttnWaves];
-    float l[kAttnWaves];
-    float o[kAttnWaves][D];
+    float m[kAttnWaves][G];
+    float l[kAttnWaves][G];
+    float o[kAttnWaves][G][D];
     int ticket;
 };
 
-// One work item (unit u, item `chunk`) by the whole workgroup. Ends with the
-// workgroup merge (one barrier); the caller barriers before LDS is reused.
-template <typename KV, int D, int TS, bool HARD>
+// One work item (key/value unit u, item `chunk`) by the whole workgroup, for the
+// G query heads u*G + j that share the unit's keys and values: every loaded
+// tile of K and V serves all G heads, each with its own query, threshold and
+// running softmax state. Ends with the workgroup merge (one barrier); the
+// caller barriers before LDS is reused.
+template <typename KV, int D, int TS, bool HARD, int G>
 __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
-                                          AttnShared<D> &sm) {
+                                          AttnShared<D, G> &sm) {
     constexpr int EPL = D / 16;
     constexpr int L = TS / 4;                 // row loads per lane per tile
     constexpr int TPB = kBlockTokens / TS;    // tiles per block
@@ -99,11 +102,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     const int row = lane >> 4;
     const int col = lane & 15;
 
-    float qr[EPL];
+    float qr[G][EPL], t[G], nbt[G];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qr[e] = a.q[(size_t)u * D + col * EPL + e] * a.s;
-    const float t = a.tau[u];
-    const float nbt = -a.nbl2e * t;  // gate exponent = nbl2e * S + nbt
+    for (int j = 0; j < G; ++j) {
+        const size_t uq = (size_t)u * G + j;  // query unit
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qr[j][e] = a.q[uq * D + col * EPL + e] * a.s;
+        t[j] = a.tau[uq];
+        nbt[j] = -a.nbl2e * t[j];  // gate exponent = nbl2e * S + nbt
+    }
 
     const KV *Ku = static_cast<const KV *>(a.K) + (size_t)u * a.T_cap * ROW;
     const KV *Vu = static_cast<const KV *>(a.V) + (size_t)u * a.T_cap * ROW;
@@ -116,11 +123,14 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     const int nb = (j1 - j0 - wave + kAttnWaves - 1) / kAttnWaves;
     const int ntiles = nb > 0 ? nb * TPB : 0;
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;  // per row: sum over this row's tokens
-    float o[EPL];
+    float m_run[G], l_run[G], o[G][EPL];  // l_run per row: this row's tokens
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+    for (int j = 0; j < G; ++j) {
+        m_run[j] = -INFINITY;
+        l_run[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
+    }
 
     auto tile_block = [&](int tt) { return iu[j0 + wave + (tt / TPB) * kAttnWaves]; };
     auto tile_base = [&](int blk, int tt) {
@@ -143,44 +153,55 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
 #pragma unroll
             for (int i = 0; i < L; ++i) vb[i].load(p + i * 4 * ROW);
         }
-        // gated logits of the tile
-        float sg[L];
+        // gated logits of the tile, per head
+        float sg[G][L];
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             float x[EPL];
             kb[i].widen(x);
-            float dot = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) dot += qr[e] * x[e];
-            const float S = row_sum16(dot);
-            float g;
-            if (HARD) {
-                g = S >= t ? S : 0.f;
-            } else {
-                g = S * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(a.nbl2e, S, nbt)));
+            for (int j = 0; j < G; ++j) {
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) dot += qr[j][e] * x[e];
+                const float S = row_sum16(dot);
+                float gv;
+                if (HARD) {
+                    gv = S >= t[j] ? S : 0.f;
+                } else {
+                    gv = S * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(a.nbl2e, S, nbt[j])));
+                }
+                sg[j][i] = gv;
             }
-            sg[i] = g;
         }
         if (valid < TS) {  // partial last block: rows past T take no weight
 #pragma unroll
             for (int i = 0; i < L; ++i)
-                if (4 * i + row >= valid) sg[i] = -INFINITY;
-        }
-        float bmax = -INFINITY;
+                if (4 * i + row >= valid) {
 #pragma unroll
-        for (int i = 0; i < L; ++i) bmax = fmaxf(bmax, sg[i]);
+                    for (int j = 0; j < G; ++j) sg[j][i] = -INFINITY;
+                }
+        }
         // the K registers are free: start the next tile's K loads
         if (tt + 1 < ntiles) {
             const KV *p = Ku + tile_base(tile_block(tt + 1), tt + 1) + lane_off;
 #pragma unroll
             for (int i = 0; i < L; ++i) kb[i].load(p + i * 4 * ROW);
         }
-        bmax = xrow_max(bmax);
-        const float m_new = fmaxf(m_run, bmax);
-        const float corr = fast_exp(m_run - m_new);
-        l_run *= corr;
+        float m_new[G];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] *= corr;
+        for (int j = 0; j < G; ++j) {
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < L; ++i) bmax = fmaxf(bmax, sg[j][i]);
+            bmax = xrow_max(bmax);
+            m_new[j] = fmaxf(m_run[j], bmax);
+            const float corr = fast_exp(m_run[j] - m_new[j]);
+            l_run[j] *= corr;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[j][e] *= corr;
+            m_run[j] = m_new[j];
+        }
         if (valid < TS) {
 #pragma unroll
             for (int i = 0; i < L; ++i)
@@ -188,67 +209,75 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         }
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            const float p = fast_exp(sg[i] - m_new);
-            l_run += p;
             float x[EPL];
             vb[i].widen(x);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] += p * x[e];
+            for (int j = 0; j < G; ++j) {
+                const float p = fast_exp(sg[j][i] - m_new[j]);
+                l_run[j] += p;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[j][e] += p * x[e];
+            }
         }
-        m_run = m_new;
     }
 
     // merge the four rows of the wave (m_run is wave-uniform)
-    const float l_w = xrow_sum(l_run);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = xrow_sum(o[e]);
-    if (lane == 0) {
-        sm.m[wave] = m_run;
-        sm.l[wave] = l_w;
-    }
-    if (lane < 16) {
+    for (int j = 0; j < G; ++j) {
+        const float l_w = xrow_sum(l_run[j]);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) sm.o[wave][lane * EPL + e] = o[e];
+        for (int e = 0; e < EPL; ++e) o[j][e] = xrow_sum(o[j][e]);
+        if (lane == 0) {
+            sm.m[wave][j] = m_run[j];
+            sm.l[wave][j] = l_w;
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm.o[wave][j][lane * EPL + e] = o[j][e];
+        }
     }
     __syncthreads();
 
-    // merge the waves of the workgroup
-    float M = -INFINITY;
+    // merge the waves of the workgroup, head by head
+    for (int j = 0; j < G; ++j) {
+        float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.m[w]);
-    float Lsum = 0.f;
-    float wgt[kAttnWaves];
+        for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.m[w][j]);
+        float Lsum = 0.f;
+        float wgt[kAttnWaves];
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
-        wgt[w] = fast_exp(sm.m[w] - M);  // a wave without blocks has m = -inf: weight 0
-        Lsum += sm.l[w] * wgt[w];
-    }
-    if (tid < D) {
-        float O = 0.f;
-#pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) O += sm.o[w][tid] * wgt[w];
-        if (nchunks == 1) {
-            a.out[(size_t)u * D + tid] = O / Lsum;
-        } else {
-            const size_t slot = (size_t)u * a.ws_chunks + chunk;
-            a.ws_o[slot * D + tid] = O;
+        for (int w = 0; w < kAttnWaves; ++w) {
+            wgt[w] = fast_exp(sm.m[w][j] - M);  // a wave without blocks has m = -inf: weight 0
+            Lsum += sm.l[w][j] * wgt[w];
         }
-    }
-    if (tid == 0) {
-        if (nchunks == 1) {
-            if (a.lse) a.lse[u] = M + __logf(Lsum);
-        } else {
-            const size_t slot = (size_t)u * a.ws_chunks + chunk;
-            a.ws_m[slot] = M;
-            a.ws_l[slot] = Lsum;
+        const size_t uq = (size_t)u * G + j;
+        if (tid < D) {
+            float O = 0.f;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) O += sm.o[w][j][tid] * wgt[w];
+            if (nchunks == 1) {
+                a.out[uq * D + tid] = O / Lsum;
+            } else {
+                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
+                a.ws_o[slot * D + tid] = O;
+            }
+        }
+        if (tid == 0) {
+            if (nchunks == 1) {
+                if (a.lse) a.lse[uq] = M + __logf(Lsum);
+            } else {
+                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
+                a.ws_m[slot] = M;
+                a.ws_l[slot] = Lsum;
+            }
         }
     }
 }
 
 // Persistent workers: each workgroup takes item tickets until the list is done.
-template <typename KV, int D, int TS, bool HARD>
+template <typename KV, int D, int TS, bool HARD, int G>
 __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArgs a) {
-    __shared__ AttnShared<D> sm;
+    __shared__ AttnShared<D, G> sm;
     const int total = a.ws_hdr[0];
     if (threadIdx.x == 0) sm.ticket = atomicAdd(&a.ws_hdr[1], 1);
     __syncthreads();
@@ -257,7 +286,7 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
         const int2 it = a.ws_items[ticket];
         int next = 0;
         if (threadIdx.x == 0) next = atomicAdd(&a.ws_hdr[1], 1);  // fetched early
-        attn_item<KV, D, TS, HARD>(a, it.x, it.y, sm);
+        attn_item<KV, D, TS, HARD, G>(a, it.x, it.y, sm);
         if (threadIdx.x == 0) sm.ticket = next;
         __syncthreads();
         ticket = sm.ticket;
@@ -274,7 +303,7 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
 constexpr int kPlanThreads = 256;
 constexpr int kPlanUnits = 64;
 
-__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int D) {
+__global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int D, int G) {
     __shared__ int red[kPlanThreads / kWave];
     __shared__ int excl[kPlanUnits];
     __shared__ int tile_total;
@@ -310,9 +339,9 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
         const int u = u0 + t;
         if (u >= a.units) break;
         const int c = a.cnt[u];
-        if (c <= 0) {
-            for (int i = lane; i < D; i += kWave) a.out[(size_t)u * D + i] = 0.f;
-            if (lane == 0 && a.lse) a.lse[u] = -INFINITY;
+        if (c <= 0) {  // nothing admitted for any of the unit's query heads
+            for (int i = lane; i < D * G; i += kWave) a.out[(size_t)u * G * D + i] = 0.f;
+            if (lane < G && a.lse) a.lse[(size_t)u * G + lane] = -INFINITY;
             continue;
         }
         const int n = (c + a.split - 1) / a.split;
@@ -338,19 +367,20 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     constexpr int NW = kCombineThreads / kWave;
     __shared__ float red[NW];
     __shared__ float part[R][D];
-    const int u = blockIdx.x;
+    const int uq = blockIdx.x;     // query unit
+    const int u = uq / a.G;        // its key/value unit
+    const int hj = uq - u * a.G;   // head within the group
     const int c = a.cnt[u];
     const int nchunks = (c + a.split - 1) / a.split;
     if (nchunks <= 1) return;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const float *wm = a.ws_m + (size_t)u * a.ws_chunks;
-    const float *wl = a.ws_l + (size_t)u * a.ws_chunks;
-    const float *wo = a.ws_o + (size_t)u * a.ws_chunks * D;
+    const size_t s0 = (size_t)u * a.ws_chunks * a.G + hj;  // partial of item i: s0 + i * G
+    const int gs = a.G;
 
     float mx = -INFINITY;
-    for (int i = tid; i < nchunks; i += kCombineThreads) mx = fmaxf(mx, wm[i]);
+    for (int i = tid; i < nchunks; i += kCombineThreads) mx = fmaxf(mx, a.ws_m[s0 + (size_t)i * gs]);
     mx = xrow_max(row_max16(mx));
     if (lane == 0) red[wave] = mx;
     __syncthreads();
@@ -360,7 +390,10 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     __syncthreads();  // red is reused below
 
     float ls = 0.f;
-    for (int i = tid; i < nchunks; i += kCombineThreads) ls += wl[i] * fast_exp(wm[i] - M);
+    for (int i = tid; i < nchunks; i += kCombineThreads) {
+        const size_t sl = s0 + (size_t)i * gs;
+        ls += a.ws_l[sl] * fast_exp(a.ws_m[sl] - M);
+    }
     ls = xrow_sum(row_sum16(ls));
     if (lane == 0) red[wave] = ls;
 
@@ -368,7 +401,10 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     const int r = tid / D;
     float O = 0.f;
 #pragma unroll 4
-    for (int i = r; i < nchunks; i += R) O += wo[(size_t)i * D + dim] * fast_exp(wm[i] - M);
+    for (int i = r; i < nchunks; i += R) {
+        const size_t sl = s0 + (size_t)i * gs;
+        O += a.ws_o[sl * D + dim] * fast_exp(a.ws_m[sl] - M);
+    }
     part[r][dim] = O;
     __syncthreads();
     if (tid < D) {
@@ -378,8 +414,8 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
         float Ot = 0.f;
 #pragma unroll
         for (int k = 0; k < R; ++k) Ot += part[k][tid];
-        a.out[(size_t)u * D + tid] = Ot / Lsum;
-        if (tid == 0 && a.lse) a.lse[u] = M + __logf(Lsum);
+        a.out[(size_t)uq * D + tid] = Ot / Lsum;
+        if (tid == 0 && a.lse) a.lse[uq] = M + __logf(Lsum);
     }
 }
 
@@ -392,7 +428,8 @@ AttnArgs make_args(const Geometry &g, const float *q, const void *K, const void 
     const AttnWorkspace w = attn_workspace_layout(g.units, max_chunks, g.d);
     char *base = static_cast<char *>(ws);
     AttnArgs a;
-    a.units = g.units;
+    a.units = g.kv_units;
+    a.G = g.G;
     a.T = g.T;
     a.T_cap = g.T_cap;
     a.nblk = g.nblk;
@@ -417,17 +454,31 @@ AttnArgs make_args(const Geometry &g, const float *q, const void *K, const void 
     return a;
 }
 
-template <typename KV, int D, int TS>
+template <typename KV, int D, int TS, int G>
 hipError_t launch_partial_t(const AttnArgs &a, bool hard, int workers, hipStream_t st) {
     const dim3 grid((unsigned)workers);
     if (hard) {
-        hipLaunchKernelGGL((attn_partial_kernel<KV, D, TS, true>), grid, dim3(kAttnWaves * kWave), 0,
-                           st, a);
+        hipLaunchKernelGGL((attn_partial_kernel<KV, D, TS, true, G>), grid,
+                           dim3(kAttnWaves * kWave), 0, st, a);
     } else {
-        hipLaunchKernelGGL((attn_partial_kernel<KV, D, TS, false>), grid, dim3(kAttnWaves * kWave),
-                           0, st, a);
+        hipLaunchKernelGGL((attn_partial_kernel<KV, D, TS, false, G>), grid,
+                           dim3(kAttnWaves * kWave), 0, st, a);
     }
     return hipGetLastError();
+}
+
+// Tile rows per K/V register buffer: smaller tiles for wider rows and more
+// query heads per key/value head keep the kernel at two waves per SIMD.
+template <typename KV, int D>
+hipError_t launch_partial_g(const AttnArgs &a, bool hard, int workers, hipStream_t st) {
+    constexpr bool wide = sizeof(KV) * D > 256;  // fp32 rows of 128
+    constexpr bool narrow = sizeof(KV) * D < 256;  // bf16 rows of 64
+    switch (a.G) {
+        case 1: return launch_partial_t<KV, D, wide ? 32 : 64, 1>(a, hard, workers, st);
+        case 2: return launch_partial_t<KV, D, narrow ? 64 : 32, 2>(a, hard, workers, st);
+        case 4: return launch_partial_t<KV, D, narrow ? 32 : (wide ? 16 : 32), 4>(a, hard, workers, st);
+        default: return launch_partial_t<KV, D, narrow ? 32 : 16, 8>(a, hard, workers, st);
+    }
 }
 
 }  // namespace
@@ -451,8 +502,9 @@ hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K,
     if (g.units == 0) return hipSuccess;
     const AttnArgs a = make_args(g, q, K, V, tau, adm_idx, adm_cnt, gate_beta, split_blocks,
                                  max_chunks, out, lse, ws);
-    hipLaunchKernelGGL(attn_plan_kernel, dim3((unsigned)((g.units + kPlanUnits - 1) / kPlanUnits)),
-                       dim3(kPlanThreads), 0, st, a, g.d);
+    hipLaunchKernelGGL(attn_plan_kernel,
+                       dim3((unsigned)((g.kv_units + kPlanUnits - 1) / kPlanUnits)),
+                       dim3(kPlanThreads), 0, st, a, g.d, g.G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // persistent workers: a few per CU, never more than the largest possible item count
@@ -461,15 +513,15 @@ hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K,
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
         return e;
     long long workers = (long long)cus * kWorkersPerCU;
-    const long long most = (long long)g.units * ((g.nblk + split_blocks - 1) / split_blocks);
+    const long long most = (long long)g.kv_units * ((g.nblk + split_blocks - 1) / split_blocks);
     if (workers > most) workers = most > 0 ? most : 1;
     const int wk = (int)workers;
     if (g.bf16) {
-        return g.d == 128 ? launch_partial_t<uint16_t, 128, 64>(a, gate_hard, wk, st)
-                          : launch_partial_t<uint16_t, 64, 64>(a, gate_hard, wk, st);
+        return g.d == 128 ? launch_partial_g<uint16_t, 128>(a, gate_hard, wk, st)
+                          : launch_partial_g<uint16_t, 64>(a, gate_hard, wk, st);
     }
-    return g.d == 128 ? launch_partial_t<float, 128, 32>(a, gate_hard, wk, st)
-                      : launch_partial_t<float, 64, 64>(a, gate_hard, wk, st);
+    return g.d == 128 ? launch_partial_g<float, 128>(a, gate_hard, wk, st)
+                      : launch_partial_g<float, 64>(a, gate_hard, wk, st);
 }
 
 hipError_t launch_attn_combine(const Geometry &g, const int32_t *adm_cnt, int split_blocks,

@@ -29,12 +29,20 @@ constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 
+// Lane permutation for a sum: every source lane of the patterns used here lies in
+// the same full row, so the zero written for an invalid source never occurs; the
+// zero "old" value lets the compiler fold the move into the add (v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp_for_add(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
 // Sum over the 16 lanes of each row; every lane of the row receives the sum.
 __device__ __forceinline__ float row_sum16(float x) {
-    x += dpp_mov<kQuadXor1>(x);
-    x += dpp_mov<kQuadXor2>(x);
-    x += dpp_mov<kRowHalfMirror>(x);
-    x += dpp_mov<kRowMirror>(x);
+    x += dpp_for_add<kQuadXor1>(x);
+    x += dpp_for_add<kQuadXor2>(x);
+    x += dpp_for_add<kRowHalfMirror>(x);
+    x += dpp_for_add<kRowMirror>(x);
     return x;
 }
 

@@ -10,7 +10,9 @@
 namespace eta {
 
 struct Geometry {
-    int units;     // B * H
+    int units;     // query units B * H
+    int kv_units;  // key/value units B * H_kv (= units for multi-head attention)
+    int G;         // query heads per key/value head (1, 2, 4 or 8)
     int d;         // 64 or 128
     int T;         // tokens present
     int T_cap;     // token capacity of K / V
@@ -31,6 +33,10 @@ hipError_t launch_screen(const Geometry &g, int H, const float *q, float *tau, c
                          const float *bias, bool predict, const float *centroid,
                          const float *var, const float *maxnorm, float z, bool geo_only,
                          int32_t *adm_idx, int32_t *adm_cnt, float *bound_out, hipStream_t st);
+
+// Union, per key/value unit, of the admitted lists of its G query heads.
+hipError_t launch_union(const Geometry &g, const int32_t *adm_idx, const int32_t *adm_cnt,
+                        int32_t *uni_idx, int32_t *uni_cnt, hipStream_t st);
 
 // Workspace layout of the split-KV attention for `units` units with at most
 // `max_chunks` work items each.

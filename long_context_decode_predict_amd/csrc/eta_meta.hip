@@ -126,7 +126,7 @@ template <typename KV, int D>
 hipError_t launch_meta_t(const Geometry &g, const void *K, float *c, float *v, float *m,
                          int blk_begin, int blk_end, hipStream_t st) {
     const int groups = (blk_end - blk_begin + kMetaBlocksPerGroup - 1) / kMetaBlocksPerGroup;
-    const dim3 grid((unsigned)((long long)g.units * groups));
+    const dim3 grid((unsigned)((long long)g.kv_units * groups));
     hipLaunchKernelGGL((block_meta_kernel<KV, D>), grid, dim3(kMetaWaves * kWave), 0, st,
                        static_cast<const KV *>(K), c, v, m, g.T, g.T_cap, g.nblk_cap, blk_begin,
                        blk_end, groups);
@@ -137,7 +137,7 @@ hipError_t launch_meta_t(const Geometry &g, const void *K, float *c, float *v, f
 
 hipError_t launch_block_meta(const Geometry &g, const void *K, float *centroid, float *var,
                              float *maxnorm, int blk_begin, int blk_end, hipStream_t st) {
-    if (blk_end <= blk_begin || g.units == 0) return hipSuccess;
+    if (blk_end <= blk_begin || g.kv_units == 0) return hipSuccess;
     if (g.bf16) {
         return g.d == 128 ? launch_meta_t<uint16_t, 128>(g, K, centroid, var, maxnorm, blk_begin, blk_end, st)
                           : launch_meta_t<uint16_t, 64>(g, K, centroid, var, maxnorm, blk_begin, blk_end, st);

@@ -8,7 +8,8 @@
 //   U_prob = s * (q . centroid + z * |q| * sqrt(var))
 //   U = min(U_geo, U_prob), or U_geo alone; admit iff U >= tau.
 //
-// One workgroup per (batch, head) unit, up to 16 waves. The centroids are
+// One workgroup per (batch, query head) unit, up to 16 waves; with grouped
+// heads each query head screens the metadata of its key/value head. The centroids are
 // dimension-major per unit, so lane l of a wave handles four consecutive
 // blocks and every load of one dimension is a contiguous 1 KiB run across the
 // wave (float4 per lane), with no cross-lane reduction. When a unit has few
@@ -33,7 +34,7 @@ constexpr int kBlocksPerWave = kWave * kBlocksPerLane;
 constexpr int kMaxSlices = 8;
 
 struct ScreenArgs {
-    int nblk, nblk_cap, H, nbg, ds;  // block groups per pass, dimension slices
+    int nblk, nblk_cap, H, G, nbg, ds;  // query heads per KV head, block groups, slices
     float s, z;
     int geo_only;
     const float *q;
@@ -94,9 +95,10 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
     const float geo_scale = a.s * qn;
     const float z_scale = a.z * qn;
 
-    const float *cu = a.centroid + (size_t)u * D * a.nblk_cap;
-    const float *vu = a.var + (size_t)u * a.nblk_cap;
-    const float *mu = a.maxnorm + (size_t)u * a.nblk_cap;
+    const int ukv = u / a.G;  // the key/value unit whose metadata this query head screens
+    const float *cu = a.centroid + (size_t)ukv * D * a.nblk_cap;
+    const float *vu = a.var + (size_t)ukv * a.nblk_cap;
+    const float *mu = a.maxnorm + (size_t)ukv * a.nblk_cap;
     int32_t *iu = a.adm_idx + (size_t)u * a.nblk_cap;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const int d0 = slice * dps;
@@ -218,6 +220,7 @@ hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau,
     a.nblk = g.nblk;
     a.nblk_cap = g.nblk_cap;
     a.H = H;
+    a.G = g.G;
     a.s = 1.0f / sqrtf((float)D);
     a.z = z;
     a.geo_only = geo_only ? 1 : 0;

@@ -1,10 +1,12 @@
 """One ETA decode step over a resident KV cache, as a sequence of C-ABI calls.
 
 ``DecodeStep`` owns the per-step device buffers (tau, admitted lists, outputs,
-workspace) for one [B,H,T_cap,d] cache and enqueues the four library calls of
-a step on the current stream with no host synchronisation:
-eta_predict_tau -> eta_screen -> eta_decode_attn (= eta_decode_attn_partial followed
-by eta_decode_attn_combine).
+workspace) for one cache of B rows, H query heads and H_kv key/value heads
+(H_kv = H: multi-head attention) and enqueues the library calls of a step on
+the current stream with no host synchronisation:
+eta_predict_tau + eta_screen (or eta_predict_screen in one launch)
+[-> eta_admit_union for grouped heads] -> eta_decode_attn
+(= eta_decode_attn_partial followed by eta_decode_attn_combine).
 """
 from __future__ import annotations
 
@@ -15,41 +17,58 @@ from . import _lib
 
 class DecodeStep:
     def __init__(self, B, H, d, T_cap, kv_dtype=torch.bfloat16, params=None, device="cuda",
-                 with_bounds=False):
+                 with_bounds=False, H_kv=None):
         self.B, self.H, self.d, self.T_cap = B, H, d, T_cap
+        self.H_kv = H if H_kv is None else H_kv
+        self.G = H // self.H_kv
         self.kv_dtype = kv_dtype
         self.params = params if params is not None else _lib.default_params()
         n = _lib.nblk_cap(T_cap)
         self.tau = torch.empty((B, H), dtype=torch.float32, device=device)
         self.adm_idx = torch.empty((B, H, n), dtype=torch.int32, device=device)
         self.adm_cnt = torch.empty((B, H), dtype=torch.int32, device=device)
+        if self.G > 1:
+            self.uni_idx = torch.empty((B, self.H_kv, n), dtype=torch.int32, device=device)
+            self.uni_cnt = torch.empty((B, self.H_kv), dtype=torch.int32, device=device)
+        else:  # multi-head: the attention reads the screen's lists directly
+            self.uni_idx, self.uni_cnt = self.adm_idx, self.adm_cnt
         self.out = torch.empty((B, H, d), dtype=torch.float32, device=device)
         self.lse = torch.empty((B, H), dtype=torch.float32, device=device)
         self.bounds = (torch.empty((B, H, n), dtype=torch.float32, device=device)
                        if with_bounds else None)
-        self.ws = _lib.alloc_workspace(B, H, d, T_cap, self.params, kv_dtype, device)
+        self._hkv_arg = 0 if self.G == 1 else self.H_kv
+        self.ws = _lib.alloc_workspace(B, H, d, T_cap, self.params, kv_dtype, device,
+                                       self._hkv_arg)
 
     def predict(self, q, W, bias, stream=None):
         _lib.eta_predict_tau(q, W, bias, self.tau, stream)
 
     def predict_screen(self, q, W, bias, meta, T, stream=None):
         _lib.eta_predict_screen(q, W, bias, meta, T, self.T_cap, self.params, self.tau,
-                                self.adm_idx, self.adm_cnt, self.bounds, self.kv_dtype, stream)
+                                self.adm_idx, self.adm_cnt, self.bounds, self.kv_dtype, stream,
+                                self._hkv_arg)
+        self.union(T, stream)
 
     def screen(self, q, meta, T, stream=None):
         _lib.eta_screen(q, self.tau, meta, T, self.T_cap, self.params, self.adm_idx,
-                        self.adm_cnt, self.bounds, self.kv_dtype, stream)
+                        self.adm_cnt, self.bounds, self.kv_dtype, stream, self._hkv_arg)
+        self.union(T, stream)
+
+    def union(self, T, stream=None):
+        if self.G > 1:
+            _lib.eta_admit_union(self.adm_idx, self.adm_cnt, self.uni_idx, self.uni_cnt, T,
+                                 self.T_cap, self.d, self.kv_dtype, stream)
 
     def attend(self, q, K, V, T, stream=None):
-        _lib.eta_decode_attn(q, K, V, T, self.tau, self.adm_idx, self.adm_cnt, self.params,
+        _lib.eta_decode_attn(q, K, V, T, self.tau, self.uni_idx, self.uni_cnt, self.params,
                              self.out, self.lse, self.ws, stream)
 
     def attend_partial(self, q, K, V, T, stream=None):
-        _lib.eta_decode_attn_partial(q, K, V, T, self.tau, self.adm_idx, self.adm_cnt,
+        _lib.eta_decode_attn_partial(q, K, V, T, self.tau, self.uni_idx, self.uni_cnt,
                                      self.params, self.out, self.lse, self.ws, stream)
 
     def attend_combine(self, K, T, stream=None):
-        _lib.eta_decode_attn_combine(K, T, self.adm_cnt, self.params, self.out, self.lse,
+        _lib.eta_decode_attn_combine(K, T, self.uni_cnt, self.params, self.out, self.lse,
                                      self.ws, stream)
 
     def capture(self, q, K, V, T, meta, W, bias, fused=True):

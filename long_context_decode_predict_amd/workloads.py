@@ -8,7 +8,11 @@ Recipe (per (batch, head) unit, per 64-token block): a block centroid drawn
 from N(0, 1)^d; each key = centroid + N(0, sigma^2) elementwise (clustered
 keys, sigma = 0.3 unless a per-head range is given); values ~ N(0, 1); the
 post-RoPE query ~ N(0, 1)^d; the predictor W is block-diagonal (head h reads
-only its own query slice) with entries N(0, 1/d). Optional "needle" keys: in a
+only its own query slice) with entries N(0, 1/d). Grouped heads (H_kv < H):
+K/V per key/value head, and the G = H / H_kv queries of a group share a common
+direction, q_h = c * q_group + sqrt(1 - c^2) * xi_h (c = group_corr), and so do
+their predictor columns, as the query heads that read one key/value head tend
+to in trained models. Optional "needle" keys: in a
 fraction of the blocks one key at a seeded slot is replaced by
 r * (0.9 * q_hat + sqrt(0.19) * u), u a random unit vector orthogonal to q_hat,
 r = sqrt(d (1 + sigma^2)) -- a key aligned with the query at cosine 0.9.
@@ -39,12 +43,22 @@ class Workload:
     head_densities: tuple | None = None  # static per-head targets (no predictor)
     needle_frac: float = 0.0
     append: int = 0             # tokens appended one by one before the step
+    H_kv: int = 0               # key/value heads (0: multi-head, H_kv = H)
+    group_corr: float = 0.0     # shared direction of a group's queries (grouped heads)
     seed: int = SEED_BASE
     note: str = field(default="", compare=False)
 
     @property
     def static_tau(self) -> bool:
         return self.head_densities is not None
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv if self.H_kv else self.H
+
+    @property
+    def G(self) -> int:
+        return self.H // self.kv_heads
 
     @property
     def T_cap(self) -> int:
@@ -76,6 +90,10 @@ WORKLOADS = {
         kv_dtype=torch.bfloat16, sigma_range=(0.1, 0.6),
         head_densities=tuple(0.1 + 0.8 * h / 15 for h in range(16)), seed=SEED_BASE + 4,
         note="frozen per-head thresholds, per-head densities 10..90%"),
+    "gqa_b32_h32kv8_d128_t128k_bf16": Workload(
+        "gqa_b32_h32kv8_d128_t128k_bf16", B=32, H=32, d=128, T=131072,
+        kv_dtype=torch.bfloat16, H_kv=8, group_corr=0.95, seed=SEED_BASE + 5,
+        note="grouped heads (4 query heads per key/value head), union loading"),
 }
 
 HEADLINE = "headline_b64_h16_d128_t128k_bf16"
@@ -95,41 +113,50 @@ def _gen(device, seed):
 
 
 def head_sigmas(w: Workload) -> torch.Tensor:
-    """Per-head in-block key spread (float32 [H], on the CPU)."""
+    """In-block key spread per key/value head (float32 [H_kv], on the CPU)."""
     if w.sigma_range is None:
-        return torch.full((w.H,), float(w.sigma), dtype=torch.float32)
+        return torch.full((w.kv_heads,), float(w.sigma), dtype=torch.float32)
     g = _gen("cpu", w.seed + 7)
     lo, hi = w.sigma_range
-    return (lo + (hi - lo) * torch.rand(w.H, generator=g)).to(torch.float32)
+    return (lo + (hi - lo) * torch.rand(w.kv_heads, generator=g)).to(torch.float32)
 
 
 def generate(w: Workload, device="cuda", T_cap: int | None = None) -> dict:
     """Draw q, K, V, W for a workload on `device`.
 
-    Returns dict(q [B,H,d] f32, K, V [B,H,T_cap,d] kv_dtype, W [H*d,H] f32 or None,
-    sigmas [H], needles: LongTensor [n,3] of (unit, block, slot) or None)."""
+    Returns dict(q [B,H,d] f32, K, V [B,H_kv,T_cap,d] kv_dtype, W [H*d,H] f32 or None,
+    sigmas [H_kv], needles: LongTensor [n,3] of (unit, block, slot) or None)."""
     T_cap = w.T_cap if T_cap is None else T_cap
     B, H, d = w.B, w.H, w.d
+    Hk = w.kv_heads
     nblk_cap = (T_cap + BLOCK - 1) // BLOCK
     g = _gen(device, w.seed)
     q = torch.randn((B, H, d), generator=g, device=device, dtype=torch.float32)
+    if w.G > 1 and w.group_corr > 0:
+        base = torch.randn((B, Hk, 1, d), generator=g, device=device, dtype=torch.float32)
+        c = float(w.group_corr)
+        q = (c * base + math.sqrt(1.0 - c * c) * q.view(B, Hk, w.G, d)).reshape(B, H, d)
     sig = head_sigmas(w).to(device)
-    K = torch.empty((B, H, T_cap, d), dtype=w.kv_dtype, device=device)
-    V = torch.empty((B, H, T_cap, d), dtype=w.kv_dtype, device=device)
+    K = torch.empty((B, Hk, T_cap, d), dtype=w.kv_dtype, device=device)
+    V = torch.empty((B, Hk, T_cap, d), dtype=w.kv_dtype, device=device)
     for b in range(B):  # one batch row at a time keeps fp32 temporaries small
-        cen = torch.randn((H, nblk_cap, 1, d), generator=g, device=device, dtype=torch.float32)
-        noise = torch.randn((H, nblk_cap, BLOCK, d), generator=g, device=device,
+        cen = torch.randn((Hk, nblk_cap, 1, d), generator=g, device=device, dtype=torch.float32)
+        noise = torch.randn((Hk, nblk_cap, BLOCK, d), generator=g, device=device,
                             dtype=torch.float32)
-        noise.mul_(sig.view(H, 1, 1, 1)).add_(cen)
-        K[b].copy_(noise.view(H, nblk_cap * BLOCK, d)[:, :T_cap])
+        noise.mul_(sig.view(Hk, 1, 1, 1)).add_(cen)
+        K[b].copy_(noise.view(Hk, nblk_cap * BLOCK, d)[:, :T_cap])
         del noise, cen
-        vb = torch.randn((H, T_cap, d), generator=g, device=device, dtype=torch.float32)
+        vb = torch.randn((Hk, T_cap, d), generator=g, device=device, dtype=torch.float32)
         V[b].copy_(vb)
         del vb
     W = None
     if not w.static_tau:
         W = torch.zeros((H * d, H), dtype=torch.float32, device=device)
         wdiag = torch.randn((H, d), generator=g, device=device, dtype=torch.float32) / math.sqrt(d)
+        if w.G > 1 and w.group_corr > 0:  # a group's predictor columns share a direction too
+            wb = torch.randn((Hk, 1, d), generator=g, device=device, dtype=torch.float32) / math.sqrt(d)
+            c = float(w.group_corr)
+            wdiag = (c * wb + math.sqrt(1.0 - c * c) * wdiag.view(Hk, w.G, d)).reshape(H, d)
         for h in range(H):
             W[h * d:(h + 1) * d, h] = wdiag[h]
     needles = None
@@ -141,6 +168,7 @@ def generate(w: Workload, device="cuda", T_cap: int | None = None) -> dict:
 def plant_needles(w: Workload, q, K, sig, g, T_cap):
     """Replace one key in a seeded fraction of each unit's blocks by a key aligned with
     the unit's query at cosine 0.9. Returns (unit, block, slot) triples."""
+    assert w.G == 1, "needles are planted for multi-head workloads only"
     B, H, d = w.B, w.H, w.d
     nblk = w.nblk
     per_unit = max(1, int(round(w.needle_frac * nblk)))

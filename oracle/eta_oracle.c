@@ -152,6 +152,24 @@ int eta_oracle_screen(int nblk, const double *U, double tau, int32_t *idx) {
     return cnt;
 }
 
+/* Grouped heads (a reading: the pages count "union density", the share of
+ * blocks loaded when the blocks of several heads are loaded together). A
+ * block is loaded for a KV head when any of its query heads admits it; each
+ * query head then attends over that union with its own gate, so blocks that
+ * only another head admitted enter through the gate's floor. */
+int eta_oracle_union(int g, const int32_t *lists, const int32_t *cnts, int stride, int nblk,
+                     int32_t *out) {
+    int cnt = 0;
+    for (int blk = 0; blk < nblk; ++blk) {
+        int hit = 0;
+        for (int j = 0; j < g && !hit; ++j)
+            for (int a = 0; a < cnts[j] && !hit; ++a)
+                if (lists[(long)j * stride + a] == blk) hit = 1;
+        if (hit) out[cnt++] = blk;
+    }
+    return cnt;
+}
+
 /* Eq. 2 of the review's "Methodology Assessment": m = sigma(beta*(S - tau)),
  * the logistic function. The hard form (beta -> infinity) is the step
  * S >= tau. */

@@ -55,6 +55,13 @@ void eta_oracle_bounds(int nblk, int d, const float *q_unit, const double *centr
  * ids in ascending order to idx (room for nblk) and returns their count. */
 int eta_oracle_screen(int nblk, const double *U, double tau, int32_t *idx);
 
+/* Union of the admitted lists of the g query heads that share one KV head
+ * (grouped-query attention): lists[j][0..cnts[j]) for j < g, each ascending,
+ * rows `stride` apart. Writes the ascending union to out (room for nblk) and
+ * returns its length. */
+int eta_oracle_union(int g, const int32_t *lists, const int32_t *cnts, int stride, int nblk,
+                     int32_t *out);
+
 /* Eq. 2 gate at one logit: sigmoid(beta*(S - tau)), or the step S >= tau. */
 double eta_oracle_gate(double S, double tau, double beta, int hard);
 

@@ -69,6 +69,8 @@ class OracleLib:
                                         ctypes.c_double, ctypes.c_int, _dp]
         L.eta_oracle_screen.restype = ctypes.c_int
         L.eta_oracle_screen.argtypes = [ctypes.c_int, _dp, ctypes.c_double, _ip]
+        L.eta_oracle_union.restype = ctypes.c_int
+        L.eta_oracle_union.argtypes = [ctypes.c_int, _ip, _ip, ctypes.c_int, ctypes.c_int, _ip]
         L.eta_oracle_gate.restype = ctypes.c_double
         L.eta_oracle_gate.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                       ctypes.c_int]
@@ -129,6 +131,20 @@ class OracleLib:
         cnt = self.L.eta_oracle_screen(len(U), U.ctypes.data_as(_dp), float(tau),
                                        idx.ctypes.data_as(_ip))
         return idx[:cnt].copy()
+
+    def union(self, lists, nblk: int) -> np.ndarray:
+        """Ascending union of a group's admitted lists (a list of int arrays)."""
+        g = len(lists)
+        stride = max([len(x) for x in lists] + [1])
+        buf = np.zeros((g, stride), dtype=np.int32)
+        cnts = np.zeros(g, dtype=np.int32)
+        for j, x in enumerate(lists):
+            buf[j, :len(x)] = x
+            cnts[j] = len(x)
+        out = np.empty(max(nblk, 1), dtype=np.int32)
+        n = self.L.eta_oracle_union(g, buf.ctypes.data_as(_ip), cnts.ctypes.data_as(_ip), stride,
+                                    nblk, out.ctypes.data_as(_ip))
+        return out[:n].copy()
 
     def gate(self, S: float, tau: float, beta: float = 5.0, hard: bool = False) -> float:
         return self.L.eta_oracle_gate(float(S), float(tau), float(beta), int(bool(hard)))

@@ -59,9 +59,9 @@ class Case:
         else:
             val = {"neg_inf": -math.inf, "pos_inf": math.inf, "nan": math.nan}[tau_mode]
             self.bias = torch.full((w.H,), val, dtype=torch.float32, device="cuda")
-        self.meta = _lib.Meta.alloc(w.B, w.H, w.d, self.T_cap)
+        self.meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, self.T_cap)
         self.step = DecodeStep(w.B, w.H, w.d, self.T_cap, w.kv_dtype, self.params,
-                               with_bounds=True)
+                               with_bounds=True, H_kv=w.kv_heads)
 
     def build_meta(self):
         _lib.eta_build_block_meta(self.data["K"], self.T, self.meta)
@@ -77,7 +77,8 @@ class Case:
     def host(self):
         s = self.step
         return {"tau": s.tau.cpu().numpy(), "idx": s.adm_idx.cpu().numpy(),
-                "cnt": s.adm_cnt.cpu().numpy(), "out": s.out.cpu().numpy(),
+                "cnt": s.adm_cnt.cpu().numpy(), "uni_idx": s.uni_idx.cpu().numpy(),
+                "uni_cnt": s.uni_cnt.cpu().numpy(), "out": s.out.cpu().numpy(),
                 "lse": s.lse.cpu().numpy(), "U": s.bounds.cpu().numpy(),
                 "centroid": self.meta.centroid, "var": self.meta.var,
                 "maxnorm": self.meta.maxnorm}
@@ -162,4 +163,76 @@ def compare_units(case: Case, units, O=None, check_meta=True):
             stats["max_lse_err"] = max(stats["max_lse_err"], abs(lse_g - lse_o))
         stats["out_checked"] += 1
         stats["max_out_err"] = max(stats["max_out_err"], err)
+    return stats
+
+
+def compare_gqa_units(case: Case, kv_units, O=None):
+    """Grouped heads: per query head masks, the union of each key/value head's lists,
+    and every query head's output over that union, against the oracle."""
+    O = O or oracle_mod.default()
+    w, T, p = case.w, case.T, case.params
+    G = w.G
+    g = case.host()
+    q = case.data["q"].cpu().numpy()
+    W = None if case.W is None else case.W.cpu().numpy()
+    tau_o = O.predict_tau(q, W, case.bias.cpu().numpy())
+    nblk = (T + 63) // 64
+    check_list_properties(g, nblk)
+    check_list_properties({"cnt": g["uni_cnt"], "idx": g["uni_idx"]}, nblk)
+    fin = np.isfinite(tau_o)
+    assert np.array_equal(fin, np.isfinite(g["tau"]))
+    assert np.all(np.abs(g["tau"][fin] - tau_o[fin]) <= TAU_TOL)
+    stats = {"kv_units": 0, "heads_checked": 0, "band_mismatch_units": 0, "max_out_err": 0.0,
+             "density": [], "union_density": []}
+    tol = OUT_TOL[w.kv_dtype]
+    for uk in kv_units:
+        b, k = divmod(int(uk), w.kv_heads)
+        Kh = kv_host(case.data["K"][b, k])
+        Vh = kv_host(case.data["V"][b, k])
+        c, v, m = O.block_meta(Kh, T)
+        masks, outs = [], []
+        for j in range(G):
+            h = k * G + j
+            U = O.bounds(q[b, h], c, v, m, z=p.z, mode=p.bound_mode)
+            Ug = g["U"][b, h, :nblk]
+            assert np.all(np.abs(Ug - U) <= 1e-5 * np.maximum(1.0, np.abs(U)))
+            t = float(tau_o[b, h])
+            mask_o = U >= t
+            mask_g = np.zeros(nblk, bool)
+            mask_g[g["idx"][b, h, :g["cnt"][b, h]]] = True
+            outside = ~(np.abs(U - t) <= BAND)
+            assert np.array_equal(mask_g[outside], mask_o[outside]), (uk, j)
+            masks.append(mask_o)
+            outs.append(outside)
+            stats["density"].append(mask_g.sum() / max(nblk, 1))
+        union_o = O.union([np.nonzero(mk)[0].astype(np.int32) for mk in masks], nblk)
+        union_g = g["uni_idx"][b, k, :g["uni_cnt"][b, k]]
+        stats["union_density"].append(len(union_g) / max(nblk, 1))
+        stats["kv_units"] += 1
+        # a block's union membership is decided when some head admits it outside the
+        # band, or every head rejects it outside the band
+        sure_in = np.zeros(nblk, bool)
+        sure_out = np.ones(nblk, bool)
+        for mk, od in zip(masks, outs):
+            sure_in |= mk & od
+            sure_out &= (~mk) & od
+        ug = np.zeros(nblk, bool)
+        ug[union_g] = True
+        assert np.all(ug[sure_in]) and not np.any(ug[sure_out]), uk
+        if not np.array_equal(union_g, union_o):
+            stats["band_mismatch_units"] += 1
+            continue
+        for j in range(G):
+            h = k * G + j
+            out_o, lse_o = O.attend(q[b, h], Kh, Vh, T, float(tau_o[b, h]), union_o,
+                                    beta=p.gate_beta, hard=bool(p.gate_hard))
+            err = float(np.max(np.abs(g["out"][b, h] - out_o)))
+            assert err <= tol, (uk, j, err)
+            lse_g = float(g["lse"][b, h])
+            if math.isinf(lse_o):
+                assert lse_g == lse_o and np.all(g["out"][b, h] == 0)
+            else:
+                assert abs(lse_g - lse_o) <= LSE_TOL, (uk, j, lse_g, lse_o)
+            stats["heads_checked"] += 1
+            stats["max_out_err"] = max(stats["max_out_err"], err)
     return stats

@@ -280,6 +280,25 @@ def check_screen_properties(O):
     assert len(O.screen(U, math.nan)) == 0
 
 
+def check_union(O):
+    """Group union against numpy's set union (library routine); one list is its own
+    union; empty lists; full coverage."""
+    rng = np.random.default_rng(16)
+    nblk = 300
+    for g in (1, 2, 4, 8):
+        lists = [np.sort(rng.choice(nblk, size=rng.integers(0, 120), replace=False)).astype(np.int32)
+                 for _ in range(g)]
+        want = lists[0]
+        for x in lists[1:]:
+            want = np.union1d(want, x)
+        assert np.array_equal(O.union(lists, nblk), want.astype(np.int32))
+    x = np.array([3, 9, 200], np.int32)
+    assert np.array_equal(O.union([x], nblk), x)
+    assert len(O.union([np.zeros(0, np.int32)] * 3, nblk)) == 0
+    assert np.array_equal(O.union([np.arange(0, nblk, 2, dtype=np.int32),
+                                   np.arange(1, nblk, 2, dtype=np.int32)], nblk), np.arange(nblk))
+
+
 # ----------------------------------------------------------------------------------------
 # Eq. 2 gate
 # ----------------------------------------------------------------------------------------

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
@@ -46,7 +46,7 @@ def test_defaults_and_strings(L):
 
 
 def shape(**kw):
-    s = dict(B=2, H=3, d=128, T=1000, T_cap=1024, block=64, kv_dtype=1)
+    s = dict(B=2, H=3, d=128, T=1000, T_cap=1024, block=64, kv_dtype=1, H_kv=0)
     s.update(kw)
     return _lib.eta_shape(**s)
 
@@ -66,6 +66,8 @@ INV, UNS, WSP = _lib.ETA_ERR_INVALID_ARG, _lib.ETA_ERR_UNSUPPORTED, _lib.ETA_ERR
     (dict(d=96), UNS), (dict(d=256), UNS), (dict(block=32), UNS), (dict(kv_dtype=5), UNS),
     (dict(T=1025), INV), (dict(T=-1), INV), (dict(B=0), INV), (dict(H=0), INV),
     (dict(T_cap=0, T=0), INV), (dict(T_cap=1000, T=900), INV),
+    (dict(H=6, H_kv=4), INV), (dict(H=6, H_kv=-1), INV), (dict(H=12, H_kv=1), UNS),
+    (dict(H=6, H_kv=2), UNS),
 ])
 def test_build_meta_shape_errors(L, s, st):
     sp = None if s is None else BY(shape(**s))
@@ -138,6 +140,16 @@ def test_predict_screen_errors(L):
     assert call(bound=FAKE + 8) == INV
     assert call(shape=dict(d=100)) == UNS
     assert call(shape=dict(T=2000)) == INV
+
+
+def test_union_errors(L):
+    s = BY(shape(H=8, H_kv=2))
+    assert L.eta_admit_union(s, None, FAKE, FAKE, FAKE, None) == INV
+    assert L.eta_admit_union(s, FAKE, None, FAKE, FAKE, None) == INV
+    assert L.eta_admit_union(s, FAKE, FAKE, None, FAKE, None) == INV
+    assert L.eta_admit_union(s, FAKE, FAKE, FAKE, None, None) == INV
+    assert L.eta_admit_union(BY(shape(H=8, H_kv=3)), FAKE, FAKE, FAKE, FAKE, None) == INV
+    assert L.eta_admit_union(BY(shape(H=24, H_kv=2)), FAKE, FAKE, FAKE, FAKE, None) == UNS
 
 
 def test_workspace_size(L):

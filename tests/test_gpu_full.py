@@ -53,6 +53,17 @@ def test_full_size(name):
         case.run(build=False)
     else:
         case.run()
+    if w.G > 1:
+        from gpu_util import compare_gqa_units
+        kv = sample_units(workloads.custom("s", B=w.B, H=w.kv_heads, T=64, seed=w.seed), n=6)
+        st = compare_gqa_units(case, kv)
+        per_head = float(np.mean(st["density"]))
+        print(f"  per-head density {per_head:.3f}, union {np.mean(st['union_density']):.3f}, "
+              f"heads checked {st['heads_checked']}, max|dout| {st['max_out_err']:.2e}", flush=True)
+        assert st["heads_checked"] >= (len(kv) - 1) * w.G
+        assert abs(per_head - w.density) < 0.1
+        case.free()
+        return
     units = sample_units(w)
     st = compare_units(case, units)
     cnt = case.step.adm_cnt.cpu().numpy()

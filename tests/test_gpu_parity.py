@@ -138,6 +138,51 @@ def test_graph_replay_matches_eager():
     case.free()
 
 
+GQA = [
+    ("g2_bf16_d128", dict(B=2, H=8, H_kv=4, d=128, T=3000, kv_dtype=torch.bfloat16,
+                          group_corr=0.9, seed=91), "predictor", {}),
+    ("g4_bf16_d128", dict(B=2, H=16, H_kv=4, d=128, T=5000, kv_dtype=torch.bfloat16,
+                          group_corr=0.95, seed=92), "predictor", {}),
+    ("g8_bf16_d128", dict(B=1, H=16, H_kv=2, d=128, T=4100, kv_dtype=torch.bfloat16,
+                          group_corr=0.9, seed=93), "predictor", {}),
+    ("g4_f32_d64", dict(B=2, H=8, H_kv=2, d=64, T=2049, kv_dtype=torch.float32,
+                        group_corr=0.5, seed=94), "predictor", {}),
+    ("g8_bf16_d64_split1", dict(B=1, H=8, H_kv=1, d=64, T=1500, kv_dtype=torch.bfloat16,
+                                seed=95), "predictor", {"split_blocks": 1}),
+    ("g2_f32_d128_hard", dict(B=1, H=4, H_kv=2, d=128, T=1000, kv_dtype=torch.float32,
+                              seed=96), "predictor", {"gate_hard": 1}),
+    ("g4_static", dict(B=2, H=16, H_kv=4, d=128, T=4096, kv_dtype=torch.bfloat16,
+                       sigma_range=(0.1, 0.6), head_densities=tuple(0.1 + 0.05 * h for h in range(16)),
+                       seed=97), "static", {}),
+    ("g4_tau_neg_inf", dict(B=1, H=8, H_kv=2, d=128, T=2000, kv_dtype=torch.bfloat16, seed=98),
+     "neg_inf", {}),
+    ("g4_tau_pos_inf", dict(B=1, H=8, H_kv=2, d=128, T=2000, kv_dtype=torch.bfloat16, seed=99),
+     "pos_inf", {}),
+]
+
+
+@pytest.mark.parametrize("name,kw,mode,pkw", GQA, ids=[c[0] for c in GQA])
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_parity_grouped_heads(name, kw, mode, pkw, fused):
+    """Grouped heads: per query head screens on the shared metadata, the union per
+    key/value head, and every query head's gated attention over that union."""
+    from gpu_util import compare_gqa_units
+    w = workloads.custom(name, **kw)
+    _announce(f"gqa {name} G={w.G} fused={fused}")
+    case = Case(w, tau_mode=mode, params=_lib.default_params(**pkw), fused=fused).run()
+    st = compare_gqa_units(case, range(w.B * w.kv_heads))
+    assert st["kv_units"] == w.B * w.kv_heads
+    assert st["band_mismatch_units"] <= 1, st
+    if mode == "neg_inf":
+        assert np.mean(st["union_density"]) == 1.0
+    if mode == "pos_inf":
+        assert np.mean(st["union_density"]) == 0.0
+        assert torch.all(case.step.out == 0) and torch.all(torch.isneginf(case.step.lse))
+    print(f"  per-head {np.mean(st['density']):.3f} union {np.mean(st['union_density']):.3f} "
+          f"max|dout| {st['max_out_err']:.2e}", flush=True)
+    case.free()
+
+
 def test_dense_matches_library_sdpa():
     """tau = -inf through the HIP path equals torch's softmax attention (CPU, float64)."""
     _announce("dense vs sdpa")

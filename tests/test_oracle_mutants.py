@@ -45,6 +45,10 @@ MUTANTS = [
     ("empty_lse_zero", "*lse = -INFINITY;", "*lse = 0.0;"),
     ("value_uses_key", "out[i] += p * kv_at(V,", "out[i] += p * kv_at(K,"),
     ("no_normalisation", "for (int i = 0; i < d; ++i) out[i] /= l;", ""),
+    ("union_first_list_only", "for (int j = 0; j < g && !hit; ++j)", "for (int j = 0; j < 1 && !hit; ++j)"),
+    ("union_wrong_row_stride", "if (lists[(long)j * stride + a] == blk) hit = 1;",
+     "if (lists[(long)j * g + a] == blk) hit = 1;"),
+    ("union_skips_first_head", "for (int j = 0; j < g && !hit; ++j)", "for (int j = 1; j < g && !hit; ++j)"),
 ]
 
 
