@@ -41,17 +41,20 @@ def elem_bytes(dtype):
     return 2 if dtype == torch.bfloat16 else 4
 
 
-def admitted_bytes(w, cnt, idx):
-    """Bytes of K and V of the admitted blocks (a partial last block counts its tokens)."""
+def admitted_bytes(w, cnt, idx, lens):
+    """Bytes of K and V of the admitted blocks (a partial last block counts its tokens);
+    cnt, idx per unit [B, heads(, n)], lens = tokens of each batch row."""
     eb = elem_bytes(w.kv_dtype)
-    nblk = w.nblk
-    last_tokens = w.T - (nblk - 1) * 64
     full = int(cnt.sum()) * 64
-    if last_tokens != 64:
-        cntf = cnt.reshape(-1)
-        idxf = idx.reshape(cntf.shape[0], -1)
-        has_last = sum(int(idxf[u, c - 1] == nblk - 1) for u, c in enumerate(cntf) if c > 0)
-        full -= has_last * (64 - last_tokens)
+    for b, T_b in enumerate(lens):
+        nblk = (T_b + 63) // 64
+        last_tokens = T_b - (nblk - 1) * 64
+        if nblk == 0 or last_tokens == 64:
+            continue
+        for h in range(cnt.shape[1]):
+            c = int(cnt[b, h])
+            if c > 0 and int(idx[b, h, c - 1]) == nblk - 1:
+                full -= 64 - last_tokens
     return 2 * full * w.d * eb
 
 
@@ -86,14 +89,20 @@ def counter_traffic(workload: str):
         return None
 
 
-def meta_bytes(w):
-    return w.B * w.kv_heads * w.nblk * (w.d + 2) * 4
+def meta_bytes(w, lens):
+    return w.kv_heads * sum((t + 63) // 64 for t in lens) * (w.d + 2) * 4
+
+
+def kv_of(data):
+    """The K, V the library reads: page pools for a paged workload, else the cache."""
+    return (data["Kp"], data["Vp"]) if "Kp" in data else (data["K"], data["V"])
 
 
 def run_steps(step, data, w, meta, W, bias, n, stream, evs=None, fused=True):
     """n decode steps; with evs, events bracket predict+screen, the split-KV partial
     kernel and the combine kernel of every step (all on the launch stream)."""
-    q, K, V = data["q"], data["K"], data["V"]
+    q = data["q"]
+    K, V = kv_of(data)
     for i in range(n):
         if evs is not None:
             evs[i][0].record(stream)
@@ -133,7 +142,8 @@ def time_steps(step, data, w, meta, W, bias, steps, warmup, fused=True):
 
 def graph_step_ms(step, data, w, meta, W, bias, steps, fused):
     """The same step captured once in a HIP graph and replayed `steps` times."""
-    graph = step.capture(data["q"], data["K"], data["V"], w.T, meta, W, bias, fused=fused)
+    K, V = kv_of(data)
+    graph = step.capture(data["q"], K, V, w.T, meta, W, bias, fused=fused)
     graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -146,7 +156,7 @@ def graph_step_ms(step, data, w, meta, W, bias, steps, fused):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=None):
+def cpu_baseline(w, data, W, bias, step_gpu_ms, params, lens, max_units=256, threads=None):
     """The fp64 oracle (as it stands) on a bounded sample of the same workload, timed on
     the host cores: predictor + bound + screen (+ union for grouped heads) + gated
     attention for the sampled key/value units' query heads, given metadata it built
@@ -173,10 +183,16 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=N
     slabs = []
     for u in units:
         b, k = divmod(int(u), w.kv_heads)
-        slabs.append((b, k, host(data["K"][b, k, :w.T]), host(data["V"][b, k, :w.T])))
+        T_b = lens[b]
+        if "Kp" in data:  # logical keys of the unit, read through the page table
+            Ku = workloads.gather_unit(data["Kp"], data["table"], b, k, T_b)
+            Vu = workloads.gather_unit(data["Vp"], data["table"], b, k, T_b)
+        else:
+            Ku, Vu = data["K"][b, k, :T_b], data["V"][b, k, :T_b]
+        slabs.append((b, k, host(Ku), host(Vu)))
     threads = threads or min(16, os.cpu_count() or 1)
     with ThreadPoolExecutor(threads) as ex:
-        metas = list(ex.map(lambda s: O.block_meta(s[2], w.T), slabs))
+        metas = list(ex.map(lambda s: O.block_meta(s[2], s[2].shape[0]), slabs))
         rows = sorted({s[0] for s in slabs})
         taus = {}
 
@@ -187,10 +203,10 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, max_units=256, threads=N
                 h = k * G + j
                 U = O.bounds(q[b, h], *metas[i], z=params.z, mode=params.bound_mode)
                 lists.append(O.screen(U, taus[b][h]))
-            adm = lists[0] if G == 1 else O.union(lists, w.nblk)
+            adm = lists[0] if G == 1 else O.union(lists, (Kh.shape[0] + 63) // 64)
             for j in range(G):
                 h = k * G + j
-                O.attend(q[b, h], Kh, Vh, w.T, taus[b][h], adm, beta=params.gate_beta,
+                O.attend(q[b, h], Kh, Vh, Kh.shape[0], taus[b][h], adm, beta=params.gate_beta,
                          hard=bool(params.gate_hard))
             return len(adm)
 
@@ -261,29 +277,44 @@ def main():
     data = workloads.generate(w, "cuda")
     W = data["W"]
     bias = calibrate.bias_for(w, data["q"], W, z=params.z)
+    lens = workloads.row_lengths(w)
+    layout = None
+    if w.var_len > 0 or w.paged:
+        lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda") if w.var_len > 0 else None
+        table = None
+        if w.paged:  # move the cache into a shuffled page pool and drop the dense copy
+            table, data["Kp"], data["Vp"] = workloads.page_pool(data["K"], data["V"], lens,
+                                                                 w.seed)
+            data["table"] = table
+            data["K"] = data["V"] = None
+            torch.cuda.empty_cache()
+        layout = _lib.KVLayout(lens_t, table)
     torch.cuda.synchronize()
     log(f"[bench] generated in {time.time() - t0:.1f}s")
+    K0 = kv_of(data)[0]
 
     meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, w.T_cap)
     append_ms = None
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if w.append:
+        assert layout is None, "appends are timed on the dense layout"
         T0 = w.T - w.append
-        _lib.eta_build_block_meta(data["K"], T0, meta)
+        _lib.eta_build_block_meta(K0, T0, meta)
         ev0.record()
         for t in range(T0, w.T):
-            _lib.eta_append_meta(data["K"], t, 1, meta)
+            _lib.eta_append_meta(K0, t, 1, meta)
         ev1.record()
         torch.cuda.synchronize()
         append_ms = ev0.elapsed_time(ev1) / w.append
     ev0.record()
-    _lib.eta_build_block_meta(data["K"], w.T, meta)
+    _lib.eta_build_block_meta(K0, w.T, meta, layout=layout)
     ev1.record()
     torch.cuda.synchronize()
     build_ms = ev0.elapsed_time(ev1)
     log(f"[bench] metadata build {build_ms:.2f} ms")
 
-    step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params, H_kv=w.kv_heads)
+    step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params, H_kv=w.kv_heads,
+                      layout=layout)
     fused = not args.unfused
     ms, attn_ms, front_ms, comb_ms = time_steps(step, data, w, meta, W, bias, args.steps,
                                                 args.warmup, fused)
@@ -292,12 +323,16 @@ def main():
     idx = step.adm_idx.cpu().numpy()
     ucnt = step.uni_cnt.cpu().numpy()     # per key/value head (the loaded blocks)
     uidx = step.uni_idx.cpu().numpy()
-    density = float(cnt.mean()) / w.nblk
-    kv_adm = admitted_bytes(w, ucnt, uidx)
-    mb = meta_bytes(w)
+    rows_nblk = np.array([(t + 63) // 64 for t in lens], dtype=np.float64)
+    frac = cnt / np.maximum(rows_nblk, 1)[:, None]  # admitted fraction of each unit's row
+    density = float(frac.mean())
+    kv_adm = admitted_bytes(w, ucnt, uidx, lens)
+    mb = meta_bytes(w, lens)
     eff_gbs = (kv_adm + mb) / (ms * 1e-3) / 1e9
     units = w.B * w.H
-    attn_alg = kv_adm + int(ucnt.sum()) * 4 + units * w.d * 4 * 2 + units * 8
+    # K/V of the loaded blocks, their list entries (and page ids), q and out, tau and lse
+    attn_alg = (kv_adm + int(ucnt.sum()) * 4 * (2 if w.paged else 1) + units * w.d * 4 * 2
+                + units * 8)
     attn_gbs = attn_alg / (attn_ms * 1e-3) / 1e9
     log(f"[bench] {ms:.3f} ms/step, density {density:.3f}, attention partial {attn_ms:.3f} ms "
         f"({attn_gbs:.0f} GB/s), combine {comb_ms:.3f} ms, predict+screen {front_ms:.3f} ms, "
@@ -311,21 +346,20 @@ def main():
              "predict_screen": "fused (eta_predict_screen)" if fused else "separate"}
     if append_ms is not None:
         extra["append_ms_per_token"] = append_ms
-    per_head = (cnt / w.nblk).mean(axis=0)
+    per_head = frac.mean(axis=0)
     extra["per_head_density_min_max"] = [float(per_head.min()), float(per_head.max())]
     union = None
     if w.G > 1:
-        extra["union_density"] = float(ucnt.mean()) / w.nblk
+        extra["union_density"] = float((ucnt / np.maximum(rows_nblk, 1)[:, None]).mean())
         extra["union_scope"] = f"blocks loaded per key/value head ({w.G} query heads each)"
     elif w.H > 1:
         # union over heads of a batch row (reported, not a traffic figure under MHA)
-        nb = w.nblk
         un = []
         for b in range(w.B):
             s = set()
             for h in range(w.H):
                 s.update(idx[b, h, :cnt[b, h]].tolist())
-            un.append(len(s) / nb)
+            un.append(len(s) / max(rows_nblk[b], 1))
         union = float(np.mean(un))
         extra["union_density"] = union
     if data["needles"] is not None:
@@ -341,7 +375,7 @@ def main():
         dms, dattn, _, _ = time_steps(step, data, w, meta, None, dense_bias,
                                       max(5, args.steps // 2), 2, fused)
         dcnt = step.uni_cnt.cpu().numpy()
-        d_bytes = admitted_bytes(w, dcnt, step.uni_idx.cpu().numpy())
+        d_bytes = admitted_bytes(w, dcnt, step.uni_idx.cpu().numpy(), lens)
         extra["dense_tau_neg_inf"] = {
             "ms_per_step": dms, "steps_per_s": 1000.0 / dms,
             "effective_kv_gbs": (d_bytes + mb) / (dms * 1e-3) / 1e9,
@@ -352,7 +386,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on host cores)")
-        cpu = cpu_baseline(w, data, W, bias, ms, params)
+        cpu = cpu_baseline(w, data, W, bias, ms, params, lens)
         log(f"[bench] cpu baseline {cpu['value']:.3f} steps/s ({cpu['sample']})")
 
     result = {
@@ -369,7 +403,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded clustered keys; see DESIGN.md)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
-                   "T": w.T,
+                   "T": w.T, "paged": w.paged, "var_len": w.var_len,
+                   "tokens_cached": int(sum(lens)),
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",
                    "split_blocks": params.split_blocks or 16, "parallelism": "single GPU"},

@@ -41,8 +41,14 @@
  *       out       float32 [B][H][d],  lse float32 [B][H]
  *     where nblk_cap = eta_nblk_cap(T_cap) = ceil(T_cap/64) rounded up to a
  *     multiple of 4.
- *   - Block beta of a unit covers tokens [64*beta, min(T, 64*beta + 64)); the
- *     last block may be partial. Tokens at or beyond T are never read.
+ *   - Block beta of a unit covers tokens [64*beta, min(T_b, 64*beta + 64)) of
+ *     its row b (T_b = seq_lens[b], or T); the last block may be partial.
+ *     Tokens at or beyond T_b are never read. Block metadata, admitted lists
+ *     and bounds are indexed by logical block in every layout; with a page
+ *     table only the K/V bytes move: block beta of (b, k) is the 64 x d run
+ *     K[page_table[b][beta]][k] of the pool.
+ *   - eta_append_meta with seq_lens: the lengths are the ones BEFORE the
+ *     append, and every row receives the same n_new tokens.
  */
 #ifndef ETA_H
 #define ETA_H
@@ -79,6 +85,19 @@ typedef struct {
     eta_dtype kv_dtype; /* element type of K and V                             */
     int H_kv;           /* key/value heads: 0 or H = multi-head; a divisor of H
                            with H / H_kv in {1, 2, 4, 8} = grouped heads       */
+    /* Optional layout of a paged / variable-length cache (all zero: the dense
+       layout K, V [B][H_kv][T_cap][d], every row holding T tokens).          */
+    const int32_t *seq_lens;   /* device int32 [B]: tokens present in row b
+                                  (each <= T; T is then the largest); null:
+                                  every row holds T                          */
+    const int32_t *page_table; /* device int32 [B][T_cap/64]: physical page of
+                                  logical block j of row b; null: dense layout.
+                                  With pages, K and V are pools
+                                  [num_pages][H_kv][64][d] and every page id
+                                  of a present block must be < num_pages (a
+                                  block whose page id is out of range is
+                                  skipped)                                   */
+    int num_pages;             /* pages in the K/V pools (page_table only)   */
 } eta_shape;
 
 typedef struct {

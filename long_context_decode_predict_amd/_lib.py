@@ -38,7 +38,9 @@ class EtaError(RuntimeError):
 class eta_shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int),
                 ("T", ctypes.c_int), ("T_cap", ctypes.c_int), ("block", ctypes.c_int),
-                ("kv_dtype", ctypes.c_int), ("H_kv", ctypes.c_int)]
+                ("kv_dtype", ctypes.c_int), ("H_kv", ctypes.c_int),
+                ("seq_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("num_pages", ctypes.c_int)]
 
 
 class eta_meta(ctypes.Structure):
@@ -141,15 +143,58 @@ def nblk_cap(T_cap: int) -> int:
     return int(lib().eta_nblk_cap(int(T_cap)))
 
 
-def make_shape(B, H, d, T, T_cap, kv_dtype: torch.dtype, H_kv: int = 0) -> eta_shape:
-    return eta_shape(int(B), int(H), int(d), int(T), int(T_cap), BLOCK, kv_code(kv_dtype),
-                     int(H_kv))
+@dataclass
+class KVLayout:
+    """Paged and/or variable-length cache (the optional fields of eta_shape).
+
+    seq_lens: int32 [B] tokens present in each row (each <= the call's T), or None.
+    page_table: int32 [B, T_cap/64] page of each logical block, or None; with it K
+    and V are pools [num_pages, H_kv, 64, d] instead of [B, H_kv, T_cap, d].
+    """
+    seq_lens: torch.Tensor | None = None
+    page_table: torch.Tensor | None = None
+
+    @property
+    def paged(self) -> bool:
+        return self.page_table is not None
 
 
-def shape_of(K: torch.Tensor, T: int) -> eta_shape:
-    """Shape descriptor of a [B,H,T_cap,d] K/V cache holding T tokens."""
-    B, H, T_cap, d = K.shape
-    return make_shape(B, H, d, T, T_cap, K.dtype)
+def make_shape(B, H, d, T, T_cap, kv_dtype: torch.dtype, H_kv: int = 0,
+               layout: KVLayout | None = None, num_pages: int = 0) -> eta_shape:
+    s = eta_shape(int(B), int(H), int(d), int(T), int(T_cap), BLOCK, kv_code(kv_dtype),
+                  int(H_kv))
+    if layout is not None:
+        if layout.seq_lens is not None:
+            _need(layout.seq_lens, "seq_lens", torch.int32, (B,))
+            s.seq_lens = layout.seq_lens.data_ptr()
+        if layout.page_table is not None:
+            _need(layout.page_table, "page_table", torch.int32, (B, T_cap // BLOCK))
+            s.page_table = layout.page_table.data_ptr()
+            s.num_pages = int(num_pages)
+    return s
+
+
+def kv_dims(K: torch.Tensor, layout: KVLayout | None = None):
+    """(B, H_kv, T_cap, d, num_pages) of a dense [B,H_kv,T_cap,d] cache, or of a page
+    pool [num_pages,H_kv,64,d] addressed through layout.page_table [B, T_cap/64]."""
+    if K.dim() != 4:
+        raise ValueError("K/V must be 4-d: [B,H_kv,T_cap,d] or a page pool [P,H_kv,64,d]")
+    if layout is not None and layout.paged:
+        P, H_kv, blk, d = K.shape
+        if blk != BLOCK:
+            raise ValueError(f"a page holds {BLOCK} tokens, got {blk}")
+        if layout.page_table.dim() != 2:
+            raise ValueError("page_table must be [B, T_cap/64]")
+        B, mp = layout.page_table.shape
+        return B, H_kv, mp * BLOCK, d, P
+    B, H_kv, T_cap, d = K.shape
+    return B, H_kv, T_cap, d, 0
+
+
+def shape_of(K: torch.Tensor, T: int, layout: KVLayout | None = None) -> eta_shape:
+    """Shape descriptor of a multi-head K/V cache holding T tokens."""
+    B, H, T_cap, d, P = kv_dims(K, layout)
+    return make_shape(B, H, d, T, T_cap, K.dtype, 0, layout, P)
 
 
 def default_params(**kw) -> eta_params:
@@ -198,18 +243,22 @@ def _check_kv(K: torch.Tensor, name="K"):
 # ------------------------------------------------------------------------------------
 # The C entry points, same names
 # ------------------------------------------------------------------------------------
-def eta_build_block_meta(K: torch.Tensor, T: int, meta: Meta, stream=None):
+def eta_build_block_meta(K: torch.Tensor, T: int, meta: Meta, stream=None,
+                         layout: KVLayout | None = None):
     _check_kv(K)
-    s = shape_of(K, T)
+    s = shape_of(K, T, layout)
     _check_meta(meta, s.B, s.H, s.d, s.T_cap)
     m = meta.c()
     _check("eta_build_block_meta",
            lib().eta_build_block_meta(ctypes.byref(s), K.data_ptr(), ctypes.byref(m), _stream(stream)))
 
 
-def eta_append_meta(K: torch.Tensor, T_old: int, n_new: int, meta: Meta, stream=None):
+def eta_append_meta(K: torch.Tensor, T_old: int, n_new: int, meta: Meta, stream=None,
+                    layout: KVLayout | None = None):
+    """With layout.seq_lens, those are the lengths before the append (T_old their
+    maximum) and every row receives n_new tokens."""
     _check_kv(K)
-    s = shape_of(K, T_old)
+    s = shape_of(K, T_old, layout)
     _check_meta(meta, s.B, s.H, s.d, s.T_cap)
     m = meta.c()
     _check("eta_append_meta",
@@ -233,11 +282,12 @@ def eta_predict_tau(q: torch.Tensor, W, bias: torch.Tensor, tau: torch.Tensor, s
 
 def eta_screen(q: torch.Tensor, tau: torch.Tensor, meta: Meta, T: int, T_cap: int,
                params: eta_params, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
-               bound_out=None, kv_dtype=torch.bfloat16, stream=None, H_kv: int = 0):
+               bound_out=None, kv_dtype=torch.bfloat16, stream=None, H_kv: int = 0,
+               layout: KVLayout | None = None):
     """Per query head lists; with grouped heads (H_kv < H) each query head screens
-    the metadata of its key/value head."""
+    the metadata of its key/value head. Only layout.seq_lens matters here."""
     B, H, d = q.shape
-    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv)
+    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv, _lens_only(layout))
     n = nblk_cap(T_cap)
     _need(q, "q", torch.float32)
     _need(tau, "tau", torch.float32, (B, H))
@@ -256,9 +306,9 @@ def eta_screen(q: torch.Tensor, tau: torch.Tensor, meta: Meta, T: int, T_cap: in
 def eta_predict_screen(q: torch.Tensor, W, bias: torch.Tensor, meta: Meta, T: int, T_cap: int,
                        params: eta_params, tau: torch.Tensor, adm_idx: torch.Tensor,
                        adm_cnt: torch.Tensor, bound_out=None, kv_dtype=torch.bfloat16,
-                       stream=None, H_kv: int = 0):
+                       stream=None, H_kv: int = 0, layout: KVLayout | None = None):
     B, H, d = q.shape
-    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv)
+    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv, _lens_only(layout))
     n = nblk_cap(T_cap)
     _need(q, "q", torch.float32)
     if W is not None:
@@ -308,21 +358,26 @@ def alloc_workspace(B, H, d, T_cap, params: eta_params, kv_dtype=torch.bfloat16,
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def attn_shape(q: torch.Tensor, K: torch.Tensor, T: int) -> eta_shape:
+def _lens_only(layout: KVLayout | None) -> KVLayout | None:
+    return None if layout is None or layout.seq_lens is None else KVLayout(layout.seq_lens)
+
+
+def attn_shape(q: torch.Tensor, K: torch.Tensor, T: int,
+               layout: KVLayout | None = None) -> eta_shape:
     """Shape of an attention call: H query heads from q, H_kv key/value heads from K."""
-    B, H_kv, T_cap, d = K.shape
+    B, H_kv, T_cap, d, P = kv_dims(K, layout)
     H = q.shape[1]
-    return make_shape(B, H, d, T, T_cap, K.dtype, H_kv if H_kv != H else 0)
+    return make_shape(B, H, d, T, T_cap, K.dtype, H_kv if H_kv != H else 0, layout, P)
 
 
-def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws):
+def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws, layout=None):
     _check_kv(K)
     _check_kv(V, "V")
     if V.shape != K.shape or V.dtype != K.dtype:
         raise ValueError("K and V must have the same shape and dtype")
     if q.dim() != 3:
         raise ValueError("q must be [B,H,d]")
-    s = attn_shape(q, K, T)
+    s = attn_shape(q, K, T, layout)
     n = nblk_cap(s.T_cap)
     H_kv = K.shape[1]
     _need(q, "q", torch.float32, (s.B, s.H, s.d))
@@ -338,8 +393,9 @@ def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws):
 
 def eta_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
                     tau: torch.Tensor, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
-                    params: eta_params, out: torch.Tensor, lse, ws: torch.Tensor, stream=None):
-    s = _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws)
+                    params: eta_params, out: torch.Tensor, lse, ws: torch.Tensor, stream=None,
+                    layout: KVLayout | None = None):
+    s = _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws, layout)
     _check("eta_decode_attn",
            lib().eta_decode_attn(ctypes.byref(s), q.data_ptr(), K.data_ptr(), V.data_ptr(),
                                  tau.data_ptr(), adm_idx.data_ptr(), adm_cnt.data_ptr(),
@@ -350,8 +406,8 @@ def eta_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
 def eta_decode_attn_partial(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
                             tau: torch.Tensor, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
                             params: eta_params, out: torch.Tensor, lse, ws: torch.Tensor,
-                            stream=None):
-    s = _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws)
+                            stream=None, layout: KVLayout | None = None):
+    s = _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws, layout)
     _check("eta_decode_attn_partial",
            lib().eta_decode_attn_partial(ctypes.byref(s), q.data_ptr(), K.data_ptr(),
                                          V.data_ptr(), tau.data_ptr(), adm_idx.data_ptr(),
@@ -361,11 +417,12 @@ def eta_decode_attn_partial(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T
 
 
 def eta_decode_attn_combine(K: torch.Tensor, T: int, adm_cnt: torch.Tensor, params: eta_params,
-                            out: torch.Tensor, lse, ws: torch.Tensor, stream=None):
+                            out: torch.Tensor, lse, ws: torch.Tensor, stream=None,
+                            layout: KVLayout | None = None):
     _check_kv(K)
     if out.dim() != 3:
         raise ValueError("out must be [B,H,d]")
-    s = attn_shape(out, K, T)
+    s = attn_shape(out, K, T, layout)
     _need(adm_cnt, "adm_cnt", torch.int32, (s.B, K.shape[1]))
     _need(out, "out", torch.float32, (s.B, s.H, s.d))
     if lse is not None:

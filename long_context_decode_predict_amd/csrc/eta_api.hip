@@ -22,6 +22,8 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // Per-unit capacity of the metadata, admitted-list and bound arrays.
 int nblk_cap_of(int T_cap) { return (int)(ceil_div(ceil_div(T_cap, kBlock), 4) * 4); }
 
+int kv_heads_of(const eta_shape *s) { return s->H_kv > 0 ? s->H_kv : s->H; }
+
 eta_status check_shape(const eta_shape *s) {
     if (s == nullptr) return ETA_ERR_INVALID_ARG;
     if (s->B < 1 || s->H < 1 || s->T < 0 || s->T_cap < 1 || s->T > s->T_cap)
@@ -38,10 +40,16 @@ eta_status check_shape(const eta_shape *s) {
         const int G = s->H / s->H_kv;
         if (G != 1 && G != 2 && G != 4 && G != 8) return ETA_ERR_UNSUPPORTED;
     }
+    if (s->seq_lens != nullptr && !aligned(s->seq_lens, 4)) return ETA_ERR_INVALID_ARG;
+    if (s->page_table != nullptr) {
+        if (!aligned(s->page_table, 4) || s->num_pages < 1) return ETA_ERR_INVALID_ARG;
+        // keeps every element offset of the pool far inside 64 bits
+        if ((long long)s->num_pages * kv_heads_of(s) > (1ll << 31)) return ETA_ERR_INVALID_ARG;
+    } else if (s->num_pages != 0) {
+        return ETA_ERR_INVALID_ARG;
+    }
     return ETA_OK;
 }
-
-int kv_heads(const eta_shape *s) { return s->H_kv > 0 ? s->H_kv : s->H; }
 
 eta_status check_meta(const eta_shape *s, const eta_meta *m) {
     if (m == nullptr || m->centroid == nullptr || m->var == nullptr || m->maxnorm == nullptr)
@@ -61,14 +69,21 @@ bool kv_aligned(const eta_shape *s, const void *p) {
 eta::Geometry geometry(const eta_shape *s, int nblk_cap) {
     eta::Geometry g;
     g.units = s->B * s->H;
-    g.kv_units = s->B * kv_heads(s);
-    g.G = s->H / kv_heads(s);
+    g.kv_units = s->B * kv_heads_of(s);
+    g.G = s->H / kv_heads_of(s);
     g.d = s->d;
     g.T = s->T;
     g.T_cap = s->T_cap;
     g.nblk = (int)ceil_div(s->T, kBlock);
     g.nblk_cap = nblk_cap;
     g.bf16 = s->kv_dtype == ETA_BF16;
+    g.lay.seq_lens = s->seq_lens;
+    g.lay.pages = s->page_table;
+    g.lay.T = s->T;
+    g.lay.T_cap = s->T_cap;
+    g.lay.H_kv = kv_heads_of(s);
+    g.lay.max_pages = s->T_cap / kBlock;
+    g.lay.num_pages = s->page_table != nullptr ? s->num_pages : 0;
     return g;
 }
 
@@ -138,7 +153,7 @@ eta_status eta_build_block_meta(const eta_shape *s, const void *K, const eta_met
     if ((st = check_meta(s, m)) != ETA_OK) return st;
     if (K == nullptr || !kv_aligned(s, K)) return ETA_ERR_INVALID_ARG;
     const eta::Geometry g = geometry(s, m->nblk_cap);
-    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, 0, g.nblk, stream));
+    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, 0, g.nblk, 0, stream));
 }
 
 eta_status eta_append_meta(const eta_shape *s, int n_new, const void *K, const eta_meta *m,
@@ -148,11 +163,10 @@ eta_status eta_append_meta(const eta_shape *s, int n_new, const void *K, const e
     if ((st = check_meta(s, m)) != ETA_OK) return st;
     if (K == nullptr || !kv_aligned(s, K)) return ETA_ERR_INVALID_ARG;
     if (n_new < 1 || (long long)s->T + n_new > s->T_cap) return ETA_ERR_INVALID_ARG;
-    eta_shape grown = *s;
-    grown.T = s->T + n_new;
-    const eta::Geometry g = geometry(&grown, m->nblk_cap);
-    const int first = s->T / kBlock;  // the block holding token T_old (maybe partial)
-    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, first, g.nblk, stream));
+    // the layout keeps the lengths before the append; each row's blocks from the one
+    // holding its first new token through the one holding its last are rebuilt
+    const eta::Geometry g = geometry(s, m->nblk_cap);
+    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, 0, 0, n_new, stream));
 }
 
 eta_status eta_predict_tau(int B, int H, int d, const float *q, const float *W,

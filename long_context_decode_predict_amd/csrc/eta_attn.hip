@@ -29,9 +29,13 @@
 // (deterministic; the kernel boundary orders the two, so no fences or atomics
 // are needed).
 //
-// The K/V capacity is a whole number of blocks, so the rows of a partial last
-// block past T are inside the allocation: they are loaded unclamped and masked
-// (their logits become -inf and their values are zeroed before use).
+// The K/V capacity is a whole number of blocks (dense layout) and a page holds
+// a whole block (paged layout), so the rows of a partial last block past the
+// row's length are inside the allocation: they are loaded unclamped and masked
+// (their logits become -inf and their values are zeroed before use). A block
+// whose page id is out of range is not read at all: its tiles load from the
+// first page and are masked whole, so the block contributes nothing (a unit
+// left with no token gets out = 0, lse = -inf, as an empty list does).
 #include "eta_device.hpp"
 #include "eta_launch.hpp"
 
@@ -42,7 +46,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kWorkersPerCU = 4;  // persistent workgroups launched per CU
 
 struct AttnArgs {
-    int units, G, T, T_cap, nblk, nblk_cap, split, ws_chunks;  // units: key/value units
+    int units, G, nblk, nblk_cap, split, ws_chunks;  // units: key/value units
     float s, nbl2e;  // 1/sqrt(d), -beta*log2(e)
     const float *q;
     const void *K;
@@ -57,6 +61,7 @@ struct AttnArgs {
     float *ws_o;
     int *ws_hdr;     // [0] = number of items, [1] = ticket counter
     int2 *ws_items;  // compacted (unit, item index) list
+    KVLayout lay;    // dense or paged rows, per-row lengths
 };
 
 // Zero the raw bits of a row held in registers (used for rows past T).
@@ -112,8 +117,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         nbt[j] = -a.nbl2e * t[j];  // gate exponent = nbl2e * S + nbt
     }
 
-    const KV *Ku = static_cast<const KV *>(a.K) + (size_t)u * a.T_cap * ROW;
-    const KV *Vu = static_cast<const KV *>(a.V) + (size_t)u * a.T_cap * ROW;
+    const KV *Kp = static_cast<const KV *>(a.K);
+    const KV *Vp = static_cast<const KV *>(a.V);
+    const int rb = u / a.lay.H_kv;          // batch row of the unit
+    const int kh = u - rb * a.lay.H_kv;     // its key/value head
+    const int Tb = a.lay.row_len(rb);       // tokens present in the row
     const int lane_off = row * ROW + col * EPL;  // element offset inside a 4-row group
     const int32_t *iu = a.idx + (size_t)u * a.nblk_cap;
 
@@ -132,24 +140,30 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
     }
 
-    auto tile_block = [&](int tt) { return iu[j0 + wave + (tt / TPB) * kAttnWaves]; };
-    auto tile_base = [&](int blk, int tt) {
-        return (size_t)blk * kBlockTokens * ROW + (size_t)((tt % TPB) * TS) * ROW;
+    // Element offset of tile tt and the number of its rows below the row's length
+    // (TS or more for every tile but a partial last block's; 0 for a bad page).
+    auto tile_at = [&](int tt, size_t &off, int &valid) {
+        const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
+        const long long bo = a.lay.block_offset(rb, kh, blk, D);
+        const int sub = (tt % TPB) * TS;
+        off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * ROW;
+        valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
     };
 
     RowLoad<KV, EPL> kb[L], vb[L];
+    size_t next_off = 0;
+    int next_valid = 0;
     if (ntiles > 0) {
-        const KV *p = Ku + tile_base(tile_block(0), 0) + lane_off;
+        tile_at(0, next_off, next_valid);
+        const KV *p = Kp + next_off + lane_off;
 #pragma unroll
         for (int i = 0; i < L; ++i) kb[i].load(p + i * 4 * ROW);
     }
     for (int tt = 0; tt < ntiles; ++tt) {
-        const int blk = tile_block(tt);
-        const size_t base = tile_base(blk, tt);
-        // rows of this tile below T (TS or more for every tile but a partial last block's)
-        const int valid = min(a.T - blk * kBlockTokens, kBlockTokens) - (tt % TPB) * TS;
+        const size_t base = next_off;
+        const int valid = next_valid;
         {
-            const KV *p = Vu + base + lane_off;
+            const KV *p = Vp + base + lane_off;
 #pragma unroll
             for (int i = 0; i < L; ++i) vb[i].load(p + i * 4 * ROW);
         }
@@ -174,7 +188,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
                 sg[j][i] = gv;
             }
         }
-        if (valid < TS) {  // partial last block: rows past T take no weight
+        if (valid < TS) {  // partial last block: rows past the row's length take no weight
 #pragma unroll
             for (int i = 0; i < L; ++i)
                 if (4 * i + row >= valid) {
@@ -184,7 +198,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         }
         // the K registers are free: start the next tile's K loads
         if (tt + 1 < ntiles) {
-            const KV *p = Ku + tile_base(tile_block(tt + 1), tt + 1) + lane_off;
+            tile_at(tt + 1, next_off, next_valid);
+            const KV *p = Kp + next_off + lane_off;
 #pragma unroll
             for (int i = 0; i < L; ++i) kb[i].load(p + i * 4 * ROW);
         }
@@ -195,12 +210,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
 #pragma unroll
             for (int i = 0; i < L; ++i) bmax = fmaxf(bmax, sg[j][i]);
             bmax = xrow_max(bmax);
-            m_new[j] = fmaxf(m_run[j], bmax);
+            const float mx = fmaxf(m_run[j], bmax);
+            // reference for the weights; a fully masked tile before any token
+            // leaves the max at -inf, and 0 then keeps the weights 0, not NaN
+            m_new[j] = mx == -INFINITY ? 0.f : mx;
             const float corr = fast_exp(m_run[j] - m_new[j]);
             l_run[j] *= corr;
 #pragma unroll
             for (int e = 0; e < EPL; ++e) o[j][e] *= corr;
-            m_run[j] = m_new[j];
+            m_run[j] = mx;
         }
         if (valid < TS) {
 #pragma unroll
@@ -243,11 +261,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, sm.m[w][j]);
+        const float Mr = M == -INFINITY ? 0.f : M;  // no token at all: weights 0, Lsum 0
         float Lsum = 0.f;
         float wgt[kAttnWaves];
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w) {
-            wgt[w] = fast_exp(sm.m[w][j] - M);  // a wave without blocks has m = -inf: weight 0
+            wgt[w] = fast_exp(sm.m[w][j] - Mr);  // a wave without tokens has m = -inf: weight 0
             Lsum += sm.l[w][j] * wgt[w];
         }
         const size_t uq = (size_t)u * G + j;
@@ -256,7 +275,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
 #pragma unroll
             for (int w = 0; w < kAttnWaves; ++w) O += sm.o[w][j][tid] * wgt[w];
             if (nchunks == 1) {
-                a.out[uq * D + tid] = O / Lsum;
+                a.out[uq * D + tid] = Lsum > 0.f ? O / Lsum : 0.f;
             } else {
                 const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
                 a.ws_o[slot * D + tid] = O;
@@ -264,7 +283,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         }
         if (tid == 0) {
             if (nchunks == 1) {
-                if (a.lse) a.lse[uq] = M + __logf(Lsum);
+                if (a.lse) a.lse[uq] = Lsum > 0.f ? M + __logf(Lsum) : -INFINITY;
             } else {
                 const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
                 a.ws_m[slot] = M;
@@ -387,12 +406,13 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     float M = red[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
+    const float Mr = M == -INFINITY ? 0.f : M;  // no token in any item: weights 0
     __syncthreads();  // red is reused below
 
     float ls = 0.f;
     for (int i = tid; i < nchunks; i += kCombineThreads) {
         const size_t sl = s0 + (size_t)i * gs;
-        ls += a.ws_l[sl] * fast_exp(a.ws_m[sl] - M);
+        ls += a.ws_l[sl] * fast_exp(a.ws_m[sl] - Mr);
     }
     ls = xrow_sum(row_sum16(ls));
     if (lane == 0) red[wave] = ls;
@@ -403,7 +423,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
 #pragma unroll 4
     for (int i = r; i < nchunks; i += R) {
         const size_t sl = s0 + (size_t)i * gs;
-        O += a.ws_o[sl * D + dim] * fast_exp(a.ws_m[sl] - M);
+        O += a.ws_o[sl * D + dim] * fast_exp(a.ws_m[sl] - Mr);
     }
     part[r][dim] = O;
     __syncthreads();
@@ -414,8 +434,8 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
         float Ot = 0.f;
 #pragma unroll
         for (int k = 0; k < R; ++k) Ot += part[k][tid];
-        a.out[(size_t)uq * D + tid] = Ot / Lsum;
-        if (tid == 0 && a.lse) a.lse[uq] = M + __logf(Lsum);
+        a.out[(size_t)uq * D + tid] = Lsum > 0.f ? Ot / Lsum : 0.f;
+        if (tid == 0 && a.lse) a.lse[uq] = Lsum > 0.f ? M + __logf(Lsum) : -INFINITY;
     }
 }
 
@@ -430,8 +450,7 @@ AttnArgs make_args(const Geometry &g, const float *q, const void *K, const void 
     AttnArgs a;
     a.units = g.kv_units;
     a.G = g.G;
-    a.T = g.T;
-    a.T_cap = g.T_cap;
+    a.lay = g.lay;
     a.nblk = g.nblk;
     a.nblk_cap = g.nblk_cap;
     a.split = split_blocks;

@@ -70,6 +70,32 @@ __device__ __forceinline__ float xrow_max(float x) {
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
+// ---- where the rows of a key/value unit live ----
+// Dense: K[(b*H_kv + k)][T_cap][d]. Paged: pools [num_pages][H_kv][64][d] and a
+// page table [B][max_pages] (logical block -> page). Rows may hold different
+// numbers of tokens (seq_lens).
+struct KVLayout {
+    const int32_t *seq_lens;  // null: every row holds T
+    const int32_t *pages;     // null: dense layout
+    int T, T_cap, H_kv, max_pages, num_pages;
+
+    __device__ __forceinline__ int row_len(int b) const {
+        if (seq_lens == nullptr) return T;
+        const int t = seq_lens[b];
+        return t < 0 ? 0 : (t > T ? T : t);
+    }
+    // Element offset of logical block j of key/value unit (b, k); -1 when the
+    // block's page is out of range.
+    __device__ __forceinline__ long long block_offset(int b, int k, int j, int d) const {
+        if (pages != nullptr) {
+            const int p = pages[(size_t)b * max_pages + j];
+            if ((unsigned)p >= (unsigned)num_pages) return -1;
+            return ((long long)p * H_kv + k) * kBlockTokens * d;
+        }
+        return ((long long)(b * H_kv + k) * T_cap + (long long)j * kBlockTokens) * d;
+    }
+};
+
 // ---- row loads: EPL elements of one token row, widened to float ----
 // KV = float or uint16_t (bfloat16 bits). EPL = d / 16.
 template <typename KV, int EPL>

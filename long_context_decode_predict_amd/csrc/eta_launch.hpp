@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "eta_device.hpp"
+
 namespace eta {
 
 struct Geometry {
@@ -19,10 +21,15 @@ struct Geometry {
     int nblk;      // ceil(T / 64)
     int nblk_cap;  // metadata / list capacity per unit (multiple of 4)
     bool bf16;     // K / V element type
+    KVLayout lay;  // dense or paged rows, optional per-row lengths
 };
 
+// Metadata of blocks [blk_begin, blk_end) of every row (clipped to the row's
+// length); with n_new > 0, of the blocks each row's next n_new tokens touch
+// (the layout's lengths are then the lengths before those tokens).
 hipError_t launch_block_meta(const Geometry &g, const void *K, float *centroid, float *var,
-                             float *maxnorm, int blk_begin, int blk_end, hipStream_t st);
+                             float *maxnorm, int blk_begin, int blk_end, int n_new,
+                             hipStream_t st);
 
 hipError_t launch_predict_tau(int B, int H, int d, const float *q, const float *W,
                               const float *bias, float *tau, hipStream_t st);

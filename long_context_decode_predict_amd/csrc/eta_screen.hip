@@ -19,6 +19,10 @@
 // compacted with wave ballots plus an LDS exclusive scan over the block
 // groups: the admitted list comes out ascending with no atomics.
 //
+// Each unit screens only the blocks of its own row (rows may hold different
+// numbers of tokens); bounds past the row's last block are not written, apart
+// from -inf in the float4 that holds that block.
+//
 // With PRED the workgroup first evaluates the threshold predictor of its unit
 // (evolve.pub review, "Methodology Assessment", Eq. 1: tau = qbar . W + b over
 // the concatenated queries of the batch row) and stores tau for the attention.
@@ -47,6 +51,7 @@ struct ScreenArgs {
     int32_t *adm_idx;
     int32_t *adm_cnt;
     float *bound_out;
+    KVLayout lay;  // per-row token counts (the K/V addresses are not used here)
 };
 
 template <int D, bool PRED>
@@ -95,6 +100,7 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
     const float geo_scale = a.s * qn;
     const float z_scale = a.z * qn;
 
+    const int nblk = (a.lay.row_len(u / a.H) + kBlockTokens - 1) / kBlockTokens;  // this row's blocks
     const int ukv = u / a.G;  // the key/value unit whose metadata this query head screens
     const float *cu = a.centroid + (size_t)ukv * D * a.nblk_cap;
     const float *vu = a.var + (size_t)ukv * a.nblk_cap;
@@ -104,9 +110,9 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
     const int d0 = slice * dps;
 
     int base = 0;
-    for (int pass0 = 0; pass0 < a.nblk; pass0 += a.nbg * kBlocksPerWave) {
+    for (int pass0 = 0; pass0 < nblk; pass0 += a.nbg * kBlocksPerWave) {
         const int blk0 = pass0 + grp * kBlocksPerWave + lane * kBlocksPerLane;
-        const bool active = blk0 < a.nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
+        const bool active = blk0 < nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (active && !a.geo_only) {
 #pragma unroll 16
@@ -160,12 +166,12 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (blk0 + j >= a.nblk) U[j] = -INFINITY;
+                    if (blk0 + j >= nblk) U[j] = -INFINITY;
             }
             int total = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                adm[j] = active && (blk0 + j < a.nblk) && (U[j] >= t);
+                adm[j] = active && (blk0 + j < nblk) && (U[j] >= t);
                 const uint64_t mask = __ballot(adm[j]);
                 before += __popcll(mask & lanes_below);
                 total += __popcll(mask);
@@ -234,6 +240,7 @@ hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau,
     a.adm_idx = idx;
     a.adm_cnt = cnt;
     a.bound_out = bound_out;
+    a.lay = g.lay;
     const dim3 block(a.nbg * a.ds * kWave);
     if (predict) {
         hipLaunchKernelGGL((screen_kernel<D, true>), dim3((unsigned)g.units), block, 0, st, a);

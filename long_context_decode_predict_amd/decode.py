@@ -7,6 +7,10 @@ the current stream with no host synchronisation:
 eta_predict_tau + eta_screen (or eta_predict_screen in one launch)
 [-> eta_admit_union for grouped heads] -> eta_decode_attn
 (= eta_decode_attn_partial followed by eta_decode_attn_combine).
+
+With ``layout`` (a ``_lib.KVLayout``) the rows hold their own lengths and/or the
+K/V bytes live in a page pool; the step reads the layout's tensors at run time,
+so a captured graph follows in-place updates of the lengths and page table.
 """
 from __future__ import annotations
 
@@ -17,8 +21,9 @@ from . import _lib
 
 class DecodeStep:
     def __init__(self, B, H, d, T_cap, kv_dtype=torch.bfloat16, params=None, device="cuda",
-                 with_bounds=False, H_kv=None):
+                 with_bounds=False, H_kv=None, layout=None):
         self.B, self.H, self.d, self.T_cap = B, H, d, T_cap
+        self.layout = layout
         self.H_kv = H if H_kv is None else H_kv
         self.G = H // self.H_kv
         self.kv_dtype = kv_dtype
@@ -46,12 +51,13 @@ class DecodeStep:
     def predict_screen(self, q, W, bias, meta, T, stream=None):
         _lib.eta_predict_screen(q, W, bias, meta, T, self.T_cap, self.params, self.tau,
                                 self.adm_idx, self.adm_cnt, self.bounds, self.kv_dtype, stream,
-                                self._hkv_arg)
+                                self._hkv_arg, self.layout)
         self.union(T, stream)
 
     def screen(self, q, meta, T, stream=None):
         _lib.eta_screen(q, self.tau, meta, T, self.T_cap, self.params, self.adm_idx,
-                        self.adm_cnt, self.bounds, self.kv_dtype, stream, self._hkv_arg)
+                        self.adm_cnt, self.bounds, self.kv_dtype, stream, self._hkv_arg,
+                        self.layout)
         self.union(T, stream)
 
     def union(self, T, stream=None):
@@ -61,15 +67,16 @@ class DecodeStep:
 
     def attend(self, q, K, V, T, stream=None):
         _lib.eta_decode_attn(q, K, V, T, self.tau, self.uni_idx, self.uni_cnt, self.params,
-                             self.out, self.lse, self.ws, stream)
+                             self.out, self.lse, self.ws, stream, self.layout)
 
     def attend_partial(self, q, K, V, T, stream=None):
         _lib.eta_decode_attn_partial(q, K, V, T, self.tau, self.uni_idx, self.uni_cnt,
-                                     self.params, self.out, self.lse, self.ws, stream)
+                                     self.params, self.out, self.lse, self.ws, stream,
+                                     self.layout)
 
     def attend_combine(self, K, T, stream=None):
         _lib.eta_decode_attn_combine(K, T, self.uni_cnt, self.params, self.out, self.lse,
-                                     self.ws, stream)
+                                     self.ws, stream, self.layout)
 
     def capture(self, q, K, V, T, meta, W, bias, fused=True):
         """Record one step into a HIP graph (torch.cuda.CUDAGraph) and return it; each

@@ -16,6 +16,12 @@ to in trained models. Optional "needle" keys: in a
 fraction of the blocks one key at a seeded slot is replaced by
 r * (0.9 * q_hat + sqrt(0.19) * u), u a random unit vector orthogonal to q_hat,
 r = sqrt(d (1 + sigma^2)) -- a key aligned with the query at cosine 0.9.
+Variable-length rows: row b holds T_b tokens, drawn uniformly in
+[(1 - var_len) T, T] (the largest row is set to T). Paged caches: each present
+64-token block of each row gets its own page of a pool [P, H_kv, 64, d], pages
+assigned in a seeded random order; pages no block uses, and the rows past T_b of
+a row's last page, are filled with NaN, so that any read the layout does not
+allow shows in the results.
 All draws use torch generators seeded per workload on the target device.
 """
 from __future__ import annotations
@@ -45,6 +51,8 @@ class Workload:
     append: int = 0             # tokens appended one by one before the step
     H_kv: int = 0               # key/value heads (0: multi-head, H_kv = H)
     group_corr: float = 0.0     # shared direction of a group's queries (grouped heads)
+    var_len: float = 0.0        # row lengths ~ U[(1 - var_len) T, T] (0: every row holds T)
+    paged: bool = False         # K/V in a shuffled page pool with a page table
     seed: int = SEED_BASE
     note: str = field(default="", compare=False)
 
@@ -94,6 +102,10 @@ WORKLOADS = {
         "gqa_b32_h32kv8_d128_t128k_bf16", B=32, H=32, d=128, T=131072,
         kv_dtype=torch.bfloat16, H_kv=8, group_corr=0.95, seed=SEED_BASE + 5,
         note="grouped heads (4 query heads per key/value head), union loading"),
+    "paged_b64_h16_d128_t128k_bf16": Workload(
+        "paged_b64_h16_d128_t128k_bf16", B=64, H=16, d=128, T=131072,
+        kv_dtype=torch.bfloat16, var_len=0.5, paged=True, seed=SEED_BASE + 6,
+        note="paged pool, shuffled pages, row lengths 64k..128k"),
 }
 
 HEADLINE = "headline_b64_h16_d128_t128k_bf16"
@@ -192,3 +204,61 @@ def plant_needles(w: Workload, q, K, sig, g, T_cap):
     rows = torch.arange(units, device=dev)[:, None].expand_as(tok)
     Kf[rows.reshape(-1), tok.reshape(-1)] = key.reshape(-1, d).to(K.dtype)
     return torch.stack([rows.reshape(-1), (tok // BLOCK).reshape(-1), (tok % BLOCK).reshape(-1)], 1)
+
+
+def row_lengths(w: Workload) -> list[int]:
+    """Seeded tokens per row: every row holds T unless var_len > 0."""
+    if w.var_len <= 0:
+        return [w.T] * w.B
+    g = _gen("cpu", w.seed + 11)
+    lo = int(math.floor((1.0 - w.var_len) * w.T))
+    lens = torch.randint(lo, w.T + 1, (w.B,), generator=g).tolist()
+    lens[int(torch.randint(0, w.B, (1,), generator=g))] = w.T  # the largest row holds T
+    return [int(t) for t in lens]
+
+
+def page_pool(K: torch.Tensor, V: torch.Tensor, lens, seed: int, spare: int = 3,
+              all_blocks: bool = False):
+    """Scatter a dense cache [B,H_kv,T_cap,d] into a shuffled page pool.
+
+    Returns (page_table int32 [B, T_cap/64], Kp, Vp [P,H_kv,64,d]). Block j of row b
+    gets a page when j < ceil(lens[b] / 64) (every block with all_blocks); the
+    table holds an out-of-range id (-1, or P + 5 on odd rows) for the others.
+    Unused pages and the rows past lens[b] of a row's last page are NaN."""
+    B, Hk, T_cap, d = K.shape
+    mp = T_cap // BLOCK
+    dev = K.device
+    need = [mp if all_blocks else (int(t) + BLOCK - 1) // BLOCK for t in lens]
+    n_used = sum(need)
+    P = n_used + spare
+    g = _gen("cpu", seed + 13)
+    perm = torch.randperm(P, generator=g)
+    table = torch.empty((B, mp), dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[nxt:nxt + need[b]].to(torch.int32)
+        table[b, need[b]:] = -1 if b % 2 == 0 else P + 5
+        nxt += need[b]
+    Kp = torch.full((P, Hk, BLOCK, d), float("nan"), dtype=K.dtype, device=dev)
+    Vp = torch.full((P, Hk, BLOCK, d), float("nan"), dtype=V.dtype, device=dev)
+    for b in range(B):  # one row at a time: no dense-sized temporaries
+        if need[b] == 0:
+            continue
+        pages = table[b, :need[b]].to(dev, torch.long)
+        Kp[pages] = K[b, :, :need[b] * BLOCK].reshape(Hk, need[b], BLOCK, d).transpose(0, 1)
+        Vp[pages] = V[b, :, :need[b] * BLOCK].reshape(Hk, need[b], BLOCK, d).transpose(0, 1)
+        tail = int(lens[b]) % BLOCK
+        if tail and not all_blocks:
+            last = int(table[b, need[b] - 1])
+            Kp[last, :, tail:] = float("nan")
+            Vp[last, :, tail:] = float("nan")
+    return table.to(dev), Kp, Vp
+
+
+def gather_unit(pool: torch.Tensor, table: torch.Tensor, b: int, k: int, T_b: int) -> torch.Tensor:
+    """The first T_b tokens [T_b, d] of key/value head k of row b, read through the table."""
+    nb = (T_b + BLOCK - 1) // BLOCK
+    if nb == 0:
+        return pool.new_empty((0, pool.shape[-1]))
+    pages = table[b, :nb].to(pool.device, torch.long)
+    return pool[pages, k].reshape(nb * BLOCK, pool.shape[-1])[:T_b]

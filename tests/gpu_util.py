@@ -43,7 +43,8 @@ class Case:
     """A workload instance on the GPU plus the library's results for one step."""
 
     def __init__(self, w: workloads.Workload, tau_mode="predictor", params=None, T=None,
-                 T_cap=None, bias=None, fused=False):
+                 T_cap=None, bias=None, fused=False, seq_lens=None, paged=None,
+                 all_pages=False):
         self.fused = fused
         self.w = w
         self.T_cap = T_cap if T_cap is not None else w.T_cap
@@ -59,18 +60,41 @@ class Case:
         else:
             val = {"neg_inf": -math.inf, "pos_inf": math.inf, "nan": math.nan}[tau_mode]
             self.bias = torch.full((w.H,), val, dtype=torch.float32, device="cuda")
+        # optional per-row lengths and page pool (the dense K/V stay for the oracle)
+        if seq_lens is None and w.var_len > 0:
+            seq_lens = workloads.row_lengths(w)
+        self.row_T = None if seq_lens is None else [int(t) for t in seq_lens]
+        paged = w.paged if paged is None else paged
+        self.layout = None
+        if self.row_T is not None or paged:
+            lens = (None if self.row_T is None else
+                    torch.tensor(self.row_T, dtype=torch.int32, device="cuda"))
+            table = None
+            if paged:
+                table, d["Kp"], d["Vp"] = workloads.page_pool(
+                    d["K"], d["V"], self.row_T or [self.T] * w.B, w.seed, all_blocks=all_pages)
+            self.layout = _lib.KVLayout(lens, table)
         self.meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, self.T_cap)
         self.step = DecodeStep(w.B, w.H, w.d, self.T_cap, w.kv_dtype, self.params,
-                               with_bounds=True, H_kv=w.kv_heads)
+                               with_bounds=True, H_kv=w.kv_heads, layout=self.layout)
+
+    def kv(self):
+        """The K, V the library reads: the page pools of a paged case, else the cache."""
+        d = self.data
+        return (d["Kp"], d["Vp"]) if d.get("Kp") is not None else (d["K"], d["V"])
+
+    def row_len(self, b: int) -> int:
+        return self.T if self.row_T is None else self.row_T[b]
 
     def build_meta(self):
-        _lib.eta_build_block_meta(self.data["K"], self.T, self.meta)
+        _lib.eta_build_block_meta(self.kv()[0], self.T, self.meta, layout=self.layout)
 
     def run(self, build=True):
         if build:
             self.build_meta()
         d = self.data
-        self.step(d["q"], d["K"], d["V"], self.T, self.meta, self.W, self.bias, fused=self.fused)
+        K, V = self.kv()
+        self.step(d["q"], K, V, self.T, self.meta, self.W, self.bias, fused=self.fused)
         torch.cuda.synchronize()
         return self
 
@@ -91,29 +115,32 @@ class Case:
         torch.cuda.empty_cache()
 
 
-def check_list_properties(g: dict, nblk: int):
-    """Every unit's list is strictly ascending, in range and exactly cnt long."""
+def check_list_properties(g: dict, nblk, rows: int | None = None):
+    """Every unit's list is strictly ascending, in range and exactly cnt long.
+    nblk: one block count for all units, or one per batch row (rows = batch size)."""
     cnt = g["cnt"].reshape(-1)
     idx = g["idx"].reshape(cnt.shape[0], -1)
-    assert np.all(cnt >= 0) and np.all(cnt <= nblk)
+    per_unit = (np.full(cnt.shape[0], nblk) if np.isscalar(nblk)
+                else np.repeat(np.asarray(nblk), cnt.shape[0] // rows))
+    assert np.all(cnt >= 0) and np.all(cnt <= per_unit)
     for u in range(cnt.shape[0]):
         lst = idx[u, :cnt[u]]
         assert np.all(np.diff(lst) > 0), u
         if len(lst):
-            assert lst[0] >= 0 and lst[-1] < nblk, u
+            assert lst[0] >= 0 and lst[-1] < per_unit[u], u
 
 
 def compare_units(case: Case, units, O=None, check_meta=True):
     """Compare the library against the oracle on the given units; returns stats."""
     O = O or oracle_mod.default()
-    w, T, p = case.w, case.T, case.params
+    w, p = case.w, case.params
     g = case.host()
     q = case.data["q"].cpu().numpy()
     W = None if case.W is None else case.W.cpu().numpy()
     bias = case.bias.cpu().numpy()
     tau_o = O.predict_tau(q, W, bias)
-    nblk = (T + 63) // 64
-    check_list_properties(g, nblk)
+    rows_nblk = [(case.row_len(b) + 63) // 64 for b in range(w.B)]
+    check_list_properties(g, rows_nblk, w.B)
     tau_g = g["tau"]
     fin = np.isfinite(tau_o)
     assert np.array_equal(fin, np.isfinite(tau_g))
@@ -123,6 +150,8 @@ def compare_units(case: Case, units, O=None, check_meta=True):
     tol = OUT_TOL[w.kv_dtype]
     for u in units:
         b, h = divmod(int(u), w.H)
+        T = case.row_len(b)
+        nblk = rows_nblk[b]
         Kh = kv_host(case.data["K"][b, h])
         Vh = kv_host(case.data["V"][b, h])
         c, v, m = O.block_meta(Kh, T)
@@ -170,15 +199,15 @@ def compare_gqa_units(case: Case, kv_units, O=None):
     """Grouped heads: per query head masks, the union of each key/value head's lists,
     and every query head's output over that union, against the oracle."""
     O = O or oracle_mod.default()
-    w, T, p = case.w, case.T, case.params
+    w, p = case.w, case.params
     G = w.G
     g = case.host()
     q = case.data["q"].cpu().numpy()
     W = None if case.W is None else case.W.cpu().numpy()
     tau_o = O.predict_tau(q, W, case.bias.cpu().numpy())
-    nblk = (T + 63) // 64
-    check_list_properties(g, nblk)
-    check_list_properties({"cnt": g["uni_cnt"], "idx": g["uni_idx"]}, nblk)
+    rows_nblk = [(case.row_len(b) + 63) // 64 for b in range(w.B)]
+    check_list_properties(g, rows_nblk, w.B)
+    check_list_properties({"cnt": g["uni_cnt"], "idx": g["uni_idx"]}, rows_nblk, w.B)
     fin = np.isfinite(tau_o)
     assert np.array_equal(fin, np.isfinite(g["tau"]))
     assert np.all(np.abs(g["tau"][fin] - tau_o[fin]) <= TAU_TOL)
@@ -187,6 +216,8 @@ def compare_gqa_units(case: Case, kv_units, O=None):
     tol = OUT_TOL[w.kv_dtype]
     for uk in kv_units:
         b, k = divmod(int(uk), w.kv_heads)
+        T = case.row_len(b)
+        nblk = rows_nblk[b]
         Kh = kv_host(case.data["K"][b, k])
         Vh = kv_host(case.data["V"][b, k])
         c, v, m = O.block_meta(Kh, T)

@@ -191,3 +191,52 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros((1, 2, 64))
     with pytest.raises(ValueError):
         _lib.eta_predict_tau(q, None, torch.zeros(2), torch.zeros((1, 2)))
+
+
+def test_layout_errors(L):
+    """Paged / variable-length descriptors: a page table needs a positive pool size,
+    a pool size needs a page table, and both arrays must be int32-aligned."""
+    m = BY(meta())
+    assert L.eta_build_block_meta(BY(shape(page_table=FAKE, num_pages=0)), FAKE, m, None) == INV
+    assert L.eta_build_block_meta(BY(shape(page_table=FAKE, num_pages=-3)), FAKE, m, None) == INV
+    assert L.eta_build_block_meta(BY(shape(num_pages=5)), FAKE, m, None) == INV
+    assert L.eta_build_block_meta(BY(shape(seq_lens=FAKE + 2)), FAKE, m, None) == INV
+    assert L.eta_build_block_meta(BY(shape(page_table=FAKE + 2, num_pages=4)), FAKE, m, None) == INV
+    assert L.eta_build_block_meta(BY(shape(page_table=FAKE, num_pages=1 << 30)), FAKE, m,
+                                  None) == INV  # pool offsets bounded
+    p = BY(params())
+    assert L.eta_screen(BY(shape(num_pages=2)), FAKE, FAKE, m, p, FAKE, FAKE, None, None) == INV
+    s = BY(shape(page_table=FAKE, num_pages=0))
+    assert L.eta_decode_attn_workspace_size(s, p) == 0
+    # the workspace does not depend on the layout
+    assert (L.eta_decode_attn_workspace_size(BY(shape(seq_lens=FAKE, page_table=FAKE,
+                                                      num_pages=9)), p)
+            == L.eta_decode_attn_workspace_size(BY(shape()), p))
+
+
+def test_page_pool_round_trip():
+    """The page-pool generator: every row's logical keys read back through the table,
+    absent blocks carry out-of-range ids, unused pages are NaN (host only)."""
+    import torch
+    from long_context_decode_predict_amd import workloads as wl
+    w = wl.custom("pp", B=4, H=2, d=64, T=300, kv_dtype=torch.float32, seed=5)
+    d = wl.generate(w, "cpu", T_cap=320)
+    lens = [300, 0, 65, 64]
+    tbl, Kp, Vp = wl.page_pool(d["K"], d["V"], lens, 5, spare=2)
+    P = Kp.shape[0]
+    assert P == 5 + 0 + 2 + 1 + 2
+    used = set()
+    for b, t in enumerate(lens):
+        nb = (t + 63) // 64
+        row = tbl[b].tolist()
+        assert all(0 <= x < P for x in row[:nb]) and all(x < 0 or x >= P for x in row[nb:])
+        used |= set(row[:nb])
+        for k in range(2):
+            assert torch.equal(wl.gather_unit(Kp, tbl, b, k, t), d["K"][b, k, :t])
+            assert torch.equal(wl.gather_unit(Vp, tbl, b, k, t), d["V"][b, k, :t])
+    assert len(used) == P - 2  # distinct pages, two spares
+    for x in set(range(P)) - used:
+        assert torch.isnan(Kp[x]).all() and torch.isnan(Vp[x]).all()
+    assert torch.isnan(Kp[tbl[2, 1], :, 1:]).all()  # past row 2's length in its last page
+    lens_w = wl.row_lengths(wl.WORKLOADS["paged_b64_h16_d128_t128k_bf16"])
+    assert max(lens_w) == 131072 and min(lens_w) >= 65536 and len(lens_w) == 64
