@@ -11,6 +11,7 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -223,6 +224,65 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, lens, max_units=256, thr
             "gpu_over_cpu": (1000.0 / step_gpu_ms) * step_s}
 
 
+def unit_kv(data, b, k, T_b):
+    """Device K, V [T_b, d] of key/value head k of row b, in either layout."""
+    if "Kp" in data:
+        return (workloads.gather_unit(data["Kp"], data["table"], b, k, T_b),
+                workloads.gather_unit(data["Vp"], data["table"], b, k, T_b))
+    return data["K"][b, k, :T_b], data["V"][b, k, :T_b]
+
+
+def screen_misses(step, data, w, lens, n_units=16):
+    """Blocks the screen skipped although one of their keys scores at or above tau
+    (the exact block maxima from plain torch matmuls on a seeded sample of query
+    heads), over the blocks whose maximum reaches tau. The combined bound is not a
+    guarantee at z = 4, so this rate is measured, not assumed."""
+    rng = np.random.default_rng(w.seed + 5)
+    units = rng.choice(w.B * w.H, size=min(n_units, w.B * w.H), replace=False)
+    q = data["q"]
+    tau = step.tau.cpu()
+    cnt = step.adm_cnt.cpu()
+    idx = step.adm_idx.cpu()
+    reach = missed = 0
+    for u in units:
+        b, h = divmod(int(u), w.H)
+        T_b = lens[b]
+        nb = (T_b + 63) // 64
+        if nb == 0:
+            continue
+        K, _ = unit_kv(data, b, h // w.G, T_b)
+        S = (K.float() @ q[b, h]) / math.sqrt(w.d)
+        pad = torch.full((nb * 64,), -math.inf, device=S.device)
+        pad[:T_b] = S
+        bmax = pad.view(nb, 64).max(dim=1).values.cpu()
+        hot = bmax >= float(tau[b, h])
+        adm = torch.zeros(nb, dtype=torch.bool)
+        adm[idx[b, h, :int(cnt[b, h])].long()] = True
+        reach += int(hot.sum())
+        missed += int((hot & ~adm).sum())
+    return {"blocks_reaching_tau": reach, "skipped_of_those": missed,
+            "rate": missed / reach if reach else 0.0, "sampled_query_heads": len(units)}
+
+
+def density_sweep(step, data, w, meta, W, params, lens, steps, fused):
+    """Step time against the admitted fraction: the predictor bias is re-calibrated
+    for each target density, everything else fixed."""
+    rows_nblk = np.array([(t + 63) // 64 for t in lens], dtype=np.float64)
+    out = []
+    for rho in (0.05, 0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9):
+        bias = calibrate.bias_for(dataclasses.replace(w, density=rho), data["q"], W, z=params.z)
+        ms, attn_ms, _, _ = time_steps(step, data, w, meta, W, bias, steps, 2, fused)
+        cnt = step.adm_cnt.cpu().numpy()
+        ucnt = step.uni_cnt.cpu().numpy()
+        out.append({"target": rho,
+                    "density": float((cnt / np.maximum(rows_nblk, 1)[:, None]).mean()),
+                    "loaded_density": float((ucnt / np.maximum(rows_nblk, 1)[:, None]).mean()),
+                    "ms_per_step": ms, "attn_partial_ms": attn_ms})
+        log(f"[bench] sweep target {rho:.2f}: density {out[-1]['density']:.3f} "
+            f"{ms:.3f} ms/step")
+    return out
+
+
 def copy_probe(gib: float, reps: int):
     """Time torch's device-to-device copy of `gib` GiB (read + write bytes counted)."""
     n = int(gib * (1 << 30)) // 4
@@ -251,6 +311,8 @@ def main():
     ap.add_argument("--workload", default=workloads.HEADLINE, choices=list(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the density sweep (step time at admitted fractions 5..90%%)")
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--unfused", action="store_true",
                     help="separate eta_predict_tau + eta_screen launches instead of "
@@ -370,6 +432,9 @@ def main():
             hit += int(np.isin(blk, idx[b, h, :cnt[b, h]]))
         extra["needle_block_recall"] = hit / len(nd)
 
+    extra["screen_misses"] = screen_misses(step, data, w, lens)
+    log(f"[bench] screen misses {extra['screen_misses']}")
+
     if not args.no_dense:
         dense_bias = torch.full((w.H,), -math.inf, device="cuda")
         dms, dattn, _, _ = time_steps(step, data, w, meta, None, dense_bias,
@@ -382,6 +447,10 @@ def main():
             "attn_gbs": (d_bytes + units * w.d * 8) / (dattn * 1e-3) / 1e9,
             "sparse_speedup": dms / ms}
         log(f"[bench] dense reference {dms:.3f} ms/step")
+
+    if not args.no_sweep and not w.static_tau:
+        extra["density_sweep"] = density_sweep(step, data, w, meta, W, params, lens,
+                                               max(5, args.steps // 5), fused)
 
     cpu = None
     if not args.no_cpu_baseline:
