@@ -27,6 +27,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* bfloat16 is the upper half of an IEEE binary32: widen by a 16-bit shift. */
@@ -233,4 +234,39 @@ void eta_oracle_attend(int T, int d, int bs, int kv_dtype, const float *q_unit,
     }
     for (int i = 0; i < d; ++i) out[i] /= l;
     *lse = mu + log(l);
+}
+
+/* Training-time forward (review "Methodology Assessment", Eq. 1-3 applied to
+ * every query token; abstract: sub-threshold logits are suppressed toward zero
+ * during training): the T_q queries are the last T_q positions of the T_k
+ * keys, and query t (position T_k - T_q + t) sees keys 0 .. its position.
+ * For each query: out and lse are the gated attention of eta_oracle_attend
+ * over its visible keys (all their blocks admitted), and gate_sum is the sum
+ * of the gates eta_oracle_gate(S_j) over those keys.
+ * Q float32 [T_q][d]; tau fp64 [T_q]; out fp64 [T_q][d]; lse, gate_sum
+ * fp64 [T_q]. Returns 0, or -1 when scratch memory cannot be had. */
+int eta_oracle_prefill(int T_q, int T_k, int d, int kv_dtype, const float *Q, const void *K,
+                       const void *V, const double *tau, double gate_beta, int gate_hard,
+                       double *out, double *lse, double *gate_sum) {
+    const int bs = 64;
+    double s = 1.0 / sqrt((double)d);
+    int nblk_max = (T_k + bs - 1) / bs;
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)(nblk_max > 0 ? nblk_max : 1));
+    if (idx == NULL) return -1;
+    for (int b = 0; b < nblk_max; ++b) idx[b] = b;
+    for (int t = 0; t < T_q; ++t) {
+        int n = T_k - T_q + t + 1; /* visible keys */
+        const float *q = Q + (long)t * d;
+        eta_oracle_attend(n, d, bs, kv_dtype, q, K, V, tau[t], idx, (n + bs - 1) / bs,
+                          gate_beta, gate_hard, out + (long)t * d, lse + t);
+        double gs = 0.0;
+        for (long j = 0; j < n; ++j) {
+            double dot = 0.0;
+            for (int i = 0; i < d; ++i) dot += (double)q[i] * kv_at(K, kv_dtype, d, j, i);
+            gs += eta_oracle_gate(s * dot, tau[t], gate_beta, gate_hard);
+        }
+        gate_sum[t] = gs;
+    }
+    free(idx);
+    return 0;
 }

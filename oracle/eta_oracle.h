@@ -73,6 +73,16 @@ void eta_oracle_attend(int T, int d, int bs, int kv_dtype, const float *q_unit,
                        int cnt, double gate_beta, int gate_hard, double *out,
                        double *lse);
 
+/* Training-time forward of a whole (row, head): the T_q queries Q [T_q][d]
+ * (float32) are the last T_q positions of the T_k keys; query t sees keys
+ * 0 .. T_k - T_q + t. Per query: out [d] and lse as eta_oracle_attend over its
+ * visible keys, and gate_sum = the sum of gate(S_j) over them. tau fp64
+ * [T_q]; out fp64 [T_q][d]; lse, gate_sum fp64 [T_q]. Returns 0, or -1 when
+ * scratch memory cannot be had (freed before returning). */
+int eta_oracle_prefill(int T_q, int T_k, int d, int kv_dtype, const float *Q, const void *K,
+                       const void *V, const double *tau, double gate_beta, int gate_hard,
+                       double *out, double *lse, double *gate_sum);
+
 #ifdef __cplusplus
 }
 #endif

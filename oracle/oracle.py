@@ -78,6 +78,10 @@ class OracleLib:
         L.eta_oracle_attend.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         _fp, _vp, _vp, ctypes.c_double, _ip, ctypes.c_int,
                                         ctypes.c_double, ctypes.c_int, _dp, _dp]
+        L.eta_oracle_prefill.restype = ctypes.c_int
+        L.eta_oracle_prefill.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         _fp, _vp, _vp, _dp, ctypes.c_double, ctypes.c_int,
+                                         _dp, _dp, _dp]
         self.L = L
         self.path = path
 
@@ -168,6 +172,31 @@ class OracleLib:
                                  len(idx), float(beta), int(bool(hard)),
                                  out.ctypes.data_as(_dp), lse.ctypes.data_as(_dp))
         return out, float(lse[0])
+
+    def prefill(self, Q, K, V, T_k: int, tau, beta: float = 5.0, hard: bool = False):
+        """Training-time forward of one (row, head): Q [T_q, d] (float32, or uint16
+        bf16 bit patterns, widened exactly), K, V [>= T_k, d], tau [T_q]; query t sits
+        at position T_k - T_q + t. Returns (out fp64 [T_q, d], lse [T_q],
+        gate_sum [T_q])."""
+        if Q.dtype == np.uint16:
+            Q = (np.ascontiguousarray(Q).astype(np.uint32) << 16).view(np.float32)
+        Q = _c(Q, np.float32)
+        T_q, d = Q.shape
+        K, kvd = _kv(K)
+        V, kvd_v = _kv(V)
+        assert kvd == kvd_v and K.shape == V.shape and K.shape[1] == d
+        assert 0 <= T_q <= T_k <= K.shape[0]
+        tau = _c(tau, np.float64)
+        out = np.empty((max(T_q, 1), d), dtype=np.float64)
+        lse = np.empty(max(T_q, 1), dtype=np.float64)
+        gs = np.empty(max(T_q, 1), dtype=np.float64)
+        tau_buf = tau if T_q else np.zeros(1)
+        rc = self.L.eta_oracle_prefill(T_q, T_k, d, kvd, Q.ctypes.data_as(_fp), K.ctypes.data,
+                                       V.ctypes.data, tau_buf.ctypes.data_as(_dp), float(beta),
+                                       int(bool(hard)), out.ctypes.data_as(_dp),
+                                       lse.ctypes.data_as(_dp), gs.ctypes.data_as(_dp))
+        assert rc == 0
+        return out[:T_q], lse[:T_q], gs[:T_q]
 
     def unit_step(self, q_unit, K, V, T, tau, meta, z=4.0, mode=BOUND_COMBINED, beta=5.0,
                   hard=False, bs=64):

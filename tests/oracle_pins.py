@@ -430,4 +430,82 @@ def check_attend_ignores_tail_and_order(O):
     assert abs(lse - ref_lse) < 1e-13
 
 
+def _sdpa_rows(Q, K, V, mask):
+    """Library attention of many queries in float64 with an additive mask [T_q, T_k]
+    (-inf hides a key); returns (out [T_q, d], lse [T_q])."""
+    Qt = torch.from_numpy(np.asarray(Q, dtype=np.float64))[None, None]
+    Kt = torch.from_numpy(np.asarray(K, dtype=np.float64))[None, None]
+    Vt = torch.from_numpy(np.asarray(V, dtype=np.float64))[None, None]
+    mt = torch.from_numpy(np.asarray(mask, dtype=np.float64))[None, None]
+    out = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, attn_mask=mt)
+    logits = (Qt[0, 0] @ Kt[0, 0].T) / math.sqrt(K.shape[1]) + mt[0, 0]
+    return out[0, 0].numpy(), torch.logsumexp(logits, dim=1).numpy()
+
+
+def _causal(T_q, T_k):
+    """Visibility of the training-time forward: query t sits at position T_k - T_q + t."""
+    return np.arange(T_k)[None, :] <= (T_k - T_q + np.arange(T_q))[:, None]
+
+
+def check_prefill_dense_is_causal_sdpa(O):
+    """tau = -inf: every gate is 1, so the training-time forward is causal softmax
+    attention (library SDPA in float64 with a bottom-right causal mask), for a whole
+    sequence and for a chunk continuing a prefix; the gate sum counts the visible keys."""
+    rng = np.random.default_rng(21)
+    d = 16
+    K = rng.standard_normal((150, d)).astype(np.float32)
+    V = rng.standard_normal((150, d)).astype(np.float32)
+    for T_q, T_k in [(130, 130), (37, 150), (1, 1), (1, 150)]:
+        Q = rng.standard_normal((T_q, d)).astype(np.float32)
+        vis = _causal(T_q, T_k)
+        want, want_lse = _sdpa_rows(Q, K[:T_k], V[:T_k], np.where(vis, 0.0, -np.inf))
+        out, lse, gs = O.prefill(Q, K, V, T_k, np.full(T_q, -np.inf))
+        np.testing.assert_allclose(out, want, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, want_lse, rtol=0, atol=1e-12)
+        assert np.array_equal(gs, vis.sum(axis=1).astype(np.float64))
+
+
+def check_prefill_gated_is_masked_sdpa(O):
+    """Finite per-token tau: the training-time forward equals SDPA with the additive
+    mask S' - S on visible keys (gate from scipy's logistic function, an independent
+    library routine) and -inf on hidden ones; the gate sum is the sum of those gates
+    (soft) or the count of visible S >= tau (hard); bf16 K/V widened exactly."""
+    from scipy.special import expit
+    rng = np.random.default_rng(22)
+    d, T_q, T_k = 16, 70, 200
+    K32 = _clustered(rng, 4, d)[:T_k]
+    V32 = rng.standard_normal((T_k, d)).astype(np.float32)
+    Q = rng.standard_normal((T_q, d)).astype(np.float32)
+    tau = rng.normal(0.3, 0.5, T_q)
+    vis = _causal(T_q, T_k)
+    for KK, VV, Kv, Vv in [(K32, V32, K32, V32),
+                           (f32_to_bf16_bits(K32), f32_to_bf16_bits(V32),
+                            bf16_bits_to_f64(f32_to_bf16_bits(K32)),
+                            bf16_bits_to_f64(f32_to_bf16_bits(V32)))]:
+        S = (Q.astype(np.float64) @ np.asarray(Kv, np.float64).T) / math.sqrt(d)
+        for beta, hard in [(5.0, False), (1.0, False), (5.0, True)]:
+            gate = (S >= tau[:, None]).astype(np.float64) if hard else expit(beta * (S - tau[:, None]))
+            mask = np.where(vis, S * gate - S, -np.inf)
+            want, want_lse = _sdpa_rows(Q, Kv, Vv, mask)
+            out, lse, gs = O.prefill(Q, KK, VV, T_k, tau, beta=beta, hard=hard)
+            np.testing.assert_allclose(out, want, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse, want_lse, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(gs, np.where(vis, gate, 0.0).sum(axis=1), rtol=0, atol=1e-9)
+
+
+def check_prefill_uniform_floor(O):
+    """tau = +inf suppresses every logit to 0 (weight e^0 = 1): each query's output is
+    the plain mean of its visible values, lse = log(visible count), gate sum 0."""
+    rng = np.random.default_rng(23)
+    d, T_q, T_k = 8, 20, 90
+    K = rng.standard_normal((T_k, d)).astype(np.float32)
+    V = rng.standard_normal((T_k, d)).astype(np.float32)
+    Q = rng.standard_normal((T_q, d)).astype(np.float32)
+    out, lse, gs = O.prefill(Q, K, V, T_k, np.full(T_q, np.inf))
+    for t in range(T_q):
+        n = T_k - T_q + t + 1
+        np.testing.assert_allclose(out[t], V[:n].astype(np.float64).mean(axis=0), rtol=0, atol=1e-12)
+        assert abs(lse[t] - math.log(n)) < 1e-12 and gs[t] == 0.0
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -48,6 +48,14 @@ MUTANTS = [
     ("union_first_list_only", "for (int j = 0; j < g && !hit; ++j)", "for (int j = 0; j < 1 && !hit; ++j)"),
     ("union_wrong_row_stride", "if (lists[(long)j * stride + a] == blk) hit = 1;",
      "if (lists[(long)j * g + a] == blk) hit = 1;"),
+    ("prefill_window_short", "int n = T_k - T_q + t + 1; /* visible keys */",
+     "int n = T_k - T_q + t; /* visible keys */"),
+    ("prefill_window_top_left", "int n = T_k - T_q + t + 1; /* visible keys */",
+     "int n = t + 1; /* visible keys */"),
+    ("gate_sum_counts_keys", "gs += eta_oracle_gate(s * dot, tau[t], gate_beta, gate_hard);",
+     "gs += 1.0;"),
+    ("gate_sum_unscaled", "gs += eta_oracle_gate(s * dot, tau[t], gate_beta, gate_hard);",
+     "gs += eta_oracle_gate(dot, tau[t], gate_beta, gate_hard);"),
     ("union_skips_first_head", "for (int j = 0; j < g && !hit; ++j)", "for (int j = 1; j < g && !hit; ++j)"),
 ]
 
