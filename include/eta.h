@@ -261,6 +261,64 @@ eta_status eta_decode_attn_combine(const eta_shape *s, const int32_t *adm_cnt,
                                    const eta_params *p, float *out, float *lse, void *ws,
                                    size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Training-time (prefill) forward
+ *
+ * The gate the model is trained with, applied densely: for every query token t
+ * of a sequence and every key j at or before it, S = q_t . k_j / sqrt(d) and
+ * the logit entering the softmax is S * sigmoid(beta * (S - tau_t)) (review
+ * "Methodology Assessment", Eq. 2 and Eq. 3; abstract: sub-threshold logits
+ * are suppressed toward zero during training rather than deleted), tau_t from
+ * Eq. 1 on token t's concatenated queries. Causal: the T_q queries are the
+ * last T_q positions of the T_k keys (T_q = T_k: a whole sequence; T_q < T_k:
+ * a chunk continuing a cached prefix).
+ *
+ * Layouts (bfloat16 unless stated):
+ *   Q     [B][H][T_q][d]         post-RoPE queries
+ *   K, V  [B][H_kv][T_k][d]      (H_kv = 0 means H; query head h reads h / G)
+ *   tau   float32 [B][H][T_q]
+ *   out   float32 [B][H][T_q][d];  lse, gate_sum float32 [B][H][T_q]
+ * d is 64 or 128; Q, K, V and out must be 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int B, H;      /* batch rows, query heads                                */
+    int H_kv;      /* key/value heads: 0 or H, or a divisor with H/H_kv in
+                      {1, 2, 4, 8}                                           */
+    int d;         /* head dimension: 64 or 128                              */
+    int T_q, T_k;  /* queries and keys per row; 0 <= T_q <= T_k; at most
+                      65535 * 128 queries                                    */
+} eta_prefill_shape;
+
+/*
+ * Eq. 1 for every query token: tau[b][h][t] = bias[h] + sum over heads g and
+ * dimensions i of Q[b][g][t][i] * W[g*d + i][h], accumulated in float32 in a
+ * fixed order (the bfloat16 queries are widened exactly). W: float32
+ * [H*d][H] or NULL (frozen per-head thresholds: tau = bias). Only T_q and the
+ * head counts of `s` are used (T_k is ignored).
+ * Errors: ETA_ERR_INVALID_ARG (null pointer, bad shape, misaligned Q),
+ * ETA_ERR_UNSUPPORTED (d not 64 or 128), ETA_ERR_HIP.
+ */
+eta_status eta_prefill_predict_tau(const eta_prefill_shape *s, const void *Q, const float *W,
+                                   const float *bias, float *tau, hipStream_t stream);
+
+/*
+ * Dense causal gated attention. Per query t: softmax over its visible keys of
+ * the gated logits, out = the weighted sum of V, lse = log of the softmax
+ * denominator (natural log, gated-logit units), gate_sum = the sum of the
+ * gates sigmoid(beta * (S - tau_t)) over the visible keys (the statistic a
+ * mean-inclusion regulariser is built from; with gate_hard the number of
+ * visible keys with S >= tau_t). lse and gate_sum may be NULL. Uses
+ * p->gate_beta and p->gate_hard (z, bound_mode and split_blocks are ignored).
+ * Precision: q.k in bfloat16 products with float32 accumulation; the softmax
+ * weights and V enter the weighted sum as float16 (V must lie within
+ * +-65504; magnitudes below 2^-14 keep fewer significant bits), accumulated
+ * in float32.
+ * Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_HIP.
+ */
+eta_status eta_prefill_attn(const eta_prefill_shape *s, const void *Q, const void *K,
+                            const void *V, const float *tau, const eta_params *p, float *out,
+                            float *lse, float *gate_sum, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

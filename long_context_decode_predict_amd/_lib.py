@@ -48,6 +48,11 @@ class eta_meta(ctypes.Structure):
                 ("maxnorm", ctypes.c_void_p), ("nblk_cap", ctypes.c_int)]
 
 
+class eta_prefill_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("H_kv", ctypes.c_int),
+                ("d", ctypes.c_int), ("T_q", ctypes.c_int), ("T_k", ctypes.c_int)]
+
+
 class eta_params(ctypes.Structure):
     _fields_ = [("gate_beta", ctypes.c_float), ("z", ctypes.c_float),
                 ("gate_hard", ctypes.c_int), ("bound_mode", ctypes.c_int),
@@ -80,6 +85,9 @@ SIGNATURES = {
                                                _vp]),
     "eta_decode_attn_combine": (ctypes.c_int, [_P(eta_shape), _vp, _P(eta_params), _vp, _vp, _vp,
                                                ctypes.c_size_t, _vp]),
+    "eta_prefill_predict_tau": (ctypes.c_int, [_P(eta_prefill_shape), _vp, _vp, _vp, _vp, _vp]),
+    "eta_prefill_attn": (ctypes.c_int, [_P(eta_prefill_shape), _vp, _vp, _vp, _vp,
+                                        _P(eta_params), _vp, _vp, _vp, _vp]),
 }
 
 
@@ -432,3 +440,55 @@ def eta_decode_attn_combine(K: torch.Tensor, T: int, adm_cnt: torch.Tensor, para
            lib().eta_decode_attn_combine(ctypes.byref(s), adm_cnt.data_ptr(),
                                          ctypes.byref(params), out.data_ptr(), _ptr(lse),
                                          ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------
+# Training-time (prefill) forward
+# ------------------------------------------------------------------------------------
+def prefill_shape(Q: torch.Tensor, K: torch.Tensor) -> eta_prefill_shape:
+    """Q [B,H,T_q,d] and K [B,H_kv,T_k,d] (bfloat16) -> the C shape descriptor."""
+    if Q.dim() != 4 or K.dim() != 4:
+        raise ValueError("Q must be [B,H,T_q,d] and K [B,H_kv,T_k,d]")
+    B, H, T_q, d = Q.shape
+    B2, H_kv, T_k, d2 = K.shape
+    if B2 != B or d2 != d:
+        raise ValueError("Q and K disagree on B or d")
+    return eta_prefill_shape(int(B), int(H), int(H_kv if H_kv != H else 0), int(d), int(T_q),
+                             int(T_k))
+
+
+def eta_prefill_predict_tau(Q: torch.Tensor, W, bias: torch.Tensor, tau: torch.Tensor,
+                            stream=None):
+    """Eq. 1 per query token from bf16 Q [B,H,T,d] -> tau float32 [B,H,T]."""
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B,H,T,d]")
+    B, H, T, d = Q.shape
+    _need(Q, "Q", torch.bfloat16)
+    if W is not None:
+        _need(W, "W", torch.float32, (H * d, H))
+    _need(bias, "bias", torch.float32, (H,))
+    _need(tau, "tau", torch.float32, (B, H, T))
+    s = eta_prefill_shape(B, H, 0, d, T, T)
+    _check("eta_prefill_predict_tau",
+           lib().eta_prefill_predict_tau(ctypes.byref(s), Q.data_ptr(), _ptr(W), bias.data_ptr(),
+                                         tau.data_ptr(), _stream(stream)))
+
+
+def eta_prefill_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tau: torch.Tensor,
+                     params: eta_params, out: torch.Tensor, lse=None, gate_sum=None,
+                     stream=None):
+    """Dense causal gated attention: the T_q queries are the last T_q of the T_k keys."""
+    s = prefill_shape(Q, K)
+    _need(Q, "Q", torch.bfloat16)
+    _need(K, "K", torch.bfloat16)
+    _need(V, "V", torch.bfloat16, tuple(K.shape))
+    _need(tau, "tau", torch.float32, (s.B, s.H, s.T_q))
+    _need(out, "out", torch.float32, (s.B, s.H, s.T_q, s.d))
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (s.B, s.H, s.T_q))
+    if gate_sum is not None:
+        _need(gate_sum, "gate_sum", torch.float32, (s.B, s.H, s.T_q))
+    _check("eta_prefill_attn",
+           lib().eta_prefill_attn(ctypes.byref(s), Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                  tau.data_ptr(), ctypes.byref(params), out.data_ptr(), _ptr(lse),
+                                  _ptr(gate_sum), _stream(stream)))

@@ -119,6 +119,26 @@ eta_status check_attn(const eta_shape *s, const eta_params *p, const int32_t *ad
     return ETA_OK;
 }
 
+eta_status check_prefill(const eta_prefill_shape *s, eta::PrefillGeometry *g) {
+    if (s == nullptr) return ETA_ERR_INVALID_ARG;
+    if (s->B < 1 || s->H < 1 || s->T_q < 0 || s->T_k < s->T_q || s->H_kv < 0)
+        return ETA_ERR_INVALID_ARG;
+    if (s->d != 64 && s->d != 128) return ETA_ERR_UNSUPPORTED;
+    if ((long long)s->B * s->H > (1ll << 24)) return ETA_ERR_INVALID_ARG;
+    if ((long long)s->T_q > 65535ll * 128) return ETA_ERR_INVALID_ARG;  // query blocks on grid y
+    const int hkv = s->H_kv > 0 ? s->H_kv : s->H;
+    if (s->H % hkv != 0) return ETA_ERR_INVALID_ARG;
+    const int G = s->H / hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return ETA_ERR_UNSUPPORTED;
+    g->B = s->B;
+    g->H = s->H;
+    g->Hkv = hkv;
+    g->d = s->d;
+    g->T_q = s->T_q;
+    g->T_k = s->T_k;
+    return ETA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,6 +286,31 @@ eta_status eta_decode_attn(const eta_shape *s, const float *q, const void *K, co
                                             ws_bytes, stream);
     if (st != ETA_OK) return st;
     return eta_decode_attn_combine(s, adm_cnt, p, out, lse, ws, ws_bytes, stream);
+}
+
+eta_status eta_prefill_predict_tau(const eta_prefill_shape *s, const void *Q, const float *W,
+                                   const float *bias, float *tau, hipStream_t stream) {
+    eta::PrefillGeometry g;
+    eta_status st = check_prefill(s, &g);
+    if (st != ETA_OK) return st;
+    if (Q == nullptr || bias == nullptr || tau == nullptr || !aligned(Q, 16))
+        return ETA_ERR_INVALID_ARG;
+    return from_hip(eta::launch_prefill_tau(g, Q, W, bias, tau, stream));
+}
+
+eta_status eta_prefill_attn(const eta_prefill_shape *s, const void *Q, const void *K,
+                            const void *V, const float *tau, const eta_params *p, float *out,
+                            float *lse, float *gate_sum, hipStream_t stream) {
+    eta::PrefillGeometry g;
+    eta_status st = check_prefill(s, &g);
+    if (st != ETA_OK) return st;
+    if ((st = check_params(p)) != ETA_OK) return st;
+    if (Q == nullptr || K == nullptr || V == nullptr || tau == nullptr || out == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
+        return ETA_ERR_INVALID_ARG;
+    return from_hip(eta::launch_prefill_attn(g, Q, K, V, tau, p->gate_beta, p->gate_hard != 0,
+                                             out, lse, gate_sum, stream));
 }
 
 }  // extern "C"

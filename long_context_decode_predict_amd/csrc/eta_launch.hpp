@@ -62,4 +62,18 @@ hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K,
 hipError_t launch_attn_combine(const Geometry &g, const int32_t *adm_cnt, int split_blocks,
                                int max_chunks, float *out, float *lse, void *ws, hipStream_t st);
 
+// Prefill (training-time forward): Q [B][H][T_q][d], K, V [B][Hkv][T_k][d] bf16.
+struct PrefillGeometry {
+    int B, H, Hkv, d, T_q, T_k;
+};
+
+// Eq. 1 per query token: tau [B][H][T_q] from the bf16 queries.
+hipError_t launch_prefill_tau(const PrefillGeometry &g, const void *Q, const float *W,
+                              const float *bias, float *tau, hipStream_t st);
+
+// Dense causal gated attention (out [B][H][T_q][d], lse and gate_sum [B][H][T_q]).
+hipError_t launch_prefill_attn(const PrefillGeometry &g, const void *Q, const void *K,
+                               const void *V, const float *tau, float gate_beta, bool gate_hard,
+                               float *out, float *lse, float *gate_sum, hipStream_t st);
+
 }  // namespace eta

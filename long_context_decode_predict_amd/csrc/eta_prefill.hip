@@ -1,0 +1,389 @@
+// eta_prefill.hip -- the training-time (prefill) forward of the ETA gate: dense
+// causal attention over whole sequences with every logit S = s * q.k multiplied
+// by sigmoid(beta * (S - tau_t)), tau_t the threshold of query token t
+// (evolve.pub review, "Methodology Assessment": Eq. 1 per token, Eq. 2 gate,
+// Eq. 3 multiplicative gating; arXiv:2609.20888 abstract: sub-threshold logits
+// are suppressed toward zero during training rather than deleted).
+//
+// Unlike the decode step this is a dense contraction, so both products run on
+// the CDNA4 matrix cores (32x32x16 MFMA):
+//   S^T = K . Q^T  bf16 x bf16 -> fp32   (M = keys, N = queries, K = head dim)
+//   O^T += V^T . P^T  fp16 x fp16 -> fp32 (M = head dim, N = queries, K = keys)
+// Computing the transposes keeps one query per lane: in the MFMA result layout
+// lane l holds query l % 32 and 32 of the tile's 64 keys, its partner lane
+// l ^ 32 the other 32, so the row softmax needs one cross-lane exchange per
+// tile. The 32 gated weights of a lane are, register for register, the B
+// operand of the P.V product (the product's reduction runs over keys in any
+// fixed order, and both operands use the same key order), so P never leaves
+// the registers. V is staged into LDS transposed and converted to fp16 (exact
+// for |v| in [2^-14, 65504]); P in fp16 keeps 11 significant bits.
+//
+// Workgroup = 4 waves = 128 consecutive queries of one (row, head); wave w owns
+// queries 32w .. 32w + 31. Key tiles of 64 are staged into LDS (K row-major,
+// V^T), the next tile's global loads are in flight while the current one is
+// computed. Causal: query i sits at position T_k - T_q + i and sees keys at or
+// before it. Grid x = (row, head), y = query block, heaviest blocks first; all
+// query blocks of one head share an XCD when B * H is a multiple of 8.
+#include "eta_device.hpp"
+#include "eta_launch.hpp"
+
+namespace eta {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPfWaves = 4;
+constexpr int kPfQ = 32 * kPfWaves;  // queries per workgroup
+constexpr int kPfKeys = 64;          // keys per tile
+
+template <int D>
+struct PfShared {
+    static constexpr int KS = D + 8;        // bf16 per K row (16 bytes of padding)
+    static constexpr int VS = kPfKeys + 4;  // fp16 per V^T row (8 bytes of padding)
+    alignas(16) uint16_t k[kPfKeys * KS];
+    alignas(16) uint16_t vt[D * VS];
+};
+
+struct PfArgs {
+    int H, Hkv, G, T_q, T_k, q_off;
+    float s, L2E, nbl2e;  // 1/sqrt(d), log2(e), -beta*log2(e)
+    const uint16_t *Q;
+    const uint16_t *K;
+    const uint16_t *V;
+    const float *tau;
+    float *out;
+    float *lse;
+    float *gate_sum;
+};
+
+__device__ __forceinline__ uint16_t f16_bits_of_bf16(uint16_t x) {
+    const _Float16 h = (_Float16)__uint_as_float((uint32_t)x << 16);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Staging of one key tile: K rows as they are, V transposed to [d][key] in fp16.
+// KPT keys x 8 dimensions of V per thread (D / 32 keys: 4 for d = 128, 2 for 64).
+template <int D>
+struct Stage {
+    static constexpr int KCH = D / 8;                            // 16-byte chunks per row
+    static constexpr int KLD = kPfKeys * KCH / (kPfWaves * kWave);  // K chunks per thread
+    static constexpr int KPT = D / 32;                           // V keys per thread
+    uint4 kr[KLD];
+    uint4 vr[KPT];
+
+    __device__ __forceinline__ void load(const PfArgs &a, const uint16_t *Kh, const uint16_t *Vh,
+                                         int k0) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int c = tid + i * kPfWaves * kWave;
+            const int row = min(k0 + c / KCH, a.T_k - 1);  // rows past T_k: clamped, masked later
+            kr[i] = *reinterpret_cast<const uint4 *>(Kh + (size_t)row * D + (c % KCH) * 8);
+        }
+        const int ka = tid / KCH;  // key group
+        const int db = tid % KCH;  // 8-dimension chunk
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int row = min(k0 + ka * KPT + r, a.T_k - 1);
+            vr[r] = *reinterpret_cast<const uint4 *>(Vh + (size_t)row * D + db * 8);
+        }
+    }
+
+    __device__ __forceinline__ void store(PfShared<D> &sm) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int c = tid + i * kPfWaves * kWave;
+            *reinterpret_cast<uint4 *>(&sm.k[(c / KCH) * PfShared<D>::KS + (c % KCH) * 8]) = kr[i];
+        }
+        const int ka = tid / KCH;
+        const int db = tid % KCH;
+        uint16_t v[KPT][8];
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const uint32_t w[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[r][2 * e] = f16_bits_of_bf16((uint16_t)(w[e] & 0xffffu));
+                v[r][2 * e + 1] = f16_bits_of_bf16((uint16_t)(w[e] >> 16));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            uint16_t *dst = &sm.vt[(db * 8 + i) * PfShared<D>::VS + ka * KPT];
+            if (KPT == 4) {
+                const uint2 p = make_uint2((uint32_t)v[0][i] | ((uint32_t)v[1][i] << 16),
+                                           (uint32_t)v[2][i] | ((uint32_t)v[3][i] << 16));
+                *reinterpret_cast<uint2 *>(dst) = p;
+            } else {
+                *reinterpret_cast<uint32_t *>(dst) = (uint32_t)v[0][i] | ((uint32_t)v[1][i] << 16);
+            }
+        }
+    }
+};
+
+template <int D, bool HARD>
+__global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs a) {
+    __shared__ PfShared<D> sm;
+    constexpr int KS = PfShared<D>::KS;
+    constexpr int VS = PfShared<D>::VS;
+    constexpr int NKS = D / 16;  // k-steps of the S product
+    constexpr int NMD = D / 32;  // head-dimension tiles of the O product
+
+    const int bh = blockIdx.x;  // b * H + h
+    const int nqb = gridDim.y;
+    const int qb = nqb - 1 - (int)blockIdx.y;  // heaviest (latest) query blocks first
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    const int hk = h / a.G;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int hl = lane >> 5;   // lane half: which 8 of a 16-wide reduction step
+    const int col = lane & 31;  // query within the wave's 32
+
+    const int q0 = qb * kPfQ;
+    const int qi = q0 + wave * 32 + col;       // this lane's query index
+    const int qc = min(qi, a.T_q - 1);         // clamped for loads
+    const int qpos = a.q_off + qi;             // its position among the keys
+    const uint16_t *Qh = a.Q + ((size_t)bh * a.T_q) * D;
+    const uint16_t *Kh = a.K + ((size_t)(b * a.Hkv + hk) * a.T_k) * D;
+    const uint16_t *Vh = a.V + ((size_t)(b * a.Hkv + hk) * a.T_k) * D;
+
+    // Q^T as the B operand of S^T = K Q^T, one 8-element slice per k-step
+    bf16x8 qB[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(Qh + (size_t)qc * D + ks * 16 + hl * 8);
+        qB[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+    const float t = a.tau[(size_t)bh * a.T_q + qc];
+    const float nbt = -a.nbl2e * t;  // gate exponent = nbl2e * S + nbt
+
+    // keys this workgroup needs: up to the position of its last query
+    const int q_last = min(q0 + kPfQ, a.T_q) - 1;
+    const int k_end = min(a.T_k, a.q_off + q_last + 1);
+    const int ntiles = (k_end + kPfKeys - 1) / kPfKeys;
+    const int wave_first_pos = a.q_off + q0 + wave * 32;  // smallest query position of the wave
+
+    f32x16 o[NMD];
+#pragma unroll
+    for (int m = 0; m < NMD; ++m) o[m] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f, g_sum = 0.f;
+
+    Stage<D> st;
+    if (ntiles > 0) st.load(a, Kh, Vh, 0);
+    for (int tt = 0; tt < ntiles; ++tt) {
+        const int k0 = tt * kPfKeys;
+        if (tt > 0) __syncthreads();  // every wave is done with the previous tile
+        st.store(sm);
+        __syncthreads();
+        if (tt + 1 < ntiles) st.load(a, Kh, Vh, k0 + kPfKeys);
+
+        // S^T for keys k0 .. k0 + 63 (two 32-key tiles) against the wave's 32 queries
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const uint4 raw = *reinterpret_cast<const uint4 *>(
+                    &sm.k[(mt * 32 + col) * KS + ks * 16 + hl * 8]);
+                s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
+                                                                qB[ks], s[mt], 0, 0, 0);
+            }
+        }
+
+        // gate, causal mask, tile maximum
+        const bool masked_tile = k0 + kPfKeys - 1 > wave_first_pos || k0 + kPfKeys > a.T_k;
+        float g[2][16];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float S = s[mt][j] * a.s;
+                float gv, gate;
+                if (HARD) {
+                    gate = S >= t ? 1.f : 0.f;
+                    gv = S >= t ? S : 0.f;
+                } else {
+                    gate = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(a.nbl2e, S, nbt)));
+                    gv = S * gate;
+                }
+                if (masked_tile) {
+                    const int key = k0 + mt * 32 + (j >> 2) * 8 + hl * 4 + (j & 3);
+                    if (key > qpos) {
+                        gv = -INFINITY;
+                        gate = 0.f;
+                    }
+                }
+                g_sum += gate;
+                g[mt][j] = gv;
+                mx = fmaxf(mx, gv);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the partner lane holds the other 32 keys
+        const float m_new = fmaxf(m_run, mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // nothing visible yet: weights 0
+        const float corr = __builtin_amdgcn_exp2f((m_run - m_ref) * a.L2E);
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int m = 0; m < NMD; ++m) o[m] *= corr;
+
+        // weights, packed as the fp16 B operand of O^T += V^T P^T: k-step s (keys
+        // 16s .. 16s + 15) takes registers 8(s%2) .. 8(s%2) + 7 of key tile s/2
+        const float mref_l = m_ref * a.L2E;
+        f16x8 pB[4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(g[mt][j], a.L2E, -mref_l));
+                l_run += p;
+                pB[mt * 2 + j / 8][j % 8] = (_Float16)p;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int m = 0; m < NMD; ++m) {
+                const uint16_t *src = &sm.vt[(m * 32 + col) * VS + ks * 16 + hl * 4];
+                const uint2 lo = *reinterpret_cast<const uint2 *>(src);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(src + 8);
+                const uint4 raw = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                o[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, raw),
+                                                              pB[ks], o[m], 0, 0, 0);
+            }
+        }
+    }
+
+    // the two halves of a query's keys meet
+    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    const float gs_tot = g_sum + __shfl_xor(g_sum, 32, kWave);
+    if (qi < a.T_q) {
+        const size_t uq = (size_t)bh * a.T_q + qi;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float *orow = a.out + uq * D;
+#pragma unroll
+        for (int m = 0; m < NMD; ++m) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d0 = m * 32 + gq * 8 + hl * 4;
+                *reinterpret_cast<float4 *>(orow + d0) =
+                    make_float4(o[m][4 * gq] * inv, o[m][4 * gq + 1] * inv, o[m][4 * gq + 2] * inv,
+                                o[m][4 * gq + 3] * inv);
+            }
+        }
+        if (hl == 0) {
+            if (a.lse) a.lse[uq] = l_tot > 0.f ? m_run + __logf(l_tot) : -INFINITY;
+            if (a.gate_sum) a.gate_sum[uq] = gs_tot;
+        }
+    }
+}
+
+// Eq. 1 for every query token of a prefill: tau[b, h, t] = bias[h] + sum over the
+// token's queries of all heads g and dimensions i of Q[b, g, t, i] * W[g*d + i, h].
+// Workgroup = 64 tokens x 4 head slices; each thread accumulates up to four heads
+// of its token in a fixed order.
+constexpr int kTauTokens = 64;
+
+template <int D>
+__global__ __launch_bounds__(4 * kWave) void prefill_tau_kernel(const uint16_t *__restrict__ Q,
+                                                                const float *__restrict__ W,
+                                                                const float *__restrict__ bias,
+                                                                float *__restrict__ tau, int H,
+                                                                int T) {
+    const int b = blockIdx.y;
+    const int tok = blockIdx.x * kTauTokens + (threadIdx.x & (kWave - 1));
+    const int slice = threadIdx.x / kWave;
+    const int tc = min(tok, T - 1);
+    for (int h0 = 0; h0 < H; h0 += 16) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        int hs[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) hs[k] = h0 + slice + 4 * k;
+        if (W != nullptr) {
+            for (int g = 0; g < H; ++g) {
+                const uint16_t *qrow = Q + (((size_t)b * H + g) * T + tc) * D;
+                for (int i0 = 0; i0 < D; i0 += 8) {
+                    const uint4 raw = *reinterpret_cast<const uint4 *>(qrow + i0);
+                    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float qv = (e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1]);
+                        const float *wr = W + (size_t)(g * D + i0 + e) * H;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            if (hs[k] < H) acc[k] = fmaf(qv, wr[hs[k]], acc[k]);
+                    }
+                }
+            }
+        }
+        if (tok < T) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (hs[k] < H) tau[((size_t)b * H + hs[k]) * T + tok] = bias[hs[k]] + acc[k];
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_prefill_t(const PrefillGeometry &g, const void *Q, const void *K, const void *V,
+                            const float *tau, float gate_beta, bool hard, float *out, float *lse,
+                            float *gate_sum, hipStream_t st) {
+    PfArgs a;
+    a.H = g.H;
+    a.Hkv = g.Hkv;
+    a.G = g.H / g.Hkv;
+    a.T_q = g.T_q;
+    a.T_k = g.T_k;
+    a.q_off = g.T_k - g.T_q;
+    a.s = 1.0f / sqrtf((float)D);
+    a.L2E = kLog2e;
+    a.nbl2e = -gate_beta * kLog2e;
+    a.Q = static_cast<const uint16_t *>(Q);
+    a.K = static_cast<const uint16_t *>(K);
+    a.V = static_cast<const uint16_t *>(V);
+    a.tau = tau;
+    a.out = out;
+    a.lse = lse;
+    a.gate_sum = gate_sum;
+    const dim3 grid((unsigned)(g.B * g.H), (unsigned)((g.T_q + kPfQ - 1) / kPfQ));
+    if (hard) {
+        hipLaunchKernelGGL((prefill_attn_kernel<D, true>), grid, dim3(kPfWaves * kWave), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((prefill_attn_kernel<D, false>), grid, dim3(kPfWaves * kWave), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_tau(const PrefillGeometry &g, const void *Q, const float *W,
+                              const float *bias, float *tau, hipStream_t st) {
+    if (g.T_q == 0) return hipSuccess;
+    const dim3 grid((unsigned)((g.T_q + kTauTokens - 1) / kTauTokens), (unsigned)g.B);
+    if (g.d == 128) {
+        hipLaunchKernelGGL((prefill_tau_kernel<128>), grid, dim3(4 * kWave), 0, st,
+                           static_cast<const uint16_t *>(Q), W, bias, tau, g.H, g.T_q);
+    } else {
+        hipLaunchKernelGGL((prefill_tau_kernel<64>), grid, dim3(4 * kWave), 0, st,
+                           static_cast<const uint16_t *>(Q), W, bias, tau, g.H, g.T_q);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const PrefillGeometry &g, const void *Q, const void *K,
+                               const void *V, const float *tau, float gate_beta, bool gate_hard,
+                               float *out, float *lse, float *gate_sum, hipStream_t st) {
+    if (g.T_q == 0) return hipSuccess;
+    return g.d == 128 ? launch_prefill_t<128>(g, Q, K, V, tau, gate_beta, gate_hard, out, lse,
+                                              gate_sum, st)
+                      : launch_prefill_t<64>(g, Q, K, V, tau, gate_beta, gate_hard, out, lse,
+                                             gate_sum, st);
+}
+
+}  // namespace eta

@@ -262,3 +262,63 @@ def gather_unit(pool: torch.Tensor, table: torch.Tensor, b: int, k: int, T_b: in
         return pool.new_empty((0, pool.shape[-1]))
     pages = table[b, :nb].to(pool.device, torch.long)
     return pool[pages, k].reshape(nb * BLOCK, pool.shape[-1])[:T_b]
+
+
+@dataclass(frozen=True)
+class PrefillWorkload:
+    """A training-time (prefill) forward: T_q queries at the end of T_k keys."""
+    name: str
+    B: int
+    H: int
+    d: int
+    T_q: int
+    T_k: int
+    H_kv: int = 0
+    sigma: float = 0.3           # in-block key spread, as for the decode caches
+    inclusion: float = 0.15      # target mean gate (about 85 % training sparsity)
+    seed: int = SEED_BASE + 100
+    note: str = field(default="", compare=False)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv if self.H_kv else self.H
+
+    @property
+    def G(self) -> int:
+        return self.H // self.kv_heads
+
+
+PREFILL_WORKLOADS = {
+    "prefill_b4_h16_d128_t8k_bf16": PrefillWorkload(
+        "prefill_b4_h16_d128_t8k_bf16", B=4, H=16, d=128, T_q=8192, T_k=8192,
+        seed=SEED_BASE + 101, note="training-time forward of 8K sequences"),
+    "prefill_b1_h32kv8_d128_t32k_bf16": PrefillWorkload(
+        "prefill_b1_h32kv8_d128_t32k_bf16", B=1, H=32, d=128, T_q=32768, T_k=32768, H_kv=8,
+        seed=SEED_BASE + 102, note="long prefill with grouped heads"),
+}
+
+
+def generate_prefill(w: PrefillWorkload, device="cuda", tau_mu: float = 0.5,
+                     tau_sigma: float = 0.5) -> dict:
+    """Q [B,H,T_q,d], K, V [B,H_kv,T_k,d] bfloat16 (keys clustered per 64-token block
+    as in the decode caches), W [H*d,H] block-diagonal N(0, 1/d), and a seeded
+    per-token threshold tau ~ N(tau_mu, tau_sigma^2) [B,H,T_q] float32 that both the
+    kernels and the oracle take as an input."""
+    g = _gen(device, w.seed)
+    B, H, Hk, d = w.B, w.H, w.kv_heads, w.d
+    nblk = (w.T_k + BLOCK - 1) // BLOCK
+    Q = torch.randn((B, H, w.T_q, d), generator=g, device=device).to(torch.bfloat16)
+    K = torch.empty((B, Hk, w.T_k, d), dtype=torch.bfloat16, device=device)
+    V = torch.empty((B, Hk, w.T_k, d), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        cen = torch.randn((Hk, nblk, 1, d), generator=g, device=device)
+        noise = torch.randn((Hk, nblk, BLOCK, d), generator=g, device=device)
+        K[b].copy_((noise * w.sigma + cen).view(Hk, nblk * BLOCK, d)[:, :w.T_k])
+        V[b].copy_(torch.randn((Hk, w.T_k, d), generator=g, device=device))
+        del cen, noise
+    W = torch.zeros((H * d, H), dtype=torch.float32, device=device)
+    wdiag = torch.randn((H, d), generator=g, device=device) / math.sqrt(d)
+    for h in range(H):
+        W[h * d:(h + 1) * d, h] = wdiag[h]
+    tau = tau_mu + tau_sigma * torch.randn((B, H, w.T_q), generator=g, device=device)
+    return {"Q": Q, "K": K, "V": V, "W": W, "tau": tau.float()}

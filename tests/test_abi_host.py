@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
@@ -240,3 +240,37 @@ def test_page_pool_round_trip():
     assert torch.isnan(Kp[tbl[2, 1], :, 1:]).all()  # past row 2's length in its last page
     lens_w = wl.row_lengths(wl.WORKLOADS["paged_b64_h16_d128_t128k_bf16"])
     assert max(lens_w) == 131072 and min(lens_w) >= 65536 and len(lens_w) == 64
+
+
+def pshape(**kw):
+    s = dict(B=2, H=4, H_kv=0, d=128, T_q=100, T_k=300)
+    s.update(kw)
+    return _lib.eta_prefill_shape(**s)
+
+
+@pytest.mark.parametrize("kw,st", [
+    (dict(d=96), UNS), (dict(B=0), INV), (dict(H=0), INV), (dict(T_q=-1), INV),
+    (dict(T_q=400), INV), (dict(H_kv=3), INV), (dict(H=16, H_kv=1), UNS), (dict(H_kv=-2), INV),
+    (dict(T_q=65535 * 128 + 1, T_k=65535 * 128 + 1), INV),
+])
+def test_prefill_shape_errors(L, kw, st):
+    p = BY(params())
+    assert L.eta_prefill_attn(BY(pshape(**kw)), FAKE, FAKE, FAKE, FAKE, p, FAKE, None, None,
+                              None) == st
+    assert L.eta_prefill_predict_tau(BY(pshape(**kw)), FAKE, FAKE, FAKE, FAKE, None) == st
+
+
+def test_prefill_pointer_errors(L):
+    s, p = BY(pshape()), BY(params())
+    call = lambda **kw: L.eta_prefill_attn(s, kw.get("Q", FAKE), kw.get("K", FAKE),
+                                           kw.get("V", FAKE), kw.get("tau", FAKE),
+                                           kw.get("p", p), kw.get("out", FAKE), None, None, None)
+    for k in ("Q", "K", "V", "tau", "out", "p"):
+        assert call(**{k: None}) == INV, k
+    for k in ("Q", "K", "V", "out"):
+        assert call(**{k: FAKE + 8}) == INV, k  # 16-byte alignment
+    assert call(p=BY(params(gate_beta=0.0))) == INV
+    assert L.eta_prefill_predict_tau(s, None, FAKE, FAKE, FAKE, None) == INV
+    assert L.eta_prefill_predict_tau(s, FAKE, FAKE, None, FAKE, None) == INV
+    assert L.eta_prefill_predict_tau(s, FAKE, FAKE, FAKE, None, None) == INV
+    assert L.eta_prefill_predict_tau(s, FAKE + 4, FAKE, FAKE, FAKE, None) == INV
