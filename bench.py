@@ -283,6 +283,135 @@ def density_sweep(step, data, w, meta, W, params, lens, steps, fused):
     return out
 
 
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix peak of the MI355X
+
+
+def prefill_flops(w) -> int:
+    """Algorithmic flops of the causal gated forward: 2 (q.k) + 2 (p.v) per visible
+    (query, key) pair and head dimension; masked halves of diagonal tiles excluded."""
+    vis = w.T_q * (w.T_k - w.T_q) + w.T_q * (w.T_q + 1) // 2
+    return 4 * w.d * vis * w.B * w.H
+
+
+def bench_prefill(args, w):
+    """The training-time forward: eta_prefill_predict_tau + eta_prefill_attn per step."""
+    from statistics import NormalDist
+
+    params = _lib.default_params()
+    log(f"[bench] generating {w.name}: B={w.B} H={w.H}/{w.kv_heads} d={w.d} "
+        f"T_q={w.T_q} T_k={w.T_k}")
+    data = workloads.generate_prefill(w)
+    # bias for about the target mean inclusion: S - tau ~ N(-bias, 1 + sigma^2 + 1) under
+    # the generator (query-key score plus the predictor's own N(0, 1) term)
+    bias_v = NormalDist().inv_cdf(1.0 - w.inclusion) * math.sqrt(2.0 + w.sigma ** 2)
+    bias = torch.full((w.H,), bias_v, dtype=torch.float32, device="cuda")
+    B, H, T_q, d = data["Q"].shape
+    tau = torch.empty((B, H, T_q), device="cuda")
+    out = torch.empty((B, H, T_q, d), device="cuda")
+    lse = torch.empty((B, H, T_q), device="cuda")
+    gs = torch.empty((B, H, T_q), device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        _lib.eta_prefill_predict_tau(data["Q"], data["W"], bias, tau)
+        if evs is not None:
+            evs[1].record(stream)
+        _lib.eta_prefill_attn(data["Q"], data["K"], data["V"], tau, params, out, lse, gs)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    tau_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    flops = prefill_flops(w)
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    vis = (w.T_q * (w.T_k - w.T_q) + w.T_q * (w.T_q + 1) // 2) * B * H
+    inclusion = float(gs.double().sum().item()) / vis
+    log(f"[bench] {ms:.3f} ms/step: attention {attn_ms:.3f} ms ({tflops:.0f} TFLOP/s), "
+        f"predictor {tau_ms:.3f} ms, mean inclusion {inclusion:.3f}")
+    # the same forward at tau = -inf (plain causal attention on the same kernel)
+    ninf = torch.full_like(tau, -math.inf)
+    e0.record(stream)
+    for _ in range(max(3, args.steps // 2)):
+        _lib.eta_prefill_attn(data["Q"], data["K"], data["V"], ninf, params, out, lse, gs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / max(3, args.steps // 2)
+    tokens = w.B * w.T_q
+    result = {
+        "metric": "ETA training-time (prefill) gated forward, query tokens/s",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (q.k), fp16 (p.v), f32 accumulate",
+        "data": "synthetic (seeded clustered keys; see DESIGN.md)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
+                   "T_q": w.T_q, "T_k": w.T_k, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel", "achieved": tflops,
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_ms": attn_ms},
+        "cpu_baseline": None,
+        "extra": {"predict_tau_ms": tau_ms, "attn_ms": attn_ms, "mean_gate_inclusion": inclusion,
+                  "dense_tau_neg_inf_attn_ms": dense_ms,
+                  "dense_tflops": flops / (dense_ms * 1e-3) / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, data, tau, params, ms)
+    print(json.dumps(result), flush=True)
+
+
+def prefill_cpu_baseline(w, data, tau, params, step_ms, n_queries=256):
+    """The oracle's forward for a seeded sample of query tokens (each with its whole
+    causal window, the last tokens of a sequence: the most expensive), timed on the
+    host cores and scaled by visible pairs to the whole workload."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as oracle_mod
+
+    O = oracle_mod.default()
+    rng = np.random.default_rng(w.seed + 9)
+    heads = rng.choice(w.B * w.H, size=min(16, w.B * w.H), replace=False)
+    per = max(1, n_queries // len(heads))
+
+    def host(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    jobs = []
+    for u in heads:
+        b, h = divmod(int(u), w.H)
+        hk = h // w.G
+        Qb = host(data["Q"][b, h, w.T_q - per:])
+        jobs.append((Qb, host(data["K"][b, hk]), host(data["V"][b, hk]),
+                     tau[b, h, w.T_q - per:].double().cpu().numpy()))
+    threads = min(16, os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda j: O.prefill(j[0], j[1], j[2], w.T_k, j[3], beta=params.gate_beta,
+                                        hard=bool(params.gate_hard)), jobs))
+    dt = time.perf_counter() - t0
+    # the sample's queries are the last `per` of T_k visible keys each
+    sample_pairs = len(heads) * sum(w.T_k - per + 1 + i for i in range(per))
+    total_pairs = (w.T_q * (w.T_k - w.T_q) + w.T_q * (w.T_q + 1) // 2) * w.B * w.H
+    step_s = dt * total_pairs / sample_pairs
+    return {"value": w.B * w.T_q / step_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{per} query tokens x {len(heads)} heads (their full causal windows), "
+                      f"{dt:.2f} s wall on {threads} threads, scaled by visible (query, key) pairs",
+            "gpu_over_cpu": step_s / (step_ms * 1e-3)}
+
+
 def copy_probe(gib: float, reps: int):
     """Time torch's device-to-device copy of `gib` GiB (read + write bytes counted)."""
     n = int(gib * (1 << 30)) // 4
@@ -308,7 +437,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=workloads.HEADLINE, choices=list(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=workloads.HEADLINE,
+                    choices=list(workloads.WORKLOADS) + list(workloads.PREFILL_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
@@ -331,6 +461,9 @@ def main():
         return
     ensure_built()
     torch.cuda.set_device(0)
+    if args.workload in workloads.PREFILL_WORKLOADS:
+        bench_prefill(args, workloads.PREFILL_WORKLOADS[args.workload])
+        return
     w = workloads.WORKLOADS[args.workload]
     params = _lib.default_params(split_blocks=args.split)
 
