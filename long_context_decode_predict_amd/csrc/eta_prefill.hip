@@ -73,54 +73,59 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 // KPT keys x 8 dimensions of V per thread (D / 32 keys: 4 for d = 128, 2 for 64);
 // each fp16 pair written to LDS holds two consecutive keys of one dimension.
 template <int D>
-struct Stage {
+struct StageShape {
     static constexpr int KCH = D / 8;                               // 16-byte chunks per row
     static constexpr int KLD = kPfKeys * KCH / (kPfWaves * kWave);  // K chunks per thread
     static constexpr int KPT = D / 32;                              // V keys per thread
-    uint4 kr[KLD];
-    uint4 vr[KPT];
-
-    __device__ __forceinline__ void load(const PfArgs &a, const uint16_t *Kh, const uint16_t *Vh,
-                                         int k0) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int c = tid + i * kPfWaves * kWave;
-            const int row = min(k0 + c / KCH, a.T_k - 1);  // rows past T_k: clamped, masked later
-            kr[i] = *reinterpret_cast<const uint4 *>(Kh + (size_t)row * D + (c % KCH) * 8);
-        }
-        const int ka = tid / KCH;  // key group
-        const int db = tid % KCH;  // 8-dimension chunk
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            const int row = min(k0 + ka * KPT + r, a.T_k - 1);
-            vr[r] = *reinterpret_cast<const uint4 *>(Vh + (size_t)row * D + db * 8);
-        }
-    }
-
-    __device__ __forceinline__ void store(PfShared<D> &sm, int buf) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int c = tid + i * kPfWaves * kWave;
-            *reinterpret_cast<uint4 *>(&sm.k[buf][(c / KCH) * PfShared<D>::KS + (c % KCH) * 8]) =
-                kr[i];
-        }
-        const int ka = tid / KCH;
-        const int db = tid % KCH;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            uint16_t *dst = &sm.vt[buf][(db * 8 + i) * PfShared<D>::VS + ka * KPT];
-            const uint32_t p01 = pack_f16(bf16_elem(vr[0], i), bf16_elem(vr[1], i));
-            if (KPT == 4) {
-                const uint32_t p23 = pack_f16(bf16_elem(vr[2], i), bf16_elem(vr[3], i));
-                *reinterpret_cast<uint2 *>(dst) = make_uint2(p01, p23);
-            } else {
-                *reinterpret_cast<uint32_t *>(dst) = p01;
-            }
-        }
-    }
 };
+
+template <int D>
+__device__ __forceinline__ void stage_load(const PfArgs &a, const uint16_t *Kh, const uint16_t *Vh,
+                                           int k0, uint4 (&kr)[StageShape<D>::KLD],
+                                           uint4 (&vr)[StageShape<D>::KPT]) {
+    using S = StageShape<D>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < S::KLD; ++i) {
+        const int c = tid + i * kPfWaves * kWave;
+        const int row = min(k0 + c / S::KCH, a.T_k - 1);  // rows past T_k: clamped, masked later
+        kr[i] = *reinterpret_cast<const uint4 *>(Kh + (size_t)row * D + (c % S::KCH) * 8);
+    }
+    const int ka = tid / S::KCH;  // key group
+    const int db = tid % S::KCH;  // 8-dimension chunk
+#pragma unroll
+    for (int r = 0; r < S::KPT; ++r) {
+        const int row = min(k0 + ka * S::KPT + r, a.T_k - 1);
+        vr[r] = *reinterpret_cast<const uint4 *>(Vh + (size_t)row * D + db * 8);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_store(PfShared<D> &sm, int buf,
+                                            const uint4 (&kr)[StageShape<D>::KLD],
+                                            const uint4 (&vr)[StageShape<D>::KPT]) {
+    using S = StageShape<D>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < S::KLD; ++i) {
+        const int c = tid + i * kPfWaves * kWave;
+        *reinterpret_cast<uint4 *>(&sm.k[buf][(c / S::KCH) * PfShared<D>::KS + (c % S::KCH) * 8]) =
+            kr[i];
+    }
+    const int ka = tid / S::KCH;
+    const int db = tid % S::KCH;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint16_t *dst = &sm.vt[buf][(db * 8 + i) * PfShared<D>::VS + ka * S::KPT];
+        const uint32_t p01 = pack_f16(bf16_elem(vr[0], i), bf16_elem(vr[1], i));
+        if (S::KPT == 4) {
+            const uint32_t p23 = pack_f16(bf16_elem(vr[2], i), bf16_elem(vr[3], i));
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(p01, p23);
+        } else {
+            *reinterpret_cast<uint32_t *>(dst) = p01;
+        }
+    }
+}
 
 // Gate, mask and tile maximum of one lane's 32 scores (acc = q.k, unscaled).
 // Returns the gated values in acc units (the 1/sqrt(d) scale is folded into
@@ -209,14 +214,17 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
     for (int m = 0; m < NMD; ++m) o[m] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f, g_sum = 0.f;  // m_run in acc units
 
-    Stage<D> st;
-    st.load(a, Kh, Vh, 0);
-    st.store(sm, 0);
+    uint4 kr[StageShape<D>::KLD], vr[StageShape<D>::KPT];
+    stage_load<D>(a, Kh, Vh, 0, kr, vr);
+    stage_store<D>(sm, 0, kr, vr);
     __syncthreads();
     for (int tt = 0; tt < ntiles; ++tt) {
         const int k0 = tt * kPfKeys;
         const int buf = tt & 1;
-        if (tt + 1 < ntiles) st.load(a, Kh, Vh, k0 + kPfKeys);  // in flight during the tile
+        // the next tile's loads are in flight during this one (issued unconditionally:
+        // rows are clamped, so the load past the last tile stays in bounds and keeps
+        // the staging registers out of scratch memory)
+        stage_load<D>(a, Kh, Vh, k0 + kPfKeys, kr, vr);
 
         // S^T for keys k0 .. k0 + 63 (two 32-key tiles) against the wave's 32 queries
         f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -283,7 +291,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
         }
         // next tile into the other buffer: its last readers finished before the
         // barrier that ended the previous iteration
-        if (tt + 1 < ntiles) st.store(sm, buf ^ 1);
+        if (tt + 1 < ntiles) stage_store<D>(sm, buf ^ 1, kr, vr);
         __syncthreads();
     }
 
