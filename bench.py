@@ -31,6 +31,7 @@ from long_context_decode_predict_amd.decode import DecodeStep  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 ATTN_SOURCES = ("eta_attn.hip", "eta_device.hpp")
+PREFILL_SOURCES = ("eta_prefill.hip", "eta_device.hpp")
 METRIC = "ETA decode steps/s and effective KV GB/s (% HBM peak), B=64 T=128K ~38% density"
 
 
@@ -59,20 +60,20 @@ def admitted_bytes(w, cnt, idx, lens):
     return 2 * full * w.d * eb
 
 
-def attn_source_sha() -> str:
+def attn_source_sha(sources=ATTN_SOURCES) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "long_context_decode_predict_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def counter_traffic(workload: str):
-    """HBM bytes per launch of the attention kernel from the committed rocprofv3 counter
+def counter_traffic(workload: str, prefix: str = "attn_partial", sources=ATTN_SOURCES):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
     summary of this workload, or None if there is none or the kernel changed since."""
-    path = os.path.join(PROFILES, f"attn_partial_{workload}.md")
+    path = os.path.join(PROFILES, f"{prefix}_{workload}.md")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -82,7 +83,7 @@ def counter_traffic(workload: str):
                                                       "attn_source_sha256"):
                 k, v = line.split(":", 1)
                 vals[k] = v.strip()
-    if vals.get("attn_source_sha256") != attn_source_sha():
+    if vals.get("attn_source_sha256") != attn_source_sha(sources):
         return None
     try:
         return int(float(vals["traffic_bytes_per_launch"]))
@@ -361,7 +362,8 @@ def bench_prefill(args, w):
                    "T_q": w.T_q, "T_k": w.T_k, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel", "achieved": tflops,
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "frac": tflops / MFMA_PEAK_TFLOPS,
+                     "traffic": counter_traffic(w.name, "prefill_attn", PREFILL_SOURCES),
                      "algorithmic_flops_per_launch": flops, "avg_launch_ms": attn_ms},
         "cpu_baseline": None,
         "extra": {"predict_tau_ms": tau_ms, "attn_ms": attn_ms, "mean_gate_inclusion": inclusion,
