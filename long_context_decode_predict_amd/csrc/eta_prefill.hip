@@ -42,6 +42,10 @@ template <int D>
 struct PfShared {
     static constexpr int KS = D + 8;        // bf16 per K row (16 bytes of padding)
     static constexpr int VS = kPfKeys + 4;  // fp16 per V^T row (8 bytes of padding)
+    // V^T row r keeps key k at column k ^ swz(r): 16-key groups are permuted by the
+    // row's 32-dimension tile, so the transposing writes (8 bytes per lane, rows
+    // 8 apart across lanes) spread over the banks; a reading wave works on one
+    // 32-row tile at a time, so its reads are only shifted.
     alignas(16) uint16_t k[2][kPfKeys * KS];  // double buffered: one barrier per tile
     alignas(16) uint16_t vt[2][D * VS];
 };
@@ -78,6 +82,9 @@ struct StageShape {
     static constexpr int KLD = kPfKeys * KCH / (kPfWaves * kWave);  // K chunks per thread
     static constexpr int KPT = D / 32;                              // V keys per thread
 };
+
+// Key swizzle of V^T row r (see PfShared): flips the 16-key group by r / 32.
+__device__ __forceinline__ int vt_swz(int r) { return ((r >> 5) & 3) << 4; }
 
 template <int D>
 __device__ __forceinline__ void stage_load(const PfArgs &a, const uint16_t *Kh, const uint16_t *Vh,
@@ -116,7 +123,8 @@ __device__ __forceinline__ void stage_store(PfShared<D> &sm, int buf,
     const int db = tid % S::KCH;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        uint16_t *dst = &sm.vt[buf][(db * 8 + i) * PfShared<D>::VS + ka * S::KPT];
+        const int row = db * 8 + i;
+        uint16_t *dst = &sm.vt[buf][row * PfShared<D>::VS + ((ka * S::KPT) ^ vt_swz(row))];
         const uint32_t p01 = pack_f16(bf16_elem(vr[0], i), bf16_elem(vr[1], i));
         if (S::KPT == 4) {
             const uint32_t p23 = pack_f16(bf16_elem(vr[2], i), bf16_elem(vr[3], i));
@@ -282,7 +290,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
             const f16x8 pB = __builtin_bit_cast(f16x8, make_uint4(pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]));
 #pragma unroll
             for (int m = 0; m < NMD; ++m) {
-                const uint16_t *src = &sm.vt[buf][(m * 32 + col) * VS + ks * 16 + hl * 4];
+                const uint16_t *src = &sm.vt[buf][(m * 32 + col) * VS + ((ks ^ (m & 3)) * 16 + hl * 4)];
                 const uint2 lo = *reinterpret_cast<const uint2 *>(src);
                 const uint2 hi = *reinterpret_cast<const uint2 *>(src + 8);
                 o[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
