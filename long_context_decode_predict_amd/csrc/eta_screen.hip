@@ -202,6 +202,157 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
     if (threadIdx.x == 0) a.adm_cnt[u] = base;
 }
 
+// Grouped heads: one workgroup per key/value unit screens its G query heads
+// together, so each block's metadata is read once for all of them (a query head
+// of the group otherwise re-reads the same centroids). Lane l of wave w handles
+// blocks 256w + 4l .. + 3 of each pass; every centroid float4 feeds 4G FMAs.
+// Each head's list is compacted exactly as in screen_kernel (ballots plus an
+// LDS scan over the waves), so it comes out ascending with no atomics.
+template <int D, bool PRED, int G>
+__global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(ScreenArgs a) {
+    __shared__ float q_s[G][D];
+    __shared__ int wave_tot[G][kScreenMaxWaves];
+    __shared__ float red[kScreenMaxWaves];
+    __shared__ float tau_s[G];
+
+    const int ukv = blockIdx.x;  // key/value unit; its query units are ukv*G + j
+    const int u0 = ukv * G;
+    const int b = u0 / a.H;
+    const int nw = blockDim.x / kWave;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+
+    for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_s[i / D][i % D] = a.q[(size_t)u0 * D + i];
+    if (PRED) {
+        for (int j = 0; j < G; ++j) {
+            const int h = (u0 + j) - b * a.H;
+            float acc = 0.f;
+            if (a.W != nullptr) {
+                const float *qb = a.q + (size_t)b * a.H * D;
+                for (int k = threadIdx.x; k < a.H * D; k += blockDim.x) acc += qb[k] * a.W[(size_t)k * a.H + h];
+            }
+            acc = xrow_sum(row_sum16(acc));
+            if (lane == 0) red[wave] = acc;
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                float sum = 0.f;
+                for (int w = 0; w < nw; ++w) sum += red[w];
+                const float t = a.bias[h] + sum;
+                tau_s[j] = t;
+                a.tau[u0 + j] = t;
+            }
+            __syncthreads();  // red is reused by the next head
+        }
+    } else {
+        if (threadIdx.x < G) tau_s[threadIdx.x] = a.tau[u0 + threadIdx.x];
+        __syncthreads();
+    }
+
+    float t[G], geo_scale[G], z_scale[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        float qq = 0.f;
+        for (int i = lane; i < D; i += kWave) qq += q_s[j][i] * q_s[j][i];
+        const float qn = sqrtf(xrow_sum(row_sum16(qq)));
+        t[j] = tau_s[j];
+        geo_scale[j] = a.s * qn;
+        z_scale[j] = a.z * qn;
+    }
+
+    const int nblk = (a.lay.row_len(b) + kBlockTokens - 1) / kBlockTokens;  // this row's blocks
+    const float *cu = a.centroid + (size_t)ukv * D * a.nblk_cap;
+    const float *vu = a.var + (size_t)ukv * a.nblk_cap;
+    const float *mu = a.maxnorm + (size_t)ukv * a.nblk_cap;
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+
+    int base[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) base[j] = 0;
+    for (int pass0 = 0; pass0 < nblk; pass0 += nw * kBlocksPerWave) {
+        const int blk0 = pass0 + wave * kBlocksPerWave + lane * kBlocksPerLane;
+        const bool active = blk0 < nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
+        float acc[G][4];
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
+        if (active && !a.geo_only) {
+#pragma unroll 8
+            for (int dim = 0; dim < D; ++dim) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(cu + (size_t)dim * a.nblk_cap + blk0);
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    const float qd = q_s[j][dim];
+                    acc[j][0] += qd * c4.x;
+                    acc[j][1] += qd * c4.y;
+                    acc[j][2] += qd * c4.z;
+                    acc[j][3] += qd * c4.w;
+                }
+            }
+        }
+        float mx[4] = {0.f, 0.f, 0.f, 0.f}, vx[4] = {0.f, 0.f, 0.f, 0.f};
+        if (active) {
+            const float4 m4 = *reinterpret_cast<const float4 *>(mu + blk0);
+            mx[0] = m4.x; mx[1] = m4.y; mx[2] = m4.z; mx[3] = m4.w;
+            if (!a.geo_only) {
+                const float4 v4 = *reinterpret_cast<const float4 *>(vu + blk0);
+                vx[0] = v4.x; vx[1] = v4.y; vx[2] = v4.z; vx[3] = v4.w;
+            }
+        }
+        int before[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float U[4];
+            bool adm[4];
+            int bf = 0, total = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float u_geo = geo_scale[j] * mx[e];
+                if (a.geo_only) {
+                    U[e] = u_geo;
+                } else {
+                    const float u_prob = a.s * (acc[j][e] + z_scale[j] * sqrtf(vx[e]));
+                    U[e] = (u_prob < u_geo) ? u_prob : u_geo;
+                }
+                if (!active || blk0 + e >= nblk) U[e] = -INFINITY;
+                adm[e] = active && (blk0 + e < nblk) && (U[e] >= t[j]);
+                const uint64_t mask = __ballot(adm[e]);
+                bf += __popcll(mask & lanes_below);
+                total += __popcll(mask);
+            }
+            before[j] = bf;
+            if (lane == 0) wave_tot[j][wave] = total;
+            if (a.bound_out != nullptr && active) {
+                *reinterpret_cast<float4 *>(a.bound_out + (size_t)(u0 + j) * a.nblk_cap + blk0) =
+                    make_float4(U[0], U[1], U[2], U[3]);
+            }
+            // the admitted blocks are rewritten after the scan below: keep the bits
+            acc[j][0] = adm[0] ? 1.f : 0.f;
+            acc[j][1] = adm[1] ? 1.f : 0.f;
+            acc[j][2] = adm[2] ? 1.f : 0.f;
+            acc[j][3] = adm[3] ? 1.f : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            int grp_base = 0, pass_total = 0;
+            for (int w = 0; w < nw; ++w) {
+                const int c = wave_tot[j][w];
+                grp_base += (w < wave) ? c : 0;
+                pass_total += c;
+            }
+            int32_t *iu = a.adm_idx + (size_t)(u0 + j) * a.nblk_cap;
+            int pos = base[j] + grp_base + before[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (acc[j][e] != 0.f) iu[pos++] = blk0 + e;
+            base[j] += pass_total;
+        }
+        __syncthreads();  // wave_tot is rewritten by the next pass
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        if (threadIdx.x == j) a.adm_cnt[u0 + j] = base[j];
+}
+
 // Block groups per pass and dimension slices: up to 16 waves; split the
 // dimension when the unit has fewer than 16 x 256 blocks.
 void pick_shape(int nblk, int d, int *nbg, int *ds) {
@@ -241,6 +392,24 @@ hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau,
     a.adm_cnt = cnt;
     a.bound_out = bound_out;
     a.lay = g.lay;
+    if (g.G > 1) {
+        int nw = (g.nblk + kBlocksPerWave - 1) / kBlocksPerWave;
+        nw = nw < 1 ? 1 : (nw > kScreenMaxWaves ? kScreenMaxWaves : nw);
+        const dim3 grid((unsigned)g.kv_units), blk(nw * kWave);
+#define ETA_SCREEN_GROUP(GG)                                                                   \
+    if (predict) {                                                                             \
+        hipLaunchKernelGGL((screen_group_kernel<D, true, GG>), grid, blk, 0, st, a);          \
+    } else {                                                                                   \
+        hipLaunchKernelGGL((screen_group_kernel<D, false, GG>), grid, blk, 0, st, a);         \
+    }
+        switch (g.G) {
+            case 2: ETA_SCREEN_GROUP(2) break;
+            case 4: ETA_SCREEN_GROUP(4) break;
+            default: ETA_SCREEN_GROUP(8) break;
+        }
+#undef ETA_SCREEN_GROUP
+        return hipGetLastError();
+    }
     const dim3 block(a.nbg * a.ds * kWave);
     if (predict) {
         hipLaunchKernelGGL((screen_kernel<D, true>), dim3((unsigned)g.units), block, 0, st, a);
