@@ -298,7 +298,7 @@ def bench_prefill(args, w):
     """The training-time forward: eta_prefill_predict_tau + eta_prefill_attn per step."""
     from statistics import NormalDist
 
-    params = _lib.default_params()
+    params = _lib.default_params(gate_hard=1 if args.hard else 0)
     log(f"[bench] generating {w.name}: B={w.B} H={w.H}/{w.kv_heads} d={w.d} "
         f"T_q={w.T_q} T_k={w.T_k}")
     data = workloads.generate_prefill(w)
@@ -359,7 +359,8 @@ def bench_prefill(args, w):
         "dtype": "bf16 (q.k), fp16 (p.v), f32 accumulate",
         "data": "synthetic (seeded clustered keys; see DESIGN.md)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
-                   "T_q": w.T_q, "T_k": w.T_k, "parallelism": "single GPU"},
+                   "T_q": w.T_q, "T_k": w.T_k, "gate": "hard" if args.hard else "sigmoid",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "prefill_attn_kernel", "achieved": tflops,
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_PEAK_TFLOPS,
@@ -446,6 +447,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the density sweep (step time at admitted fractions 5..90%%)")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--hard", action="store_true",
+                    help="the hard gate (step at tau) instead of the sigmoid")
     ap.add_argument("--unfused", action="store_true",
                     help="separate eta_predict_tau + eta_screen launches instead of "
                          "eta_predict_screen")
@@ -467,7 +470,7 @@ def main():
         bench_prefill(args, workloads.PREFILL_WORKLOADS[args.workload])
         return
     w = workloads.WORKLOADS[args.workload]
-    params = _lib.default_params(split_blocks=args.split)
+    params = _lib.default_params(split_blocks=args.split, gate_hard=1 if args.hard else 0)
 
     log(f"[bench] generating {w.name}: B={w.B} H={w.H} d={w.d} T={w.T} {w.kv_dtype}")
     t0 = time.time()
@@ -611,7 +614,8 @@ def main():
                    "tokens_cached": int(sum(lens)),
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",
-                   "split_blocks": params.split_blocks or 16, "parallelism": "single GPU"},
+                   "split_blocks": params.split_blocks or 16,
+                   "gate": "hard" if params.gate_hard else "sigmoid", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "attn_partial_kernel", "achieved": attn_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
                      "traffic": counter_traffic(w.name),

@@ -55,17 +55,31 @@ __device__ __forceinline__ float row_max16(float x) {
     return x;
 }
 
+// Combine lanes l and l ^ 16 (rows 0-1 and 2-3) or l and l ^ 32 (the two halves of
+// the wave) without LDS: each swap leaves a lane's own value in one result and its
+// partner's in the other, the lower row's first in both, so both partners get
+// bitwise the same result (addition and max are commutative, so it also equals
+// adding the partner's value to one's own).
+__device__ __forceinline__ float row_pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Combine the four rows of the wave (lanes c, c+16, c+32, c+48).
-__device__ __forceinline__ float xrow_sum(float x) {
-    x += __shfl_xor(x, 16, kWave);
-    x += __shfl_xor(x, 32, kWave);
-    return x;
-}
-__device__ __forceinline__ float xrow_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16, kWave));
-    x = fmaxf(x, __shfl_xor(x, 32, kWave));
-    return x;
-}
+__device__ __forceinline__ float xrow_sum(float x) { return half_pair_sum(row_pair_sum(x)); }
+__device__ __forceinline__ float xrow_max(float x) { return half_pair_max(row_pair_max(x)); }
 
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }

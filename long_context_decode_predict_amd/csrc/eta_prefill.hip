@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
         } else {
             mx = gate_tile<HARD, GSUM, false>(a, acc, t_acc, nbt, 0, g, g_sum);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));  // the partner lane holds the other 32 keys
+        mx = half_pair_max(mx);  // the partner lane l ^ 32 holds the other 32 keys
         const float m_new = fmaxf(m_run, mx);
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // nothing visible yet: weights 0
         const float corr = __builtin_amdgcn_exp2f((m_run - m_ref) * a.c_soft);
@@ -304,8 +304,8 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
     }
 
     // the two halves of a query's keys meet
-    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-    const float gs_tot = GSUM ? g_sum + __shfl_xor(g_sum, 32, kWave) : 0.f;
+    const float l_tot = half_pair_sum(l_run);
+    const float gs_tot = GSUM ? half_pair_sum(g_sum) : 0.f;
     if (qi < a.T_q) {
         const size_t uq = (size_t)bh * a.T_q + qi;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
