@@ -225,6 +225,40 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, lens, max_units=256, thr
             "gpu_over_cpu": (1000.0 / step_gpu_ms) * step_s}
 
 
+def row_rooflines(w, lens, params, build_ms, front_ms, attn_ms, attn_alg, comb_ms, cnt, ucnt,
+                  fused):
+    """Achieved HBM GB/s of each step of the path against the 8 TB/s peak: algorithmic
+    bytes (what the step must read and write once) over its measured time."""
+    eb = elem_bytes(w.kv_dtype)
+    units_kv = w.kv_heads
+    nblk_rows = [(t + 63) // 64 for t in lens]
+    blocks_kv = units_kv * sum(nblk_rows)               # metadata entries
+    meta_b = blocks_kv * (w.d + 2) * 4
+    k_bytes = units_kv * sum(lens) * w.d * eb
+    split = params.split_blocks or 16
+    items = np.ceil(ucnt / split)
+    multi = items * (items > 1)
+    comb_b = int(multi.sum()) * w.G * (w.d + 2) * 4 + int((items > 1).sum()) * w.G * w.d * 4
+    front_b = (meta_b + int(cnt.sum()) * 4 + w.B * w.H * (w.d * 4 + 8)
+               + (w.H * w.d * w.H * 4 if fused and not w.static_tau else 0))
+    if w.G > 1:  # the union reads the per-head lists and writes the union
+        front_b += int(cnt.sum()) * 4 + int(ucnt.sum()) * 4
+
+    def row(nbytes, ms, what):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bytes": int(nbytes), "ms": ms, "gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+                "what": what}
+
+    return {
+        "a0_meta_build": row(k_bytes + meta_b, build_ms, "K read once, metadata written"),
+        "a1_a2_predict_screen": row(front_b, front_ms, "metadata of every block read once"
+                                    + (" per key/value unit, union" if w.G > 1 else "")
+                                    + ", lists written"),
+        "a3_attention_partial": row(attn_alg, attn_ms, "admitted K/V read once"),
+        "a4_combine": row(comb_b, comb_ms, "partials of multi-item units read, out written"),
+    }
+
+
 def unit_kv(data, b, k, T_b):
     """Device K, V [T_b, d] of key/value head k of row b, in either layout."""
     if "Kp" in data:
@@ -546,6 +580,8 @@ def main():
              "predict_screen": "fused (eta_predict_screen)" if fused else "separate"}
     if append_ms is not None:
         extra["append_ms_per_token"] = append_ms
+    extra["rows"] = row_rooflines(w, lens, params, build_ms, front_ms, attn_ms, attn_alg, comb_ms,
+                                  cnt, ucnt, fused)
     per_head = frac.mean(axis=0)
     extra["per_head_density_min_max"] = [float(per_head.min()), float(per_head.max())]
     union = None
