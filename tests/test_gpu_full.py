@@ -89,3 +89,55 @@ def test_full_size(name):
         st = compare_units(case, units[:4], check_meta=False)
         assert st["out_checked"] == len(units[:4])
     case.free()
+
+
+@pytest.mark.parametrize("name", list(workloads.PREFILL_WORKLOADS))
+def test_prefill_full_size(name):
+    """The training-time forward at the benchmark's sizes and launch configuration
+    (Eq. 1 per token on the GPU, then the gated forward): a seeded sample of
+    (row, head, query) triples, spread over early, middle and last positions, is
+    compared with the oracle (its own Eq. 1 for tau, a one-query call over the
+    query's causal window)."""
+    from oracle import oracle as oracle_mod
+    from statistics import NormalDist
+    import math
+    w = workloads.PREFILL_WORKLOADS[name]
+    print(f"\n[full] {name} B={w.B} H={w.H}/{w.kv_heads} d={w.d} T={w.T_q}", flush=True)
+    data = workloads.generate_prefill(w)
+    params = _lib.default_params()
+    bias_v = NormalDist().inv_cdf(1.0 - w.inclusion) * math.sqrt(2.0 + w.sigma ** 2)
+    bias = torch.full((w.H,), bias_v, dtype=torch.float32, device="cuda")
+    B, H, T, d = data["Q"].shape
+    tau = torch.empty((B, H, T), device="cuda")
+    out = torch.empty((B, H, T, d), device="cuda")
+    lse = torch.empty((B, H, T), device="cuda")
+    gs = torch.empty((B, H, T), device="cuda")
+    _lib.eta_prefill_predict_tau(data["Q"], data["W"], bias, tau)
+    _lib.eta_prefill_attn(data["Q"], data["K"], data["V"], tau, params, out, lse, gs)
+    torch.cuda.synchronize()
+    O = oracle_mod.default()
+    rng = np.random.default_rng(w.seed)
+    picks = [(0, 0, 0), (B - 1, H - 1, T - 1)]
+    picks += [(int(rng.integers(B)), int(rng.integers(H)), int(t))
+              for t in np.concatenate([rng.integers(0, 256, 4), rng.integers(256, T, 10)])]
+    Wn = data["W"].cpu().numpy()
+    bn = bias.cpu().numpy()
+    worst = 0.0
+    for b, h, t in picks:
+        hk = h // w.G
+        q_tok = data["Q"][b, :, t, :].float().cpu().numpy()[None]  # all heads of token t
+        tau_o = float(O.predict_tau(q_tok, Wn, bn)[0, h])
+        assert abs(float(tau[b, h, t]) - tau_o) <= 1e-5, (b, h, t)
+        Kb = data["K"][b, hk, :t + 1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        Vb = data["V"][b, hk, :t + 1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        Qb = data["Q"][b, h, t:t + 1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        o_o, l_o, g_o = O.prefill(Qb, Kb, Vb, t + 1, np.array([tau_o]))
+        err = float(np.max(np.abs(out[b, h, t].cpu().numpy() - o_o[0])))
+        assert err <= 2e-3, (b, h, t, err)
+        assert abs(float(lse[b, h, t]) - l_o[0]) <= 1e-4, (b, h, t)
+        assert abs(float(gs[b, h, t]) - g_o[0]) <= 1e-4 * abs(g_o[0]) + 1e-3, (b, h, t)
+        worst = max(worst, err)
+    incl = float(gs.double().sum()) / (B * H * T * (T + 1) / 2)
+    print(f"  sampled {len(picks)} queries, max|dout| {worst:.2e}, mean inclusion {incl:.3f}",
+          flush=True)
+    assert 0.05 < incl < 0.3
