@@ -8,8 +8,9 @@
  *      Assessment", Eq. 1), or use frozen per-head constants (abstract: offline
  *      calibration);
  *   2. screen every 64-token KV block in O(1) against tau with a bound built
- *      from cached per-block metadata (abstract: geometric-probabilistic
- *      bounds; review "Summary": centroid / variance / max-norm);
+ *      from cached per-block metadata (abstract: a bound with a geometric
+ *      and a probabilistic part; review "Summary": centroid / variance /
+ *      max-norm);
  *   3. skip every block whose bound is below tau (review Q&A "What is ETA?");
  *   4. softmax attention over the admitted blocks' tokens, each logit S
  *      multiplied by the gate sigmoid(beta*(S - tau)) (Eq. 2 and Eq. 3), so a
@@ -165,9 +166,9 @@ eta_status eta_predict_tau(int B, int H, int d, const float *q, const float *W,
                            const float *bias, float *tau, hipStream_t stream);
 
 /*
- * O(1) block screen (abstract: cached geometric-probabilistic bounds; review
- * Q&A "What is ETA?": a block whose best possible score is below tau is
- * skipped). With s = 1/sqrt(d), per block:
+ * Constant-time block screen (abstract: a cached bound with a geometric and a
+ * probabilistic part; review Q&A "What is ETA?": a block none of whose keys
+ * can reach tau is skipped). With s = 1/sqrt(d), per block:
  *   U_geo  = s * |q| * maxnorm                        (Cauchy-Schwarz)
  *   U_prob = s * (q . centroid + z * |q| * sqrt(var)) (centroid + z std devs)
  *   U = min(U_geo, U_prob)  (ETA_BOUND_COMBINED)  or  U_geo (ETA_BOUND_GEO)
@@ -197,9 +198,9 @@ eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W
 
 /*
  * Grouped heads: union, per key/value head, of the admitted lists of its G
- * query heads (the pages' "union density" is the share of blocks loaded this
- * way; abstract: tokens co-admitted by coarse block selection are absorbed by
- * the gate's floor). uni_idx[k] = ascending union of adm_idx[k*G + j][0..cnt)
+ * query heads (the pages measure the fraction of blocks fetched this way;
+ * abstract: the gate's floor makes tokens that only ride along with a selected
+ * block harmless). uni_idx[k] = ascending union of adm_idx[k*G + j][0..cnt)
  * over j < G, uni_cnt[k] its length. Deterministic. With G = 1 it copies the
  * lists. Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_HIP.
  */
@@ -212,7 +213,7 @@ size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);
 
 /*
  * Block-sparse split-KV decode attention with the ETA gate (Eq. 2 and Eq. 3;
- * abstract: sub-threshold logits suppressed toward zero). adm_idx / adm_cnt
+ * abstract: a logit under the threshold is multiplied down to zero). adm_idx / adm_cnt
  * are lists per key/value unit ([B][H_kv][nblk_cap], [B][H_kv]): the
  * eta_screen lists for multi-head attention, the eta_admit_union lists for
  * grouped heads. Every query head h of key/value unit k attends, with its own
@@ -267,8 +268,9 @@ eta_status eta_decode_attn_combine(const eta_shape *s, const int32_t *adm_cnt,
  * The gate the model is trained with, applied densely: for every query token t
  * of a sequence and every key j at or before it, S = q_t . k_j / sqrt(d) and
  * the logit entering the softmax is S * sigmoid(beta * (S - tau_t)) (review
- * "Methodology Assessment", Eq. 2 and Eq. 3; abstract: sub-threshold logits
- * are suppressed toward zero during training rather than deleted), tau_t from
+ * "Methodology Assessment", Eq. 2 and Eq. 3; abstract: in training a logit
+ * under the threshold is multiplied down to zero instead of being masked
+ * out), tau_t from
  * Eq. 1 on token t's concatenated queries. Causal: the T_q queries are the
  * last T_q positions of the T_k keys (T_q = T_k: a whole sequence; T_q < T_k:
  * a chunk continuing a cached prefix).

@@ -2,8 +2,8 @@
 // causal attention over whole sequences with every logit S = s * q.k multiplied
 // by sigmoid(beta * (S - tau_t)), tau_t the threshold of query token t
 // (evolve.pub review, "Methodology Assessment": Eq. 1 per token, Eq. 2 gate,
-// Eq. 3 multiplicative gating; arXiv:2609.20888 abstract: sub-threshold logits
-// are suppressed toward zero during training rather than deleted).
+// Eq. 3 multiplicative gating; arXiv:2609.20888 abstract: in training a logit
+// under the threshold is multiplied down to zero instead of being masked out).
 //
 // Unlike the decode step this is a dense contraction, so both products run on
 // the CDNA4 matrix cores (32x32x16 MFMA):

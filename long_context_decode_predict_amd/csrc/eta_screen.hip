@@ -1,8 +1,9 @@
 // eta_screen.hip -- O(1) per-block screen and ordered compaction.
 //
-// arXiv:2609.20888 abstract: KV blocks are screened in O(1) time from cached
-// geometric-probabilistic bounds; evolve.pub review, Q&A "What is ETA?": a
-// block whose best possible score is below the threshold is skipped. With
+// arXiv:2609.20888 abstract: each KV block is screened in constant time from a
+// cached bound with a geometric and a probabilistic part; evolve.pub review,
+// Q&A "What is ETA?": a block none of whose keys can reach the threshold is
+// skipped. With
 // s = 1/sqrt(d):
 //   U_geo  = s * |q| * maxnorm                       (Cauchy-Schwarz)
 //   U_prob = s * (q . centroid + z * |q| * sqrt(var))

@@ -1,10 +1,10 @@
 // eta_union.hip -- union of the admitted lists of the query heads that share
 // one key/value head (grouped heads).
 //
-// The pages count "union density": the share of KV blocks that must be loaded
-// when the blocks several heads admit are loaded together (evolve.pub review,
-// Q&A on speed and "Summary"; arXiv:2609.20888 abstract: tokens co-admitted by
-// coarse block selection are absorbed). With G query heads per key/value head,
+// The pages measure the fraction of KV blocks fetched when the selections of
+// several heads are fetched together (evolve.pub review, Q&A on speed and
+// "Summary"), and the gate's floor is what lets tokens that only ride along with
+// a selected block do no harm (arXiv:2609.20888 abstract). With G query heads per key/value head,
 // a block is loaded once for the key/value head when any of its G query heads
 // admits it, and each query head attends over that union with its own gate.
 //

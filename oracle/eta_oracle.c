@@ -12,10 +12,10 @@
  *     skipped when the best score any of its keys could reach is below tau;
  *   - the same review, "Summary": the screen uses cached per-block centroid,
  *     variance and max-norm metadata;
- *   - the paper abstract (montaan.com paper page, "Abstract"): O(1) block
- *     screening from cached geometric-probabilistic bounds, sub-threshold
- *     logits suppressed toward zero, frozen per-head thresholds after offline
- *     calibration.
+ *   - the paper abstract (montaan.com paper page, "Abstract"): constant-time
+ *     block screening from cached bounds with a geometric and a probabilistic
+ *     part, logits under the threshold multiplied down to zero, frozen per-head
+ *     thresholds after offline calibration.
  * Where the pages leave a step open, the reading taken is stated at the
  * function. Only the test suite, the smoke check and the benchmark's CPU
  * baseline may load this file's library; the GPU path never does.
@@ -153,8 +153,8 @@ int eta_oracle_screen(int nblk, const double *U, double tau, int32_t *idx) {
     return cnt;
 }
 
-/* Grouped heads (a reading: the pages count "union density", the share of
- * blocks loaded when the blocks of several heads are loaded together). A
+/* Grouped heads (a reading: the pages measure the fraction of blocks fetched
+ * when the selections of several heads are fetched together). A
  * block is loaded for a KV head when any of its query heads admits it; each
  * query head then attends over that union with its own gate, so blocks that
  * only another head admitted enter through the gate's floor. */
@@ -237,8 +237,8 @@ void eta_oracle_attend(int T, int d, int bs, int kv_dtype, const float *q_unit,
 }
 
 /* Training-time forward (review "Methodology Assessment", Eq. 1-3 applied to
- * every query token; abstract: sub-threshold logits are suppressed toward zero
- * during training): the T_q queries are the last T_q positions of the T_k
+ * every query token; abstract: in training a logit under the threshold is
+ * multiplied down to zero): the T_q queries are the last T_q positions of the T_k
  * keys, and query t (position T_k - T_q + t) sees keys 0 .. its position.
  * For each query: out and lse are the gated attention of eta_oracle_attend
  * over its visible keys (all their blocks admitted), and gate_sum is the sum

@@ -11,8 +11,8 @@ Sources pinned (pages describing arXiv:2609.20888):
   * evolve.pub review, "Methodology Assessment": Eq. 1 predictor, Eq. 2
     logistic gate with slope 3.35e-4 at 8, Eq. 3 multiplicative gating;
   * evolve.pub review, Q&A on attention sinks: a suppressed logit weighs e^0 = 1;
-  * evolve.pub review, Q&A "What is ETA?": blocks whose best possible score is
-    below tau are skipped (hence the bound must dominate every key's score).
+  * evolve.pub review, Q&A "What is ETA?": a block none of whose keys can reach
+    tau is skipped (hence the bound must dominate every key's score).
 """
 from __future__ import annotations
 
