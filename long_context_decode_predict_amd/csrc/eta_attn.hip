@@ -23,6 +23,9 @@
 //   - dot products reduce over the 16 lanes of a DPP row; the gated logits of
 //     a whole tile are formed first, so the running (max, sum, weighted V)
 //     state is rescaled once per tile, not per token.
+// With grouped heads (G > 1) the per-row dot products are reduce-scattered
+// instead (attn_item_dist): each lane ends with whole (head, row) pairs and the
+// gate and softmax weight are evaluated once per pair, not on all 16 lanes.
 // The waves' states merge in LDS. A one-item unit writes out/lse directly;
 // otherwise each item stores a (max, sum, weighted V) partial and the combine
 // kernel merges a unit's partials in item order with a log-sum-exp
@@ -293,6 +296,283 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     }
 }
 
+// ---- grouped heads: one gate per (token, head) instead of one per lane ----
+//
+// With G query heads per tile every 16-lane row holds, per lane, partial dot
+// products of P = G*L (head, row-load) pairs (head-major: k = j*L + i). A
+// reduce-scatter over the row (four halving steps on the same DPP patterns as
+// row_sum16) leaves lane c with the full sums of the m = P/16 pairs
+// k = c*m .. c*m + m - 1, all of one head j = c*m / L. The gate, the tile
+// maximum and the softmax weight are then computed once per pair rather than on
+// all 16 lanes of the row; the weights come back to the row with one DPP row
+// broadcast per pair for the P.V products.
+
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+// Broadcast lane n (compile-time after unrolling) of each row to the row.
+__device__ __forceinline__ float row_bcast_n(float x, int n) {
+    switch (n) {
+        case 0: return row_bcast<0>(x);
+        case 1: return row_bcast<1>(x);
+        case 2: return row_bcast<2>(x);
+        case 3: return row_bcast<3>(x);
+        case 4: return row_bcast<4>(x);
+        case 5: return row_bcast<5>(x);
+        case 6: return row_bcast<6>(x);
+        case 7: return row_bcast<7>(x);
+        case 8: return row_bcast<8>(x);
+        case 9: return row_bcast<9>(x);
+        case 10: return row_bcast<10>(x);
+        case 11: return row_bcast<11>(x);
+        case 12: return row_bcast<12>(x);
+        case 13: return row_bcast<13>(x);
+        case 14: return row_bcast<14>(x);
+        default: return row_bcast<15>(x);
+    }
+}
+
+// One halving step of the reduce-scatter: lanes whose `hi` bit is clear keep
+// the first half of v (plus the partner's first half), the others the second.
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_step(float (&v)[64], bool hi) {
+#pragma unroll
+    for (int t = 0; t < N / 2; ++t) {
+        const float lo_sum = v[t] + dpp_for_add<CTRL>(v[t]);
+        const float hi_sum = v[N / 2 + t] + dpp_for_add<CTRL>(v[N / 2 + t]);
+        v[t] = hi ? hi_sum : lo_sum;
+    }
+}
+
+// Maximum / sum over the aligned group of GS lanes of a row (GS = 16/G).
+template <int GS>
+__device__ __forceinline__ float group_max(float x) {
+    if (GS >= 2) x = fmaxf(x, dpp_mov<kQuadXor1>(x));
+    if (GS >= 4) x = fmaxf(x, dpp_mov<kQuadXor2>(x));
+    if (GS >= 8) x = fmaxf(x, dpp_mov<kRowHalfMirror>(x));
+    if (GS >= 16) x = fmaxf(x, dpp_mov<kRowMirror>(x));
+    return x;
+}
+template <int GS>
+__device__ __forceinline__ float group_sum(float x) {
+    if (GS >= 2) x += dpp_for_add<kQuadXor1>(x);
+    if (GS >= 4) x += dpp_for_add<kQuadXor2>(x);
+    if (GS >= 8) x += dpp_for_add<kRowHalfMirror>(x);
+    if (GS >= 16) x += dpp_for_add<kRowMirror>(x);
+    return x;
+}
+
+template <typename KV, int D, int TS, bool HARD, int G>
+__device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chunk,
+                                               AttnShared<D, G> &sm) {
+    constexpr int EPL = D / 16;
+    constexpr int L = TS / 4;               // row loads per lane per tile
+    constexpr int TPB = kBlockTokens / TS;  // tiles per block
+    constexpr int ROW = D;
+    constexpr int P = G * L;                // (head, row-load) pairs per row
+    constexpr int M = P / 16;               // pairs owned per lane
+    constexpr int GS = 16 / G;              // lanes of a row that own one head
+    static_assert(P >= 16 && P <= 64 && P % 16 == 0 && L % M == 0, "pair layout");
+    const int c = a.cnt[u];
+    const int nchunks = (c + a.split - 1) / a.split;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int row = lane >> 4;
+    const int col = lane & 15;
+    const int my_j = col / GS;          // the head whose pairs this lane owns
+    const int my_i0 = (col * M) % L;    // its first row-load
+
+    float qr[G][EPL];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const size_t uq = (size_t)u * G + j;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qr[j][e] = a.q[uq * D + col * EPL + e] * a.s;
+    }
+    const float t_own = a.tau[(size_t)u * G + my_j];
+    const float nbt_own = -a.nbl2e * t_own;
+
+    const KV *Kp = static_cast<const KV *>(a.K);
+    const KV *Vp = static_cast<const KV *>(a.V);
+    const int rb = u / a.lay.H_kv;
+    const int kh = u - rb * a.lay.H_kv;
+    const int Tb = a.lay.row_len(rb);
+    const int lane_off = row * ROW + col * EPL;
+    const int32_t *iu = a.idx + (size_t)u * a.nblk_cap;
+
+    const int j0 = chunk * a.split;
+    const int j1 = min(c, j0 + a.split);
+    const int nb = (j1 - j0 - wave + kAttnWaves - 1) / kAttnWaves;
+    const int ntiles = nb > 0 ? nb * TPB : 0;
+
+    float m_run = -INFINITY, l_run = 0.f;  // for head my_j: l over this lane's pairs
+    float o[G][EPL];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
+
+    auto tile_at = [&](int tt, size_t &off, int &valid) {
+        const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
+        const long long bo = a.lay.block_offset(rb, kh, blk, D);
+        const int sub = (tt % TPB) * TS;
+        off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * ROW;
+        valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
+    };
+
+    RowLoad<KV, EPL> kb[L], vb[L];
+    size_t next_off = 0;
+    int next_valid = 0;
+    if (ntiles > 0) {
+        tile_at(0, next_off, next_valid);
+        const KV *p = Kp + next_off + lane_off;
+#pragma unroll
+        for (int i = 0; i < L; ++i) kb[i].load(p + i * 4 * ROW);
+    }
+    for (int tt = 0; tt < ntiles; ++tt) {
+        const size_t base = next_off;
+        const int valid = next_valid;
+        {
+            const KV *p = Vp + base + lane_off;
+#pragma unroll
+            for (int i = 0; i < L; ++i) vb[i].load(p + i * 4 * ROW);
+        }
+        // partial dots of every (head, row-load) pair, head-major
+        float v[64];
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            float x[EPL];
+            kb[i].widen(x);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) dot += qr[j][e] * x[e];
+                v[j * L + i] = dot;
+            }
+        }
+        // the K registers are free: start the next tile's K loads
+        if (tt + 1 < ntiles) {
+            tile_at(tt + 1, next_off, next_valid);
+            const KV *p = Kp + next_off + lane_off;
+#pragma unroll
+            for (int i = 0; i < L; ++i) kb[i].load(p + i * 4 * ROW);
+        }
+        // reduce-scatter over the row: lane col ends with pairs col*M .. col*M + M - 1
+        rs_step<kRowMirror, P>(v, (col >> 3) & 1);
+        rs_step<kRowHalfMirror, P / 2>(v, (col >> 2) & 1);
+        rs_step<kQuadXor2, P / 4>(v, (col >> 1) & 1);
+        rs_step<kQuadXor1, P / 8>(v, col & 1);
+
+        // gate of the owned pairs, rows past the row's length masked
+        float gv[M];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            const float S = v[t];
+            float g;
+            if (HARD) {
+                g = S >= t_own ? S : 0.f;
+            } else {
+                g = S * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(a.nbl2e, S, nbt_own)));
+            }
+            if (4 * (my_i0 + t) + row >= valid) g = -INFINITY;
+            gv[t] = g;
+            bmax = fmaxf(bmax, g);
+        }
+        bmax = xrow_max(group_max<GS>(bmax));  // over the head's lanes and the 4 rows
+        const float mx = fmaxf(m_run, bmax);
+        const float m_ref = mx == -INFINITY ? 0.f : mx;  // nothing visible yet: weights 0
+        const float corr = fast_exp(m_run - m_ref);
+        m_run = mx;
+        l_run *= corr;
+        float pw[M];
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            pw[t] = fast_exp(gv[t] - m_ref);
+            l_run += pw[t];
+        }
+        // every lane rescales and accumulates all G heads' outputs
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float cj = row_bcast_n(corr, j * GS);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[j][e] *= cj;
+        }
+        if (valid < TS) {
+#pragma unroll
+            for (int i = 0; i < L; ++i)
+                if (4 * i + row >= valid) zero_row<KV, EPL>(vb[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            float x[EPL];
+            vb[i].widen(x);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int k = j * L + i;
+                const float p = row_bcast_n(pw[k % M], k / M);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[j][e] += p * x[e];
+            }
+        }
+    }
+
+    // merge: l over the head's lanes and the rows; outputs over the rows
+    const float l_head = xrow_sum(group_sum<GS>(l_run));
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[j][e] = xrow_sum(o[j][e]);
+        if (lane < 16) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm.o[wave][j][lane * EPL + e] = o[j][e];
+        }
+    }
+    if (lane < 16 && col % GS == 0) {  // the first lane of each head's group, row 0
+        sm.m[wave][my_j] = m_run;
+        sm.l[wave][my_j] = l_head;
+    }
+    __syncthreads();
+
+    for (int j = 0; j < G; ++j) {
+        float M_ = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) M_ = fmaxf(M_, sm.m[w][j]);
+        const float Mr = M_ == -INFINITY ? 0.f : M_;
+        float Lsum = 0.f;
+        float wgt[kAttnWaves];
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+            wgt[w] = fast_exp(sm.m[w][j] - Mr);
+            Lsum += sm.l[w][j] * wgt[w];
+        }
+        const size_t uq = (size_t)u * G + j;
+        if (tid < D) {
+            float O = 0.f;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) O += sm.o[w][j][tid] * wgt[w];
+            if (nchunks == 1) {
+                a.out[uq * D + tid] = Lsum > 0.f ? O / Lsum : 0.f;
+            } else {
+                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
+                a.ws_o[slot * D + tid] = O;
+            }
+        }
+        if (tid == 0) {
+            if (nchunks == 1) {
+                if (a.lse) a.lse[uq] = Lsum > 0.f ? M_ + __logf(Lsum) : -INFINITY;
+            } else {
+                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
+                a.ws_m[slot] = M_;
+                a.ws_l[slot] = Lsum;
+            }
+        }
+    }
+}
+
 // Persistent workers: each workgroup takes item tickets until the list is done.
 template <typename KV, int D, int TS, bool HARD, int G>
 __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArgs a) {
@@ -305,7 +585,11 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
         const int2 it = a.ws_items[ticket];
         int next = 0;
         if (threadIdx.x == 0) next = atomicAdd(&a.ws_hdr[1], 1);  // fetched early
-        attn_item<KV, D, TS, HARD, G>(a, it.x, it.y, sm);
+        if constexpr (G > 1) {  // multi-head attention keeps the one-pass row layout
+            attn_item_dist<KV, D, TS, HARD, G>(a, it.x, it.y, sm);
+        } else {
+            attn_item<KV, D, TS, HARD, G>(a, it.x, it.y, sm);
+        }
         if (threadIdx.x == 0) sm.ticket = next;
         __syncthreads();
         ticket = sm.ticket;
