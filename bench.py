@@ -241,8 +241,8 @@ def row_rooflines(w, lens, params, build_ms, front_ms, attn_ms, attn_alg, comb_m
     comb_b = int(multi.sum()) * w.G * (w.d + 2) * 4 + int((items > 1).sum()) * w.G * w.d * 4
     front_b = (meta_b + int(cnt.sum()) * 4 + w.B * w.H * (w.d * 4 + 8)
                + (w.H * w.d * w.H * 4 if fused and not w.static_tau else 0))
-    if w.G > 1:  # the union reads the per-head lists and writes the union
-        front_b += int(cnt.sum()) * 4 + int(ucnt.sum()) * 4
+    if w.G > 1:  # the union is written (and, when formed by its own kernel, the lists re-read)
+        front_b += (0 if fused else int(cnt.sum()) * 4) + int(ucnt.sum()) * 4
 
     def row(nbytes, ms, what):
         gbs = nbytes / (ms * 1e-3) / 1e9

@@ -207,6 +207,22 @@ eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W
 eta_status eta_admit_union(const eta_shape *s, const int32_t *adm_idx, const int32_t *adm_cnt,
                            int32_t *uni_idx, int32_t *uni_cnt, hipStream_t stream);
 
+/*
+ * eta_predict_screen followed by eta_admit_union, in one launch: with grouped
+ * heads one workgroup screens the G query heads of a key/value unit together,
+ * so the union of their lists is formed from the same admission bits and
+ * written beside them. Outputs and errors as the two calls it replaces (tau,
+ * adm_idx, adm_cnt and bound_out as eta_predict_screen; uni_idx, uni_cnt as
+ * eta_admit_union, [B][H_kv][nblk_cap] and [B][H_kv]). Requires grouped heads
+ * (H_kv < H): with multi-head attention the lists are already per key/value
+ * unit and the call returns ETA_ERR_INVALID_ARG.
+ */
+eta_status eta_predict_screen_union(const eta_shape *s, const float *q, const float *W,
+                                    const float *bias, const eta_meta *m, const eta_params *p,
+                                    float *tau, int32_t *adm_idx, int32_t *adm_cnt,
+                                    int32_t *uni_idx, int32_t *uni_cnt, float *bound_out,
+                                    hipStream_t stream);
+
 /* Bytes of device workspace the attention calls need for this shape and split
  * size (0 on invalid arguments). The layout is private to the library. */
 size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);

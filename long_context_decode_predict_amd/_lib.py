@@ -77,6 +77,9 @@ SIGNATURES = {
     "eta_predict_screen": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _P(eta_meta),
                                           _P(eta_params), _vp, _vp, _vp, _vp, _vp]),
     "eta_admit_union": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp]),
+    "eta_predict_screen_union": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _P(eta_meta),
+                                                _P(eta_params), _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _vp]),
     "eta_decode_attn_workspace_size": (ctypes.c_size_t, [_P(eta_shape), _P(eta_params)]),
     "eta_decode_attn": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp, _vp,
                                        _P(eta_params), _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -334,6 +337,37 @@ def eta_predict_screen(q: torch.Tensor, W, bias: torch.Tensor, meta: Meta, T: in
                                     ctypes.byref(m), ctypes.byref(params), tau.data_ptr(),
                                     adm_idx.data_ptr(), adm_cnt.data_ptr(), _ptr(bound_out),
                                     _stream(stream)))
+
+
+def eta_predict_screen_union(q: torch.Tensor, W, bias: torch.Tensor, meta: Meta, T: int,
+                             T_cap: int, params: eta_params, tau: torch.Tensor,
+                             adm_idx: torch.Tensor, adm_cnt: torch.Tensor, uni_idx: torch.Tensor,
+                             uni_cnt: torch.Tensor, bound_out=None, kv_dtype=torch.bfloat16,
+                             stream=None, layout: KVLayout | None = None):
+    """Grouped heads: eta_predict_screen and eta_admit_union in one launch."""
+    B, H, d = q.shape
+    H_kv = uni_idx.shape[1]
+    s = make_shape(B, H, d, T, T_cap, kv_dtype, H_kv, _lens_only(layout))
+    n = nblk_cap(T_cap)
+    _need(q, "q", torch.float32)
+    if W is not None:
+        _need(W, "W", torch.float32, (H * d, H))
+    _need(bias, "bias", torch.float32, (H,))
+    _need(tau, "tau", torch.float32, (B, H))
+    _check_meta(meta, B, H_kv, d, T_cap)
+    _need(adm_idx, "adm_idx", torch.int32, (B, H, n))
+    _need(adm_cnt, "adm_cnt", torch.int32, (B, H))
+    _need(uni_idx, "uni_idx", torch.int32, (B, H_kv, n))
+    _need(uni_cnt, "uni_cnt", torch.int32, (B, H_kv))
+    if bound_out is not None:
+        _need(bound_out, "bound_out", torch.float32, (B, H, n))
+    m = meta.c()
+    _check("eta_predict_screen_union",
+           lib().eta_predict_screen_union(ctypes.byref(s), q.data_ptr(), _ptr(W), bias.data_ptr(),
+                                          ctypes.byref(m), ctypes.byref(params), tau.data_ptr(),
+                                          adm_idx.data_ptr(), adm_cnt.data_ptr(),
+                                          uni_idx.data_ptr(), uni_cnt.data_ptr(),
+                                          _ptr(bound_out), _stream(stream)))
 
 
 def eta_admit_union(adm_idx: torch.Tensor, adm_cnt: torch.Tensor, uni_idx: torch.Tensor,

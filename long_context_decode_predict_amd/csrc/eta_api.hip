@@ -233,6 +233,26 @@ eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W
                                        adm_cnt, bound_out, stream));
 }
 
+eta_status eta_predict_screen_union(const eta_shape *s, const float *q, const float *W,
+                                    const float *bias, const eta_meta *m, const eta_params *p,
+                                    float *tau, int32_t *adm_idx, int32_t *adm_cnt,
+                                    int32_t *uni_idx, int32_t *uni_cnt, float *bound_out,
+                                    hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_meta(s, m)) != ETA_OK) return st;
+    if ((st = check_params(p)) != ETA_OK) return st;
+    if (q == nullptr || bias == nullptr || tau == nullptr || adm_idx == nullptr ||
+        adm_cnt == nullptr || uni_idx == nullptr || uni_cnt == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (kv_heads_of(s) == s->H) return ETA_ERR_INVALID_ARG;  // grouped heads only
+    if (bound_out != nullptr && !aligned(bound_out, 16)) return ETA_ERR_INVALID_ARG;
+    const eta::Geometry g = geometry(s, m->nblk_cap);
+    return from_hip(eta::launch_screen(g, s->H, q, tau, W, bias, true, m->centroid, m->var,
+                                       m->maxnorm, p->z, p->bound_mode == ETA_BOUND_GEO, adm_idx,
+                                       adm_cnt, bound_out, stream, uni_idx, uni_cnt));
+}
+
 eta_status eta_admit_union(const eta_shape *s, const int32_t *adm_idx, const int32_t *adm_cnt,
                            int32_t *uni_idx, int32_t *uni_cnt, hipStream_t stream) {
     eta_status st = check_shape(s);

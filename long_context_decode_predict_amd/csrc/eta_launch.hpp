@@ -36,10 +36,13 @@ hipError_t launch_predict_tau(int B, int H, int d, const float *q, const float *
 
 // Screen; with `predict` the threshold of every unit is first evaluated from
 // q, W (nullable) and bias and stored to tau, otherwise tau is read.
+// With grouped heads and uni_idx non-null the union per key/value unit is
+// written in the same launch.
 hipError_t launch_screen(const Geometry &g, int H, const float *q, float *tau, const float *W,
                          const float *bias, bool predict, const float *centroid,
                          const float *var, const float *maxnorm, float z, bool geo_only,
-                         int32_t *adm_idx, int32_t *adm_cnt, float *bound_out, hipStream_t st);
+                         int32_t *adm_idx, int32_t *adm_cnt, float *bound_out, hipStream_t st,
+                         int32_t *uni_idx = nullptr, int32_t *uni_cnt = nullptr);
 
 // Union, per key/value unit, of the admitted lists of its G query heads.
 hipError_t launch_union(const Geometry &g, const int32_t *adm_idx, const int32_t *adm_cnt,

@@ -53,6 +53,8 @@ struct ScreenArgs {
     int32_t *adm_cnt;
     float *bound_out;
     KVLayout lay;  // per-row token counts (the K/V addresses are not used here)
+    int32_t *uni_idx;  // grouped heads: union per key/value unit (null: not formed here)
+    int32_t *uni_cnt;
 };
 
 template <int D, bool PRED>
@@ -208,11 +210,13 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
 // of the group otherwise re-reads the same centroids). Lane l of wave w handles
 // blocks 256w + 4l .. + 3 of each pass; every centroid float4 feeds 4G FMAs.
 // Each head's list is compacted exactly as in screen_kernel (ballots plus an
-// LDS scan over the waves), so it comes out ascending with no atomics.
+// LDS scan over the waves), so it comes out ascending with no atomics; when
+// asked, the union of the G lists is compacted the same way from the OR of the
+// heads' admission bits.
 template <int D, bool PRED, int G>
 __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(ScreenArgs a) {
     __shared__ float q_s[G][D];
-    __shared__ int wave_tot[G][kScreenMaxWaves];
+    __shared__ int wave_tot[G + 1][kScreenMaxWaves];  // per head, then the union
     __shared__ float red[kScreenMaxWaves];
     __shared__ float tau_s[G];
 
@@ -269,6 +273,8 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
     int base[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) base[j] = 0;
+    int base_u = 0;
+    const bool with_union = a.uni_idx != nullptr;
     for (int pass0 = 0; pass0 < nblk; pass0 += nw * kBlocksPerWave) {
         const int blk0 = pass0 + wave * kBlocksPerWave + lane * kBlocksPerLane;
         const bool active = blk0 < nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
@@ -299,6 +305,7 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
             }
         }
         int before[G];
+        bool uadm[4] = {false, false, false, false};
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             float U[4];
@@ -326,12 +333,39 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
                     make_float4(U[0], U[1], U[2], U[3]);
             }
             // the admitted blocks are rewritten after the scan below: keep the bits
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uadm[e] = uadm[e] || adm[e];
             acc[j][0] = adm[0] ? 1.f : 0.f;
             acc[j][1] = adm[1] ? 1.f : 0.f;
             acc[j][2] = adm[2] ? 1.f : 0.f;
             acc[j][3] = adm[3] ? 1.f : 0.f;
         }
+        int before_u = 0;
+        if (with_union) {
+            int total = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint64_t mask = __ballot(uadm[e]);
+                before_u += __popcll(mask & lanes_below);
+                total += __popcll(mask);
+            }
+            if (lane == 0) wave_tot[G][wave] = total;
+        }
         __syncthreads();
+        if (with_union) {
+            int grp_base = 0, pass_total = 0;
+            for (int w = 0; w < nw; ++w) {
+                const int c = wave_tot[G][w];
+                grp_base += (w < wave) ? c : 0;
+                pass_total += c;
+            }
+            int32_t *iu = a.uni_idx + (size_t)ukv * a.nblk_cap;
+            int pos = base_u + grp_base + before_u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (uadm[e]) iu[pos++] = blk0 + e;
+            base_u += pass_total;
+        }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             int grp_base = 0, pass_total = 0;
@@ -352,6 +386,7 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
 #pragma unroll
     for (int j = 0; j < G; ++j)
         if (threadIdx.x == j) a.adm_cnt[u0 + j] = base[j];
+    if (with_union && threadIdx.x == 0) a.uni_cnt[ukv] = base_u;
 }
 
 // Block groups per pass and dimension slices: up to 16 waves; split the
@@ -372,7 +407,7 @@ template <int D>
 hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau, const float *W,
                            const float *bias, bool predict, const float *c, const float *v,
                            const float *m, float z, bool geo_only, int32_t *idx, int32_t *cnt,
-                           float *bound_out, hipStream_t st) {
+                           float *bound_out, hipStream_t st, int32_t *uni_idx, int32_t *uni_cnt) {
     ScreenArgs a;
     pick_shape(g.nblk, D, &a.nbg, &a.ds);
     a.nblk = g.nblk;
@@ -393,6 +428,8 @@ hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau,
     a.adm_cnt = cnt;
     a.bound_out = bound_out;
     a.lay = g.lay;
+    a.uni_idx = g.G > 1 ? uni_idx : nullptr;
+    a.uni_cnt = g.G > 1 ? uni_cnt : nullptr;
     if (g.G > 1) {
         int nw = (g.nblk + kBlocksPerWave - 1) / kBlocksPerWave;
         nw = nw < 1 ? 1 : (nw > kScreenMaxWaves ? kScreenMaxWaves : nw);
@@ -425,12 +462,15 @@ hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau,
 hipError_t launch_screen(const Geometry &g, int H, const float *q, float *tau, const float *W,
                          const float *bias, bool predict, const float *centroid,
                          const float *var, const float *maxnorm, float z, bool geo_only,
-                         int32_t *adm_idx, int32_t *adm_cnt, float *bound_out, hipStream_t st) {
+                         int32_t *adm_idx, int32_t *adm_cnt, float *bound_out, hipStream_t st,
+                         int32_t *uni_idx, int32_t *uni_cnt) {
     if (g.units == 0) return hipSuccess;
     return g.d == 128 ? launch_screen_t<128>(g, H, q, tau, W, bias, predict, centroid, var, maxnorm,
-                                             z, geo_only, adm_idx, adm_cnt, bound_out, st)
+                                             z, geo_only, adm_idx, adm_cnt, bound_out, st,
+                                             uni_idx, uni_cnt)
                       : launch_screen_t<64>(g, H, q, tau, W, bias, predict, centroid, var, maxnorm,
-                                            z, geo_only, adm_idx, adm_cnt, bound_out, st);
+                                            z, geo_only, adm_idx, adm_cnt, bound_out, st,
+                                            uni_idx, uni_cnt);
 }
 
 }  // namespace eta

@@ -4,8 +4,9 @@
 workspace) for one cache of B rows, H query heads and H_kv key/value heads
 (H_kv = H: multi-head attention) and enqueues the library calls of a step on
 the current stream with no host synchronisation:
-eta_predict_tau + eta_screen (or eta_predict_screen in one launch)
-[-> eta_admit_union for grouped heads] -> eta_decode_attn
+eta_predict_tau + eta_screen [-> eta_admit_union for grouped heads], or in one
+launch eta_predict_screen (eta_predict_screen_union for grouped heads)
+-> eta_decode_attn
 (= eta_decode_attn_partial followed by eta_decode_attn_combine).
 
 With ``layout`` (a ``_lib.KVLayout``) the rows hold their own lengths and/or the
@@ -49,10 +50,14 @@ class DecodeStep:
         _lib.eta_predict_tau(q, W, bias, self.tau, stream)
 
     def predict_screen(self, q, W, bias, meta, T, stream=None):
+        if self.G > 1:  # the union comes out of the same launch
+            _lib.eta_predict_screen_union(q, W, bias, meta, T, self.T_cap, self.params, self.tau,
+                                          self.adm_idx, self.adm_cnt, self.uni_idx, self.uni_cnt,
+                                          self.bounds, self.kv_dtype, stream, self.layout)
+            return
         _lib.eta_predict_screen(q, W, bias, meta, T, self.T_cap, self.params, self.tau,
                                 self.adm_idx, self.adm_cnt, self.bounds, self.kv_dtype, stream,
                                 self._hkv_arg, self.layout)
-        self.union(T, stream)
 
     def screen(self, q, meta, T, stream=None):
         _lib.eta_screen(q, self.tau, meta, T, self.T_cap, self.params, self.adm_idx,

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
@@ -274,3 +274,18 @@ def test_prefill_pointer_errors(L):
     assert L.eta_prefill_predict_tau(s, FAKE, FAKE, None, FAKE, None) == INV
     assert L.eta_prefill_predict_tau(s, FAKE, FAKE, FAKE, None, None) == INV
     assert L.eta_prefill_predict_tau(s, FAKE + 4, FAKE, FAKE, FAKE, None) == INV
+
+
+def test_predict_screen_union_errors(L):
+    p = BY(params())
+    call = lambda sh, **kw: L.eta_predict_screen_union(
+        BY(sh), kw.get("q", FAKE), FAKE, kw.get("bias", FAKE), BY(meta()), p, FAKE, FAKE, FAKE,
+        kw.get("uidx", FAKE), kw.get("ucnt", FAKE), None, None)
+    g = shape(H=8, H_kv=2)
+    assert call(shape()) == INV  # multi-head: no union to form
+    assert call(shape(H=8, H_kv=8)) == INV
+    assert call(g, uidx=None) == INV
+    assert call(g, ucnt=None) == INV
+    assert call(g, q=None) == INV
+    assert call(g, bias=None) == INV
+    assert call(shape(H=8, H_kv=3)) == INV
