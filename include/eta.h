@@ -116,7 +116,8 @@ typedef struct {
     int gate_hard;      /* 1: gate is the step S >= tau instead of the sigmoid */
     int bound_mode;     /* eta_bound_mode; default ETA_BOUND_COMBINED          */
     int split_blocks;   /* admitted blocks per split-KV work item (1..4096);
-                           0 = library default (16)                            */
+                           0 = library default (8 with multi-head attention,
+                           16 with grouped heads)                              */
 } eta_params;
 
 /* Defaults: beta = 5 (the end of the 1 -> 5 anneal of Eq. 2), z = 4, soft

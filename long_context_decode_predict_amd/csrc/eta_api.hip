@@ -12,7 +12,11 @@
 namespace {
 
 constexpr int kBlock = 64;
-constexpr int kDefaultSplit = 16;
+// Default blocks per split-KV work item: smaller items balance the persistent
+// workers better under multi-head attention; with grouped heads an item already
+// carries G heads' work (and G partials), so larger items pay off there.
+constexpr int kDefaultSplitMHA = 8;
+constexpr int kDefaultSplitGrouped = 16;
 constexpr int kMaxSplit = 4096;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -97,7 +101,10 @@ eta_status check_params(const eta_params *p) {
     return ETA_OK;
 }
 
-int split_of(const eta_params *p) { return p->split_blocks == 0 ? kDefaultSplit : p->split_blocks; }
+int split_of(const eta_shape *s, const eta_params *p) {
+    if (p->split_blocks != 0) return p->split_blocks;
+    return kv_heads_of(s) < s->H ? kDefaultSplitGrouped : kDefaultSplitMHA;
+}
 
 eta_status from_hip(hipError_t e) { return e == hipSuccess ? ETA_OK : ETA_ERR_HIP; }
 
@@ -111,7 +118,7 @@ eta_status check_attn(const eta_shape *s, const eta_params *p, const int32_t *ad
     if (adm_cnt == nullptr || out == nullptr) return ETA_ERR_INVALID_ARG;
     const size_t need = eta_decode_attn_workspace_size(s, p);
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return ETA_ERR_WORKSPACE;
-    long long mc = ceil_div(ceil_div(s->T_cap, kBlock), split_of(p));
+    long long mc = ceil_div(ceil_div(s->T_cap, kBlock), split_of(s, p));
     if (mc < 1) mc = 1;
     if ((long long)s->B * s->H * mc > 0x7fffffffll) return ETA_ERR_INVALID_ARG;
     *g = geometry(s, nblk_cap_of(s->T_cap));
@@ -265,7 +272,7 @@ eta_status eta_admit_union(const eta_shape *s, const int32_t *adm_idx, const int
 
 size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p) {
     if (check_shape(s) != ETA_OK || check_params(p) != ETA_OK) return 0;
-    const int split = split_of(p);
+    const int split = split_of(s, p);
     long long max_chunks = ceil_div(ceil_div(s->T_cap, kBlock), split);
     if (max_chunks < 1) max_chunks = 1;
     return eta::attn_workspace_layout(s->B * s->H, (int)max_chunks, s->d).bytes;
@@ -283,7 +290,7 @@ eta_status eta_decode_attn_partial(const eta_shape *s, const float *q, const voi
         return ETA_ERR_INVALID_ARG;
     if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
     return from_hip(eta::launch_attn_partial(g, q, K, V, tau, adm_idx, adm_cnt, p->gate_beta,
-                                             p->gate_hard != 0, split_of(p), max_chunks, out, lse,
+                                             p->gate_hard != 0, split_of(s, p), max_chunks, out, lse,
                                              ws, stream));
 }
 
@@ -294,7 +301,7 @@ eta_status eta_decode_attn_combine(const eta_shape *s, const int32_t *adm_cnt,
     int max_chunks = 0;
     eta_status st = check_attn(s, p, adm_cnt, out, ws, ws_bytes, &g, &max_chunks);
     if (st != ETA_OK) return st;
-    return from_hip(eta::launch_attn_combine(g, adm_cnt, split_of(p), max_chunks, out, lse, ws,
+    return from_hip(eta::launch_attn_combine(g, adm_cnt, split_of(s, p), max_chunks, out, lse, ws,
                                              stream));
 }
 
