@@ -410,7 +410,7 @@ def bench_prefill(args, w):
     print(json.dumps(result), flush=True)
 
 
-def prefill_cpu_baseline(w, data, tau, params, step_ms, n_queries=256):
+def prefill_cpu_baseline(w, data, tau, params, step_ms, n_queries=1024):
     """The oracle's forward for a seeded sample of query tokens (each with its whole
     causal window, the last tokens of a sequence: the most expensive), timed on the
     host cores and scaled by visible pairs to the whole workload."""
