@@ -7,8 +7,9 @@
 // absorbs the tokens that coarse block selection lets in (abstract).
 //
 // Work decomposition. A unit's ascending admitted list is cut into work items
-// of `split` blocks. A one-workgroup plan kernel scans the per-unit item counts
-// into a compacted item list (and settles empty units directly); a persistent
+// of `split` blocks. A plan kernel (one workgroup per 64 units) scans the
+// per-unit item counts into a compacted item list (and settles empty units
+// directly); a persistent
 // grid of a few workgroups per CU then takes items from the list through a
 // device-scope ticket counter, so no workgroup is launched for an absent item
 // and the load balances itself whatever the per-unit densities. A workgroup of
@@ -35,10 +36,11 @@
 // The K/V capacity is a whole number of blocks (dense layout) and a page holds
 // a whole block (paged layout), so the rows of a partial last block past the
 // row's length are inside the allocation: they are loaded unclamped and masked
-// (their logits become -inf and their values are zeroed before use). A block
-// whose page id is out of range is not read at all: its tiles load from the
-// first page and are masked whole, so the block contributes nothing (a unit
-// left with no token gets out = 0, lse = -inf, as an empty list does).
+// (their logits become -inf and their values are zeroed before use). For a
+// block whose page id is out of range no byte of the pool outside its pages is
+// touched: the tiles load from the first page instead and are masked whole, so
+// the block contributes nothing (a unit left with no token gets out = 0,
+// lse = -inf, as an empty list does).
 #include "eta_device.hpp"
 #include "eta_launch.hpp"
 
@@ -771,7 +773,8 @@ hipError_t launch_partial_t(const AttnArgs &a, bool hard, int workers, hipStream
 }
 
 // Tile rows per K/V register buffer: smaller tiles for wider rows and more
-// query heads per key/value head keep the kernel at two waves per SIMD.
+// query heads per key/value head keep every instance but fp32 d = 128 with
+// G = 2 at two or three waves per SIMD.
 template <typename KV, int D>
 hipError_t launch_partial_g(const AttnArgs &a, bool hard, int workers, hipStream_t st) {
     constexpr bool wide = sizeof(KV) * D > 256;  // fp32 rows of 128
@@ -780,7 +783,7 @@ hipError_t launch_partial_g(const AttnArgs &a, bool hard, int workers, hipStream
         case 1: return launch_partial_t<KV, D, wide ? 32 : 64, 1>(a, hard, workers, st);
         case 2: return launch_partial_t<KV, D, narrow ? 64 : 32, 2>(a, hard, workers, st);
         case 4: return launch_partial_t<KV, D, narrow ? 32 : (wide ? 16 : 32), 4>(a, hard, workers, st);
-        default: return launch_partial_t<KV, D, narrow ? 32 : 16, 8>(a, hard, workers, st);
+        default: return launch_partial_t<KV, D, narrow ? 32 : (D == 128 ? 8 : 16), 8>(a, hard, workers, st);
     }
 }
 

@@ -102,6 +102,10 @@ WORKLOADS = {
         "gqa_b32_h32kv8_d128_t128k_bf16", B=32, H=32, d=128, T=131072,
         kv_dtype=torch.bfloat16, H_kv=8, group_corr=0.95, seed=SEED_BASE + 5,
         note="grouped heads (4 query heads per key/value head), union loading"),
+    "gqa8_b16_h64kv8_d128_t128k_bf16": Workload(
+        "gqa8_b16_h64kv8_d128_t128k_bf16", B=16, H=64, d=128, T=131072,
+        kv_dtype=torch.bfloat16, H_kv=8, group_corr=0.95, seed=SEED_BASE + 7,
+        note="eight query heads per key/value head (a 70B-class layer), union loading"),
     "paged_b64_h16_d128_t128k_bf16": Workload(
         "paged_b64_h16_d128_t128k_bf16", B=64, H=16, d=128, T=131072,
         kv_dtype=torch.bfloat16, var_len=0.5, paged=True, seed=SEED_BASE + 6,
