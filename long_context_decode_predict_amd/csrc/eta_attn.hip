@@ -24,9 +24,11 @@
 //   - dot products reduce over the 16 lanes of a DPP row; the gated logits of
 //     a whole tile are formed first, so the running (max, sum, weighted V)
 //     state is rescaled once per tile, not per token.
-// With grouped heads (G > 1) the per-row dot products are reduce-scattered
-// instead (attn_item_dist): each lane ends with whole (head, row) pairs and the
-// gate and softmax weight are evaluated once per pair, not on all 16 lanes.
+// With grouped heads (G > 1) q.K and P.V are dense products over the G heads:
+// with bf16 K/V they run on the matrix cores (attn_item_mfma); with fp32 K/V
+// the per-row dot products are reduce-scattered (attn_item_dist) so each lane
+// ends with whole (head, row) pairs and the gate and softmax weight are
+// evaluated once per pair, not on all 16 lanes.
 // The waves' states merge in LDS. A one-item unit writes out/lse directly;
 // otherwise each item stores a (max, sum, weighted V) partial and the combine
 // kernel merges a unit's partials in item order with a log-sum-exp
@@ -365,6 +367,50 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Workgroup merge of one item for G heads: every wave has left its (max, sum,
+// weighted V) state per head in sm; the states are combined in wave order and
+// either normalised into out/lse (a one-item unit) or stored as the item's
+// partial for the combine kernel.
+template <int D, int G>
+__device__ __forceinline__ void merge_heads(const AttnArgs &a, int u, int chunk, int nchunks,
+                                            AttnShared<D, G> &sm) {
+    const int tid = threadIdx.x;
+    for (int j = 0; j < G; ++j) {
+        float M_ = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) M_ = fmaxf(M_, sm.m[w][j]);
+        const float Mr = M_ == -INFINITY ? 0.f : M_;
+        float Lsum = 0.f;
+        float wgt[kAttnWaves];
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+            wgt[w] = fast_exp(sm.m[w][j] - Mr);
+            Lsum += sm.l[w][j] * wgt[w];
+        }
+        const size_t uq = (size_t)u * G + j;
+        if (tid < D) {
+            float O = 0.f;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) O += sm.o[w][j][tid] * wgt[w];
+            if (nchunks == 1) {
+                a.out[uq * D + tid] = Lsum > 0.f ? O / Lsum : 0.f;
+            } else {
+                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
+                a.ws_o[slot * D + tid] = O;
+            }
+        }
+        if (tid == 0) {
+            if (nchunks == 1) {
+                if (a.lse) a.lse[uq] = Lsum > 0.f ? M_ + __logf(Lsum) : -INFINITY;
+            } else {
+                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
+                a.ws_m[slot] = M_;
+                a.ws_l[slot] = Lsum;
+            }
+        }
+    }
+}
+
 template <typename KV, int D, int TS, bool HARD, int G>
 __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chunk,
                                                AttnShared<D, G> &sm) {
@@ -539,40 +585,253 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
     }
     __syncthreads();
 
-    for (int j = 0; j < G; ++j) {
-        float M_ = -INFINITY;
+    merge_heads<D, G>(a, u, chunk, nchunks, sm);
+}
+
+// ---- grouped heads on the matrix cores (bf16 K/V) ----
+//
+// With G query heads per key/value unit, q.K over a tile is a dense
+// [tokens x d] x [d x G] product and P.V a [G x tokens] x [tokens x d] one, so
+// both run on the 16x16x32 bf16 MFMA (A: lane l holds row l%16, k-slots
+// 8*(l/16) + [0, 8); B: column l%16, the same k-slots; D: column l%16, rows
+// 4*(l/16) + [0, 4)). K and V enter as stored. The fp32 operands (scaled
+// queries, softmax weights) are split into a bf16 value and a bf16 residual
+// (x - hi, exact in fp32), which sit in columns [0, G) and [8, 8 + G) of the
+// same B operand: one MFMA forms both partial products and a DPP rotation of
+// each row by 8 lanes adds them. A query keeps a third bf16 term (the residual
+// of the residual, columns [0, G) of a second operand, accumulated into the
+// same logits), so a logit is exact to about 2^-26 of its terms: close to fp32
+// arithmetic, which the hard gate's step at tau needs; a weight's two terms
+// leave about 2^-17 of it.
+//
+// A wave's tile is 32 tokens, in two halves of 16. Lane (g, n) = (lane/16,
+// lane%16):
+//   q.K: it loads 16 bytes of token 16h + n at element 32kc + 8g (A operand of
+//     half h, k-step kc), holds query column n at the same elements (B), and
+//     receives the logits of tokens 16h + 4g + i (i < 4) for column n.
+//   So it owns, per column, the tokens tok(g, j) = 4g + j for j < 4 and
+//     16 + 4g + j - 4 for j >= 4: exactly k-slots 8g + j of the P.V product's
+//     B operand, which therefore needs no data movement.
+//   P.V: one MFMA per e < EPL = d/16, A row n <-> element EPL*n + e. The lane
+//     loads elements [EPL*n, EPL*n + EPL) of its eight tokens (16 lanes read a
+//     whole row per load), transposes them in registers with v_perm, and
+//     accumulates elements EPL*(4g + i) + e of column n.
+// Columns n and n + 8 hold the same head's logits after the rotation, so both
+// evaluate the same gate and weight; the value lane keeps the rounded weight,
+// the residual lane the remainder.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRowRor8 = 0x128;  // DPP row_ror:8: lane n of a row reads lane (n + 8) % 16
+
+// Round-to-nearest-even bf16 of a pair, packed (x0 in the low half).
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+}
+// The bf16 value of a pair (sel = 0) or its residual x - value (sel = 1).
+__device__ __forceinline__ uint32_t split_pair(float x0, float x1, float sel) {
+    const uint32_t h = pack_bf16(x0, x1);
+    return pack_bf16(fmaf(-sel, bf16_lo(h), x0), fmaf(-sel, bf16_hi(h), x1));
+}
+// Three-term split of a pair: x = v + r + t to about 2^-26 |x|; `main` gets v
+// (sel = 0) or r (sel = 1), `third` gets t where sel = 0 and zero elsewhere.
+__device__ __forceinline__ void split3_pair(float x0, float x1, float sel, uint32_t &main,
+                                            uint32_t &third) {
+    const uint32_t v = pack_bf16(x0, x1);
+    const float r0 = x0 - bf16_lo(v), r1 = x1 - bf16_hi(v);
+    const uint32_t r = pack_bf16(r0, r1);
+    main = sel != 0.f ? r : v;
+    third = sel != 0.f ? 0u : pack_bf16(r0 - bf16_lo(r), r1 - bf16_hi(r));
+}
+// Element e of a bf16 row held in registers, as the 32-bit word holding it.
+__device__ __forceinline__ uint32_t row_word(const RowLoad<uint16_t, 8> &r, int w) {
+    return w == 0 ? r.raw.x : w == 1 ? r.raw.y : w == 2 ? r.raw.z : r.raw.w;
+}
+__device__ __forceinline__ uint32_t row_word(const RowLoad<uint16_t, 4> &r, int w) {
+    return w == 0 ? r.raw.x : r.raw.y;
+}
+
+template <int D, bool HARD, int G>
+__device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chunk,
+                                               AttnShared<D, G> &sm) {
+    constexpr int KC = D / 32;   // k-steps of q.K per half tile
+    constexpr int EPL = D / 16;  // V elements per lane and token = P.V MFMAs per tile
+    constexpr int TT = 32;       // tokens per tile
+    constexpr int TPB = kBlockTokens / TT;
+    static_assert(G >= 2 && G <= 8, "two operand columns per head");
+    using VRow = RowLoad<uint16_t, EPL>;
+    const int c = a.cnt[u];
+    const int nchunks = (c + a.split - 1) / a.split;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    const int head = n & 7;
+    const bool live = head < G;
+    const float sel = n >= 8 ? 1.f : 0.f;  // residual column
+
+    bf16x8 qb[KC], qt[KC];  // query columns: value / residual, and the third terms
+    {
+        const float *qh = a.q + ((size_t)u * G + (live ? head : 0)) * D + 8 * g;
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) M_ = fmaxf(M_, sm.m[w][j]);
-        const float Mr = M_ == -INFINITY ? 0.f : M_;
-        float Lsum = 0.f;
-        float wgt[kAttnWaves];
+        for (int kc = 0; kc < KC; ++kc) {
+            float x[8];
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
-            wgt[w] = fast_exp(sm.m[w][j] - Mr);
-            Lsum += sm.l[w][j] * wgt[w];
-        }
-        const size_t uq = (size_t)u * G + j;
-        if (tid < D) {
-            float O = 0.f;
-#pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) O += sm.o[w][j][tid] * wgt[w];
-            if (nchunks == 1) {
-                a.out[uq * D + tid] = Lsum > 0.f ? O / Lsum : 0.f;
-            } else {
-                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
-                a.ws_o[slot * D + tid] = O;
-            }
-        }
-        if (tid == 0) {
-            if (nchunks == 1) {
-                if (a.lse) a.lse[uq] = Lsum > 0.f ? M_ + __logf(Lsum) : -INFINITY;
-            } else {
-                const size_t slot = ((size_t)u * a.ws_chunks + chunk) * G + j;
-                a.ws_m[slot] = M_;
-                a.ws_l[slot] = Lsum;
-            }
+            for (int e = 0; e < 8; ++e) x[e] = live ? qh[32 * kc + e] * a.s : 0.f;
+            uint4 w, t;
+            split3_pair(x[0], x[1], sel, w.x, t.x);
+            split3_pair(x[2], x[3], sel, w.y, t.y);
+            split3_pair(x[4], x[5], sel, w.z, t.z);
+            split3_pair(x[6], x[7], sel, w.w, t.w);
+            qb[kc] = __builtin_bit_cast(bf16x8, w);
+            qt[kc] = __builtin_bit_cast(bf16x8, t);
         }
     }
+    const float t_own = live ? a.tau[(size_t)u * G + head] : 0.f;
+    const float nbt_own = -a.nbl2e * t_own;
+
+    const uint16_t *Kp = static_cast<const uint16_t *>(a.K);
+    const uint16_t *Vp = static_cast<const uint16_t *>(a.V);
+    const int rb = u / a.lay.H_kv;
+    const int kh = u - rb * a.lay.H_kv;
+    const int Tb = a.lay.row_len(rb);
+    const int k_off = n * D + 8 * g;        // + 16*D*h + 32*kc
+    const int v_off = 4 * g * D + EPL * n;  // + (j + (j >= 4 ? 12 : 0)) * D
+    const int32_t *iu = a.idx + (size_t)u * a.nblk_cap;
+
+    const int j0 = chunk * a.split;
+    const int j1 = min(c, j0 + a.split);
+    const int nb = (j1 - j0 - wave + kAttnWaves - 1) / kAttnWaves;
+    const int ntiles = nb > 0 ? nb * TPB : 0;
+
+    auto tile_at = [&](int tt, size_t &off, int &valid) {
+        const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
+        const long long bo = a.lay.block_offset(rb, kh, blk, D);
+        const int sub = (tt % TPB) * TT;
+        off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * D;
+        valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;  // column n's head, over this lane's tokens
+    f32x4 o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    uint4 kr[2][KC];
+    VRow vr[8];
+    size_t next_off = 0;
+    int next_valid = 0;
+    if (ntiles > 0) {
+        tile_at(0, next_off, next_valid);
+        const uint16_t *p = Kp + next_off + k_off;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                kr[h][kc] = *reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc);
+    }
+    for (int tt = 0; tt < ntiles; ++tt) {
+        const size_t base = next_off;
+        const int valid = next_valid;
+        {
+            const uint16_t *p = Vp + base + v_off;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vr[j].load(p + (j + (j >= 4 ? 12 : 0)) * D);
+        }
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const bf16x8 k0 = __builtin_bit_cast(bf16x8, kr[0][kc]);
+            const bf16x8 k1 = __builtin_bit_cast(bf16x8, kr[1][kc]);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[kc], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[kc], s1, 0, 0, 0);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qt[kc], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qt[kc], s1, 0, 0, 0);
+        }
+        // the K registers are free: start the next tile's K loads
+        if (tt + 1 < ntiles) {
+            tile_at(tt + 1, next_off, next_valid);
+            const uint16_t *p = Kp + next_off + k_off;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc)
+                    kr[h][kc] = *reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc);
+        }
+        // logits of tok(g, j) for column n: value (+ third) part + residual part
+        float gv[8];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float part = j < 4 ? s0[j] : s1[j - 4];
+            const float S = part + dpp_for_add<kRowRor8>(part);
+            float gt;
+            if (HARD) {
+                gt = S >= t_own ? S : 0.f;
+            } else {
+                gt = S * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(a.nbl2e, S, nbt_own)));
+            }
+            if (4 * g + j + (j >= 4 ? 12 : 0) >= valid) gt = -INFINITY;
+            gv[j] = gt;
+            bmax = fmaxf(bmax, gt);
+        }
+        bmax = xrow_max(bmax);  // over the four lane rows: the tile's 32 tokens
+        const float mx = fmaxf(m_run, bmax);
+        const float m_ref = mx == -INFINITY ? 0.f : mx;  // nothing visible yet: weights 0
+        const float corr = fast_exp(m_run - m_ref);
+        m_run = mx;
+        l_run *= corr;
+        float pw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pw[j] = fast_exp(gv[j] - m_ref);
+            l_run += pw[j];
+        }
+        const uint4 pwb = make_uint4(split_pair(pw[0], pw[1], sel), split_pair(pw[2], pw[3], sel),
+                                     split_pair(pw[4], pw[5], sel), split_pair(pw[6], pw[7], sel));
+        const bf16x8 pB = __builtin_bit_cast(bf16x8, pwb);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[e] *= corr;
+        if (valid < TT) {  // rows past the row's length hold arbitrary bits
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (4 * g + j + (j >= 4 ? 12 : 0) >= valid) zero_row<uint16_t, EPL>(vr[j]);
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const uint32_t sel_b = (e & 1) ? 0x07060302u : 0x05040100u;
+            const uint4 w = make_uint4(
+                __builtin_amdgcn_perm(row_word(vr[1], e / 2), row_word(vr[0], e / 2), sel_b),
+                __builtin_amdgcn_perm(row_word(vr[3], e / 2), row_word(vr[2], e / 2), sel_b),
+                __builtin_amdgcn_perm(row_word(vr[5], e / 2), row_word(vr[4], e / 2), sel_b),
+                __builtin_amdgcn_perm(row_word(vr[7], e / 2), row_word(vr[6], e / 2), sel_b));
+            o[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pB, o[e],
+                                                           0, 0, 0);
+        }
+    }
+
+    // value + residual columns; then lane (g, n < G) holds elements
+    // EPL*(4g + i) + e of head n
+    const float l_head = xrow_sum(l_run);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[e][i] += dpp_for_add<kRowRor8>(o[e][i]);
+    if (n < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sm.o[wave][n][EPL * (4 * g + i) + e] = o[e][i];
+        if (g == 0) {
+            sm.m[wave][n] = m_run;
+            sm.l[wave][n] = l_head;
+        }
+    }
+    __syncthreads();
+    merge_heads<D, G>(a, u, chunk, nchunks, sm);
 }
 
 // Persistent workers: each workgroup takes item tickets until the list is done.
@@ -587,9 +846,11 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
         const int2 it = a.ws_items[ticket];
         int next = 0;
         if (threadIdx.x == 0) next = atomicAdd(&a.ws_hdr[1], 1);  // fetched early
-        if constexpr (G > 1) {  // multi-head attention keeps the one-pass row layout
+        if constexpr (G > 1 && sizeof(KV) == 2) {  // grouped heads, bf16: matrix cores
+            attn_item_mfma<D, HARD, G>(a, it.x, it.y, sm);
+        } else if constexpr (G > 1) {  // grouped heads, fp32: reduce-scatter on the VALU
             attn_item_dist<KV, D, TS, HARD, G>(a, it.x, it.y, sm);
-        } else {
+        } else {  // multi-head attention: the one-pass row layout
             attn_item<KV, D, TS, HARD, G>(a, it.x, it.y, sm);
         }
         if (threadIdx.x == 0) sm.ticket = next;

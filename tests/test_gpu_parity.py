@@ -153,6 +153,12 @@ GQA = [
                               seed=96), "predictor", {"gate_hard": 1}),
     ("g8_f32_d128", dict(B=2, H=8, H_kv=1, d=128, T=1100, kv_dtype=torch.float32,
                          group_corr=0.7, seed=100), "predictor", {}),
+    ("g4_bf16_d128_hard", dict(B=2, H=8, H_kv=2, d=128, T=2500, kv_dtype=torch.bfloat16,
+                               group_corr=0.9, seed=101), "predictor", {"gate_hard": 1}),
+    ("g8_bf16_d64_hard", dict(B=1, H=16, H_kv=2, d=64, T=1800, kv_dtype=torch.bfloat16,
+                              seed=102), "predictor", {"gate_hard": 1}),
+    ("g2_bf16_d128_beta20", dict(B=2, H=4, H_kv=2, d=128, T=2200, kv_dtype=torch.bfloat16,
+                                 seed=103), "predictor", {"gate_beta": 20.0}),
     ("g4_static", dict(B=2, H=16, H_kv=4, d=128, T=4096, kv_dtype=torch.bfloat16,
                        sigma_range=(0.1, 0.6), head_densities=tuple(0.1 + 0.05 * h for h in range(16)),
                        seed=97), "static", {}),
