@@ -55,6 +55,7 @@ struct ScreenArgs {
     KVLayout lay;  // per-row token counts (the K/V addresses are not used here)
     int32_t *uni_idx;  // grouped heads: union per key/value unit (null: not formed here)
     int32_t *uni_cnt;
+    int w_vec;         // W is 16-byte aligned and H % 4 == 0 (rows of W load as float4)
 };
 
 template <int D, bool PRED>
@@ -217,7 +218,7 @@ template <int D, bool PRED, int G>
 __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(ScreenArgs a) {
     __shared__ float q_s[G][D];
     __shared__ int wave_tot[G + 1][kScreenMaxWaves];  // per head, then the union
-    __shared__ float red[kScreenMaxWaves];
+    __shared__ float red[G][kScreenMaxWaves];
     __shared__ float tau_s[G];
 
     const int ukv = blockIdx.x;  // key/value unit; its query units are ukv*G + j
@@ -229,25 +230,52 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
 
     for (int i = threadIdx.x; i < G * D; i += blockDim.x) q_s[i / D][i % D] = a.q[(size_t)u0 * D + i];
     if (PRED) {
-        for (int j = 0; j < G; ++j) {
-            const int h = (u0 + j) - b * a.H;
-            float acc = 0.f;
-            if (a.W != nullptr) {
-                const float *qb = a.q + (size_t)b * a.H * D;
-                for (int k = threadIdx.x; k < a.H * D; k += blockDim.x) acc += qb[k] * a.W[(size_t)k * a.H + h];
+        // the group's G heads are G adjacent columns of W: one pass over W's rows
+        // reads each row's G entries together (one 16-byte load per 4 heads)
+        const int h0 = u0 - b * a.H;
+        float acc[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc[j] = 0.f;
+        if (a.W != nullptr) {
+            const float *qb = a.q + (size_t)b * a.H * D;
+            const int HD = a.H * D;
+            if (G % 4 == 0 && a.w_vec) {
+                for (int k = threadIdx.x; k < HD; k += blockDim.x) {
+                    const float qv = qb[k];
+                    const float4 *wr = reinterpret_cast<const float4 *>(a.W + (size_t)k * a.H + h0);
+#pragma unroll
+                    for (int j4 = 0; j4 < G / 4; ++j4) {
+                        const float4 w4 = wr[j4];
+                        acc[4 * j4 + 0] += qv * w4.x;
+                        acc[4 * j4 + 1] += qv * w4.y;
+                        acc[4 * j4 + 2] += qv * w4.z;
+                        acc[4 * j4 + 3] += qv * w4.w;
+                    }
+                }
+            } else {
+                for (int k = threadIdx.x; k < HD; k += blockDim.x) {
+                    const float qv = qb[k];
+                    const float *wr = a.W + (size_t)k * a.H + h0;
+#pragma unroll
+                    for (int j = 0; j < G; ++j) acc[j] += qv * wr[j];
+                }
             }
-            acc = xrow_sum(row_sum16(acc));
-            if (lane == 0) red[wave] = acc;
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                float sum = 0.f;
-                for (int w = 0; w < nw; ++w) sum += red[w];
-                const float t = a.bias[h] + sum;
-                tau_s[j] = t;
-                a.tau[u0 + j] = t;
-            }
-            __syncthreads();  // red is reused by the next head
         }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float r = xrow_sum(row_sum16(acc[j]));
+            if (lane == 0) red[j][wave] = r;
+        }
+        __syncthreads();
+        if (threadIdx.x < G) {
+            const int j = threadIdx.x;
+            float sum = 0.f;
+            for (int w = 0; w < nw; ++w) sum += red[j][w];
+            const float t = a.bias[h0 + j] + sum;
+            tau_s[j] = t;
+            a.tau[u0 + j] = t;
+        }
+        __syncthreads();
     } else {
         if (threadIdx.x < G) tau_s[threadIdx.x] = a.tau[u0 + threadIdx.x];
         __syncthreads();
@@ -430,6 +458,7 @@ hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau,
     a.lay = g.lay;
     a.uni_idx = g.G > 1 ? uni_idx : nullptr;
     a.uni_cnt = g.G > 1 ? uni_cnt : nullptr;
+    a.w_vec = (W != nullptr && reinterpret_cast<uintptr_t>(W) % 16 == 0 && H % 4 == 0) ? 1 : 0;
     if (g.G > 1) {
         int nw = (g.nblk + kBlocksPerWave - 1) / kBlocksPerWave;
         nw = nw < 1 ? 1 : (nw > kScreenMaxWaves ? kScreenMaxWaves : nw);

@@ -191,6 +191,43 @@ def test_parity_grouped_heads(name, kw, mode, pkw, fused):
     case.free()
 
 
+def test_grouped_predictor_unaligned_W():
+    """The fused grouped screen reads the G predictor columns of a row of W with
+    16-byte loads when W is 16-byte aligned and one float at a time otherwise: the
+    same products summed in the same order, so tau, the lists and the union are
+    bitwise equal, and tau matches the oracle's Eq. 1."""
+    _announce("gqa unaligned W")
+    w = workloads.custom("uw", B=2, H=16, H_kv=2, d=128, T=3000, kv_dtype=torch.bfloat16,
+                         group_corr=0.9, seed=104)
+    case = Case(w, fused=True).run()
+    n = _lib.nblk_cap(case.T_cap)
+
+    def screen(Wt):
+        r = dict(tau=torch.empty((w.B, w.H), device="cuda"),
+                 idx=torch.full((w.B, w.H, n), -1, dtype=torch.int32, device="cuda"),
+                 cnt=torch.empty((w.B, w.H), dtype=torch.int32, device="cuda"),
+                 uidx=torch.full((w.B, w.kv_heads, n), -1, dtype=torch.int32, device="cuda"),
+                 ucnt=torch.empty((w.B, w.kv_heads), dtype=torch.int32, device="cuda"))
+        _lib.eta_predict_screen_union(case.data["q"], Wt, case.bias, case.meta, w.T, case.T_cap,
+                                      case.params, r["tau"], r["idx"], r["cnt"], r["uidx"],
+                                      r["ucnt"], kv_dtype=w.kv_dtype)
+        torch.cuda.synchronize()
+        return r
+
+    aligned = screen(case.W)
+    buf = torch.empty(case.W.numel() + 1, device="cuda")
+    Wu = buf[1:].view_as(case.W)
+    Wu.copy_(case.W)
+    assert Wu.data_ptr() % 16 != 0
+    unaligned = screen(Wu)
+    for k in aligned:
+        assert torch.equal(aligned[k], unaligned[k]), k
+    O = oracle_mod.default()
+    tau_o = O.predict_tau(case.data["q"].cpu().numpy(), case.W.cpu().numpy(), case.bias.cpu().numpy())
+    assert np.max(np.abs(aligned["tau"].cpu().numpy() - tau_o)) <= 1e-5
+    case.free()
+
+
 def test_dense_matches_library_sdpa():
     """tau = -inf through the HIP path equals torch's softmax attention (CPU, float64)."""
     _announce("dense vs sdpa")
