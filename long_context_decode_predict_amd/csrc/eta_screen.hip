@@ -37,6 +37,8 @@ constexpr int kScreenMaxWaves = 16;
 constexpr int kBlocksPerLane = 4;
 constexpr int kBlocksPerWave = kWave * kBlocksPerLane;
 constexpr int kMaxSlices = 8;
+constexpr int kDimBatch = 4;  // grouped screen: centroid dimensions loaded per batch
+constexpr int kGroupMaxWaves = 8;  // grouped screen: waves per workgroup (registers for G heads)
 
 struct ScreenArgs {
     int nblk, nblk_cap, H, G, nbg, ds;  // query heads per KV head, block groups, slices
@@ -119,14 +121,33 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
         const bool active = blk0 < nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         if (active && !a.geo_only) {
-#pragma unroll 16
-            for (int dim = d0; dim < d0 + dps; ++dim) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(cu + (size_t)dim * a.nblk_cap + blk0);
-                const float qd = q_s[dim];
-                acc[0] += qd * c4.x;
-                acc[1] += qd * c4.y;
-                acc[2] += qd * c4.z;
-                acc[3] += qd * c4.w;
+            // batches of kDimBatch dimensions (dps is a multiple of 8), the next
+            // batch's loads in flight while the current one is used
+            const float *cp = cu + (size_t)d0 * a.nblk_cap + blk0;
+            const size_t st = a.nblk_cap;
+            const int nbt = dps / kDimBatch;
+            float4 cb[2][kDimBatch];
+            auto load = [&](float4(&dst)[kDimBatch], int bt) {
+#pragma unroll
+                for (int i = 0; i < kDimBatch; ++i)
+                    dst[i] = *reinterpret_cast<const float4 *>(cp + (size_t)(bt * kDimBatch + i) * st);
+            };
+            auto use = [&](const float4(&src)[kDimBatch], int bt) {
+#pragma unroll
+                for (int i = 0; i < kDimBatch; ++i) {
+                    const float qd = q_s[d0 + bt * kDimBatch + i];
+                    acc[0] += qd * src[i].x;
+                    acc[1] += qd * src[i].y;
+                    acc[2] += qd * src[i].z;
+                    acc[3] += qd * src[i].w;
+                }
+            };
+            load(cb[0], 0);
+            for (int bt = 0; bt < nbt; bt += 2) {  // nbt is even
+                load(cb[1], bt + 1);
+                use(cb[0], bt);
+                if (bt + 2 < nbt) load(cb[0], bt + 2);
+                use(cb[1], bt + 1);
             }
         }
         if (a.ds > 1) {  // add the slices' partial dots in slice order
@@ -215,10 +236,10 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
 // asked, the union of the G lists is compacted the same way from the OR of the
 // heads' admission bits.
 template <int D, bool PRED, int G>
-__global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(ScreenArgs a) {
+__global__ __launch_bounds__(kGroupMaxWaves *kWave) void screen_group_kernel(ScreenArgs a) {
     __shared__ float q_s[G][D];
-    __shared__ int wave_tot[G + 1][kScreenMaxWaves];  // per head, then the union
-    __shared__ float red[G][kScreenMaxWaves];
+    __shared__ int wave_tot[G + 1][kGroupMaxWaves];  // per head, then the union
+    __shared__ float red[G][kGroupMaxWaves];
     __shared__ float tau_s[G];
 
     const int ukv = blockIdx.x;  // key/value unit; its query units are ukv*G + j
@@ -240,6 +261,7 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
             const float *qb = a.q + (size_t)b * a.H * D;
             const int HD = a.H * D;
             if (G % 4 == 0 && a.w_vec) {
+#pragma unroll 4
                 for (int k = threadIdx.x; k < HD; k += blockDim.x) {
                     const float qv = qb[k];
                     const float4 *wr = reinterpret_cast<const float4 *>(a.W + (size_t)k * a.H + h0);
@@ -253,6 +275,7 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
                     }
                 }
             } else {
+#pragma unroll 4
                 for (int k = threadIdx.x; k < HD; k += blockDim.x) {
                     const float qv = qb[k];
                     const float *wr = a.W + (size_t)k * a.H + h0;
@@ -310,16 +333,33 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_group_kernel(Sc
 #pragma unroll
         for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
         if (active && !a.geo_only) {
-#pragma unroll 8
-            for (int dim = 0; dim < D; ++dim) {
-                const float4 c4 = *reinterpret_cast<const float4 *>(cu + (size_t)dim * a.nblk_cap + blk0);
+            // centroid rows in batches of kDimBatch dimensions, the next batch's loads
+            // in flight while the current one is used
+            const float *cp = cu + blk0;
+            const size_t st = a.nblk_cap;
+            float4 cb[2][kDimBatch];
 #pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    const float qd = q_s[j][dim];
-                    acc[j][0] += qd * c4.x;
-                    acc[j][1] += qd * c4.y;
-                    acc[j][2] += qd * c4.z;
-                    acc[j][3] += qd * c4.w;
+            for (int i = 0; i < kDimBatch; ++i) cb[0][i] = *reinterpret_cast<const float4 *>(cp + i * st);
+#pragma unroll
+            for (int bt = 0; bt < D / kDimBatch; ++bt) {
+                const int cur = bt & 1;
+                if (bt + 1 < D / kDimBatch) {
+#pragma unroll
+                    for (int i = 0; i < kDimBatch; ++i)
+                        cb[cur ^ 1][i] = *reinterpret_cast<const float4 *>(
+                            cp + (size_t)((bt + 1) * kDimBatch + i) * st);
+                }
+#pragma unroll
+                for (int i = 0; i < kDimBatch; ++i) {
+                    const float4 c4 = cb[cur][i];
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {
+                        const float qd = q_s[j][bt * kDimBatch + i];
+                        acc[j][0] += qd * c4.x;
+                        acc[j][1] += qd * c4.y;
+                        acc[j][2] += qd * c4.z;
+                        acc[j][3] += qd * c4.w;
+                    }
                 }
             }
         }
@@ -461,7 +501,7 @@ hipError_t launch_screen_t(const Geometry &g, int H, const float *q, float *tau,
     a.w_vec = (W != nullptr && reinterpret_cast<uintptr_t>(W) % 16 == 0 && H % 4 == 0) ? 1 : 0;
     if (g.G > 1) {
         int nw = (g.nblk + kBlocksPerWave - 1) / kBlocksPerWave;
-        nw = nw < 1 ? 1 : (nw > kScreenMaxWaves ? kScreenMaxWaves : nw);
+        nw = nw < 1 ? 1 : (nw > kGroupMaxWaves ? kGroupMaxWaves : nw);
         const dim3 grid((unsigned)g.kv_units), blk(nw * kWave);
 #define ETA_SCREEN_GROUP(GG)                                                                   \
     if (predict) {                                                                             \
