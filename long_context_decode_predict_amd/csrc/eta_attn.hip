@@ -731,7 +731,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                kr[h][kc] = *reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc);
+                kr[h][kc] = ld_stream(reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc));
     }
     for (int tt = 0; tt < ntiles; ++tt) {
         const size_t base = next_off;
@@ -759,7 +759,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc)
-                    kr[h][kc] = *reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc);
+                    kr[h][kc] = ld_stream(reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc));
         }
         // logits of tok(g, j) for column n: value (+ third) part + residual part
         float gv[8];

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
             auto load = [&](float4(&dst)[kDimBatch], int bt) {
 #pragma unroll
                 for (int i = 0; i < kDimBatch; ++i)
-                    dst[i] = *reinterpret_cast<const float4 *>(cp + (size_t)(bt * kDimBatch + i) * st);
+                    dst[i] = ld_stream(reinterpret_cast<const float4 *>(cp + (size_t)(bt * kDimBatch + i) * st));
             };
             auto use = [&](const float4(&src)[kDimBatch], int bt) {
 #pragma unroll
@@ -174,13 +174,13 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
         int before = 0;
         if (slice == 0) {
             if (active) {
-                const float4 m4 = *reinterpret_cast<const float4 *>(mu + blk0);
+                const float4 m4 = ld_stream(reinterpret_cast<const float4 *>(mu + blk0));
                 const float mx[4] = {m4.x, m4.y, m4.z, m4.w};
                 if (a.geo_only) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) U[j] = geo_scale * mx[j];
                 } else {
-                    const float4 v4 = *reinterpret_cast<const float4 *>(vu + blk0);
+                    const float4 v4 = ld_stream(reinterpret_cast<const float4 *>(vu + blk0));
                     const float vx[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -339,15 +339,15 @@ __global__ __launch_bounds__(kGroupMaxWaves *kWave) void screen_group_kernel(Scr
             const size_t st = a.nblk_cap;
             float4 cb[2][kDimBatch];
 #pragma unroll
-            for (int i = 0; i < kDimBatch; ++i) cb[0][i] = *reinterpret_cast<const float4 *>(cp + i * st);
+            for (int i = 0; i < kDimBatch; ++i) cb[0][i] = ld_stream(reinterpret_cast<const float4 *>(cp + i * st));
 #pragma unroll
             for (int bt = 0; bt < D / kDimBatch; ++bt) {
                 const int cur = bt & 1;
                 if (bt + 1 < D / kDimBatch) {
 #pragma unroll
                     for (int i = 0; i < kDimBatch; ++i)
-                        cb[cur ^ 1][i] = *reinterpret_cast<const float4 *>(
-                            cp + (size_t)((bt + 1) * kDimBatch + i) * st);
+                        cb[cur ^ 1][i] = ld_stream(reinterpret_cast<const float4 *>(
+                            cp + (size_t)((bt + 1) * kDimBatch + i) * st));
                 }
 #pragma unroll
                 for (int i = 0; i < kDimBatch; ++i) {
@@ -365,10 +365,10 @@ __global__ __launch_bounds__(kGroupMaxWaves *kWave) void screen_group_kernel(Scr
         }
         float mx[4] = {0.f, 0.f, 0.f, 0.f}, vx[4] = {0.f, 0.f, 0.f, 0.f};
         if (active) {
-            const float4 m4 = *reinterpret_cast<const float4 *>(mu + blk0);
+            const float4 m4 = ld_stream(reinterpret_cast<const float4 *>(mu + blk0));
             mx[0] = m4.x; mx[1] = m4.y; mx[2] = m4.z; mx[3] = m4.w;
             if (!a.geo_only) {
-                const float4 v4 = *reinterpret_cast<const float4 *>(vu + blk0);
+                const float4 v4 = ld_stream(reinterpret_cast<const float4 *>(vu + blk0));
                 vx[0] = v4.x; vx[1] = v4.y; vx[2] = v4.z; vx[3] = v4.w;
             }
         }
