@@ -116,8 +116,9 @@ typedef struct {
     int gate_hard;      /* 1: gate is the step S >= tau instead of the sigmoid */
     int bound_mode;     /* eta_bound_mode; default ETA_BOUND_COMBINED          */
     int split_blocks;   /* admitted blocks per split-KV work item (1..4096);
-                           0 = library default (8 with multi-head attention,
-                           16 with grouped heads)                              */
+                           0 = library default, 8 per query head of a
+                           key/value unit: 8 * G (8 with multi-head attention,
+                           32 with G = 4); see eta_split_blocks              */
 } eta_params;
 
 /* Defaults: beta = 5 (the end of the 1 -> 5 anneal of Eq. 2), z = 4, soft
@@ -128,6 +129,11 @@ eta_params eta_default_params(void);
  * a cache of T_cap tokens: ceil(T_cap / 64) rounded up to a multiple of 4
  * (0 if T_cap < 1). */
 int eta_nblk_cap(int T_cap);
+
+/* The split-KV item length the attention calls use for this shape and these
+ * parameters: p->split_blocks if nonzero, else the default 8 * G. Returns 0 if
+ * s or p is null or p->split_blocks is out of range. Host-only, no GPU work. */
+int eta_split_blocks(const eta_shape *s, const eta_params *p);
 
 /* Human-readable name of a status code (static storage). */
 const char *eta_status_string(eta_status st);

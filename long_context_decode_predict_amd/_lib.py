@@ -67,6 +67,7 @@ _lib = None
 SIGNATURES = {
     "eta_default_params": (eta_params, []),
     "eta_nblk_cap": (ctypes.c_int, [ctypes.c_int]),
+    "eta_split_blocks": (ctypes.c_int, [_P(eta_shape), _P(eta_params)]),
     "eta_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "eta_build_block_meta": (ctypes.c_int, [_P(eta_shape), _vp, _P(eta_meta), _vp]),
     "eta_append_meta": (ctypes.c_int, [_P(eta_shape), ctypes.c_int, _vp, _P(eta_meta), _vp]),
@@ -152,6 +153,12 @@ def kv_code(dtype: torch.dtype) -> int:
 
 def nblk_cap(T_cap: int) -> int:
     return int(lib().eta_nblk_cap(int(T_cap)))
+
+
+def split_blocks(H: int, H_kv: int, params: "eta_params") -> int:
+    """The split-KV item length the library uses (eta_split_blocks)."""
+    s = eta_shape(1, int(H), 128, 64, 64, BLOCK, 1, int(H_kv))
+    return int(lib().eta_split_blocks(ctypes.byref(s), ctypes.byref(params)))
 
 
 @dataclass

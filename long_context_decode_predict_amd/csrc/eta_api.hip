@@ -15,8 +15,10 @@ constexpr int kBlock = 64;
 // Default blocks per split-KV work item: smaller items balance the persistent
 // workers better under multi-head attention; with grouped heads an item already
 // carries G heads' work (and G partials), so larger items pay off there.
-constexpr int kDefaultSplitMHA = 8;
-constexpr int kDefaultSplitGrouped = 16;
+// Default split-KV item: 8 admitted blocks per query head of the key/value
+// unit, i.e. 8 * G (an item carries the state and partials of G heads, so its
+// fixed cost grows with G and so should its length).
+constexpr int kDefaultSplitPerHead = 8;
 constexpr int kMaxSplit = 4096;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -103,7 +105,9 @@ eta_status check_params(const eta_params *p) {
 
 int split_of(const eta_shape *s, const eta_params *p) {
     if (p->split_blocks != 0) return p->split_blocks;
-    return kv_heads_of(s) < s->H ? kDefaultSplitGrouped : kDefaultSplitMHA;
+    const int hkv = kv_heads_of(s);
+    const int G = (hkv > 0 && hkv < s->H) ? s->H / hkv : 1;
+    return kDefaultSplitPerHead * G;
 }
 
 eta_status from_hip(hipError_t e) { return e == hipSuccess ? ETA_OK : ETA_ERR_HIP; }
@@ -161,6 +165,11 @@ eta_params eta_default_params(void) {
 }
 
 int eta_nblk_cap(int T_cap) { return T_cap < 1 ? 0 : nblk_cap_of(T_cap); }
+
+int eta_split_blocks(const eta_shape *s, const eta_params *p) {
+    if (s == nullptr || p == nullptr || p->split_blocks < 0 || p->split_blocks > kMaxSplit) return 0;
+    return split_of(s, p);
+}
 
 const char *eta_status_string(eta_status st) {
     switch (st) {

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
@@ -43,6 +43,13 @@ def test_defaults_and_strings(L):
         assert _lib.status_string(st) == s
     assert [L.eta_nblk_cap(t) for t in (0, 1, 64, 65, 256, 257, 2048, 131072)] == \
         [0, 4, 4, 4, 4, 8, 32, 2048]
+    # split-KV item: 8 blocks per query head of a key/value unit unless given
+    d = L.eta_default_params()
+    assert [_lib.split_blocks(H, Hkv, d) for H, Hkv in ((16, 0), (16, 16), (8, 4), (32, 8),
+                                                        (64, 8))] == [8, 8, 16, 32, 64]
+    assert _lib.split_blocks(32, 8, _lib.default_params(split_blocks=5)) == 5
+    assert _lib.split_blocks(32, 8, _lib.default_params(split_blocks=-1)) == 0
+    assert L.eta_split_blocks(None, BY(d)) == 0
 
 
 def shape(**kw):
