@@ -235,7 +235,7 @@ def row_rooflines(w, lens, params, build_ms, front_ms, attn_ms, attn_alg, comb_m
     blocks_kv = units_kv * sum(nblk_rows)               # metadata entries
     meta_b = blocks_kv * (w.d + 2) * 4
     k_bytes = units_kv * sum(lens) * w.d * eb
-    split = _lib.split_blocks(w.H, w.kv_heads, params)
+    split = _lib.split_blocks(w.B, w.H, w.kv_heads, w.T_cap, params)
     items = np.ceil(ucnt / split)
     multi = items * (items > 1)
     comb_b = int(multi.sum()) * w.G * (w.d + 2) * 4 + int((items > 1).sum()) * w.G * w.d * 4
@@ -653,7 +653,7 @@ def main():
                    "tokens_cached": int(sum(lens)),
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",
-                   "split_blocks": _lib.split_blocks(w.H, w.kv_heads, params),
+                   "split_blocks": _lib.split_blocks(w.B, w.H, w.kv_heads, w.T_cap, params),
                    "gate": "hard" if params.gate_hard else "sigmoid", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "attn_partial_kernel", "achieved": attn_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,

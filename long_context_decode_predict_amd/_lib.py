@@ -155,9 +155,9 @@ def nblk_cap(T_cap: int) -> int:
     return int(lib().eta_nblk_cap(int(T_cap)))
 
 
-def split_blocks(H: int, H_kv: int, params: "eta_params") -> int:
+def split_blocks(B: int, H: int, H_kv: int, T_cap: int, params: "eta_params") -> int:
     """The split-KV item length the library uses (eta_split_blocks)."""
-    s = eta_shape(1, int(H), 128, 64, 64, BLOCK, 1, int(H_kv))
+    s = eta_shape(int(B), int(H), 128, 0, int(T_cap), BLOCK, 1, int(H_kv))
     return int(lib().eta_split_blocks(ctypes.byref(s), ctypes.byref(params)))
 
 

@@ -17,8 +17,11 @@ constexpr int kBlock = 64;
 // carries G heads' work (and G partials), so larger items pay off there.
 // Default split-KV item: 8 admitted blocks per query head of the key/value
 // unit, i.e. 8 * G (an item carries the state and partials of G heads, so its
-// fixed cost grows with G and so should its length).
+// fixed cost grows with G and so should its length), doubled for caches of at
+// least 2^20 unit blocks, where there are items enough to keep the grid busy
+// with longer ones.
 constexpr int kDefaultSplitPerHead = 8;
+constexpr long long kLongItemSlots = 1ll << 20;
 constexpr int kMaxSplit = 4096;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -107,7 +110,8 @@ int split_of(const eta_shape *s, const eta_params *p) {
     if (p->split_blocks != 0) return p->split_blocks;
     const int hkv = kv_heads_of(s);
     const int G = (hkv > 0 && hkv < s->H) ? s->H / hkv : 1;
-    return kDefaultSplitPerHead * G;
+    const long long slots = (long long)s->B * hkv * nblk_cap_of(s->T_cap);
+    return kDefaultSplitPerHead * G * (slots >= kLongItemSlots ? 2 : 1);
 }
 
 eta_status from_hip(hipError_t e) { return e == hipSuccess ? ETA_OK : ETA_ERR_HIP; }
