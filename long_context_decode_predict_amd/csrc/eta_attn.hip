@@ -86,11 +86,12 @@ __device__ __forceinline__ void zero_row<float, 8>(RowLoad<float, 8> &r) {
 template <>
 __device__ __forceinline__ void zero_row<float, 4>(RowLoad<float, 4> &r) { r.a = make_float4(0.f, 0.f, 0.f, 0.f); }
 
-template <int D, int G>
+template <int D, int G, bool KT = false>
 struct AttnShared {
     float m[kAttnWaves][G];
     float l[kAttnWaves][G];
     float o[kAttnWaves][G][D];
+    uint4 kt[KT ? kAttnWaves : 1][KT ? 4 * D : 1];  // matrix-core path: each wave's K tile
     int ticket;
 };
 
@@ -371,9 +372,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // weighted V) state per head in sm; the states are combined in wave order and
 // either normalised into out/lse (a one-item unit) or stored as the item's
 // partial for the combine kernel.
-template <int D, int G>
+template <int D, int G, typename SM>
 __device__ __forceinline__ void merge_heads(const AttnArgs &a, int u, int chunk, int nchunks,
-                                            AttnShared<D, G> &sm) {
+                                            SM &sm) {
     const int tid = threadIdx.x;
     for (int j = 0; j < G; ++j) {
         float M_ = -INFINITY;
@@ -606,9 +607,11 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
 //
 // A wave's tile is 32 tokens, in two halves of 16. Lane (g, n) = (lane/16,
 // lane%16):
-//   q.K: it loads 16 bytes of token 16h + n at element 32kc + 8g (A operand of
-//     half h, k-step kc), holds query column n at the same elements (B), and
-//     receives the logits of tokens 16h + 4g + i (i < 4) for column n.
+//   q.K: it reads 16 bytes of token 16h + n at element 32kc + 8g (A operand of
+//     half h, k-step kc) from the wave's LDS copy of the K tile (loaded whole
+//     rows at a time, so HBM sees full 128-byte lines per load), holds query
+//     column n at the same elements (B), and receives the logits of tokens
+//     16h + 4g + i (i < 4) for column n.
 //   So it owns, per column, the tokens tok(g, j) = 4g + j for j < 4 and
 //     16 + 4g + j - 4 for j >= 4: exactly k-slots 8g + j of the P.V product's
 //     B operand, which therefore needs no data movement.
@@ -655,7 +658,7 @@ __device__ __forceinline__ uint32_t row_word(const RowLoad<uint16_t, 4> &r, int 
 
 template <int D, bool HARD, int G>
 __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chunk,
-                                               AttnShared<D, G> &sm) {
+                                               AttnShared<D, G, true> &sm) {
     constexpr int KC = D / 32;   // k-steps of q.K per half tile
     constexpr int EPL = D / 16;  // V elements per lane and token = P.V MFMAs per tile
     constexpr int TT = 32;       // tokens per tile
@@ -698,7 +701,15 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     const int rb = u / a.lay.H_kv;
     const int kh = u - rb * a.lay.H_kv;
     const int Tb = a.lay.row_len(rb);
-    const int k_off = n * D + 8 * g;        // + 16*D*h + 32*kc
+    // K tile: loaded row by row (CPR lanes per token row, TPI rows per load), kept
+    // in this wave's LDS with 16-byte chunk c of token t at slot c ^ (t % CPR), and
+    // read back in the A-operand layout (both directions free of bank conflicts)
+    constexpr int CPR = D / 8;         // 16-byte chunks per token row
+    constexpr int TPI = kWave / CPR;   // token rows per load instruction
+    constexpr int NLD = TT / TPI;      // loads per tile
+    const int ld_tok = lane / CPR, ld_ch = lane % CPR;
+    const int k_off = ld_tok * D + ld_ch * 8;  // + TPI*D*i
+    uint4 *kt = sm.kt[wave];
     const int v_off = 4 * g * D + EPL * n;  // + (j + (j >= 4 ? 12 : 0)) * D
     const int32_t *iu = a.idx + (size_t)u * a.nblk_cap;
 
@@ -720,18 +731,23 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    uint4 kr[2][KC];
+    uint4 kr[NLD];
     VRow vr[8];
+    auto k_store = [&]() {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int t = i * TPI + ld_tok;
+            kt[t * CPR + (ld_ch ^ (t % CPR))] = kr[i];
+        }
+    };
     size_t next_off = 0;
     int next_valid = 0;
     if (ntiles > 0) {
         tile_at(0, next_off, next_valid);
         const uint16_t *p = Kp + next_off + k_off;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                kr[h][kc] = ld_stream(reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc));
+        for (int i = 0; i < NLD; ++i) kr[i] = ld_stream(reinterpret_cast<const uint4 *>(p + TPI * D * i));
+        k_store();
     }
     for (int tt = 0; tt < ntiles; ++tt) {
         const size_t base = next_off;
@@ -744,22 +760,21 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            const bf16x8 k0 = __builtin_bit_cast(bf16x8, kr[0][kc]);
-            const bf16x8 k1 = __builtin_bit_cast(bf16x8, kr[1][kc]);
+            const int c = 4 * kc + g;  // this lane's chunk of tokens n and 16 + n
+            const bf16x8 k0 = __builtin_bit_cast(bf16x8, kt[n * CPR + (c ^ (n % CPR))]);
+            const bf16x8 k1 = __builtin_bit_cast(bf16x8, kt[(16 + n) * CPR + (c ^ ((16 + n) % CPR))]);
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[kc], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[kc], s1, 0, 0, 0);
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qt[kc], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qt[kc], s1, 0, 0, 0);
         }
-        // the K registers are free: start the next tile's K loads
+        // the tile's K is read: start the next tile's K loads (into LDS at the end)
         if (tt + 1 < ntiles) {
             tile_at(tt + 1, next_off, next_valid);
             const uint16_t *p = Kp + next_off + k_off;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc)
-                    kr[h][kc] = ld_stream(reinterpret_cast<const uint4 *>(p + 16 * D * h + 32 * kc));
+            for (int i = 0; i < NLD; ++i)
+                kr[i] = ld_stream(reinterpret_cast<const uint4 *>(p + TPI * D * i));
         }
         // logits of tok(g, j) for column n: value (+ third) part + residual part
         float gv[8];
@@ -811,6 +826,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
             o[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pB, o[e],
                                                            0, 0, 0);
         }
+        if (tt + 1 < ntiles) k_store();
     }
 
     // value + residual columns; then lane (g, n < G) holds elements
@@ -837,7 +853,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
 // Persistent workers: each workgroup takes item tickets until the list is done.
 template <typename KV, int D, int TS, bool HARD, int G>
 __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArgs a) {
-    __shared__ AttnShared<D, G> sm;
+    __shared__ AttnShared<D, G, (G > 1 && sizeof(KV) == 2)> sm;
     const int total = a.ws_hdr[0];
     if (threadIdx.x == 0) sm.ticket = atomicAdd(&a.ws_hdr[1], 1);
     __syncthreads();
