@@ -9,7 +9,7 @@
 //   U_prob = s * (q . centroid + z * |q| * sqrt(var))
 //   U = min(U_geo, U_prob), or U_geo alone; admit iff U >= tau.
 //
-// One workgroup per (batch, query head) unit, up to 16 waves; with grouped
+// One workgroup per (batch, query head) unit, up to 8 waves; with grouped
 // heads each query head screens the metadata of its key/value head. The centroids are
 // dimension-major per unit, so lane l of a wave handles four consecutive
 // blocks and every load of one dimension is a contiguous 1 KiB run across the
@@ -33,7 +33,7 @@
 namespace eta {
 namespace {
 
-constexpr int kScreenMaxWaves = 16;
+constexpr int kScreenMaxWaves = 8;  // two workgroups fit a CU: one streams while the other syncs
 constexpr int kBlocksPerLane = 4;
 constexpr int kBlocksPerWave = kWave * kBlocksPerLane;
 constexpr int kMaxSlices = 8;
@@ -457,8 +457,8 @@ __global__ __launch_bounds__(kGroupMaxWaves *kWave) void screen_group_kernel(Scr
     if (with_union && threadIdx.x == 0) a.uni_cnt[ukv] = base_u;
 }
 
-// Block groups per pass and dimension slices: up to 16 waves; split the
-// dimension when the unit has fewer than 16 x 256 blocks.
+// Block groups per pass and dimension slices: up to 8 waves; split the
+// dimension when the unit has fewer than 8 x 256 blocks.
 void pick_shape(int nblk, int d, int *nbg, int *ds) {
     int g = (nblk + kBlocksPerWave - 1) / kBlocksPerWave;
     g = g < 1 ? 1 : (g > kScreenMaxWaves ? kScreenMaxWaves : g);
