@@ -888,21 +888,26 @@ constexpr int kPlanUnits = 64;
 __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int D, int G) {
     __shared__ int red[kPlanThreads / kWave];
     __shared__ int excl[kPlanUnits];
+    __shared__ int cnt_s[kPlanUnits];
     __shared__ int tile_total;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
+    static_assert(kPlanUnits == kWave, "one lane per unit of the tile");
     const int u0 = blockIdx.x * kPlanUnits;
     auto items_of = [&](int u) { return (a.cnt[u] + a.split - 1) / a.split; };
 
     int before = 0;  // items of units [0, u0)
+#pragma unroll 4
     for (int u = tid; u < u0; u += kPlanThreads) before += items_of(u);
 #pragma unroll
     for (int k = 1; k < kWave; k <<= 1) before += __shfl_xor(before, k, kWave);
     if (lane == 0) red[wave] = before;
     if (wave == 0) {
         const int u = u0 + lane;
-        const int n = u < a.units ? items_of(u) : 0;
+        const int c = u < a.units ? a.cnt[u] : 0;
+        const int n = (c + a.split - 1) / a.split;
+        cnt_s[lane] = c;
         int x = n;  // inclusive scan over the tile's units
 #pragma unroll
         for (int k = 1; k < kWave; k <<= 1) {
@@ -920,7 +925,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     for (int t = wave; t < kPlanUnits; t += kPlanThreads / kWave) {
         const int u = u0 + t;
         if (u >= a.units) break;
-        const int c = a.cnt[u];
+        const int c = cnt_s[t];
         if (c <= 0) {  // nothing admitted for any of the unit's query heads
             for (int i = lane; i < D * G; i += kWave) a.out[(size_t)u * G * D + i] = 0.f;
             if (lane < G && a.lse) a.lse[(size_t)u * G + lane] = -INFINITY;

@@ -120,6 +120,12 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
         const int blk0 = pass0 + grp * kBlocksPerWave + lane * kBlocksPerLane;
         const bool active = blk0 < nblk;  // nblk_cap % 4 == 0: the float4 is in bounds
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        // max norms and variances first: their loads overlap the centroid rows'
+        float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f), v4 = m4;
+        if (slice == 0 && active) {
+            m4 = ld_stream(reinterpret_cast<const float4 *>(mu + blk0));
+            if (!a.geo_only) v4 = ld_stream(reinterpret_cast<const float4 *>(vu + blk0));
+        }
         if (active && !a.geo_only) {
             // batches of kDimBatch dimensions (dps is a multiple of 8), the next
             // batch's loads in flight while the current one is used
@@ -174,13 +180,11 @@ __global__ __launch_bounds__(kScreenMaxWaves *kWave) void screen_kernel(ScreenAr
         int before = 0;
         if (slice == 0) {
             if (active) {
-                const float4 m4 = ld_stream(reinterpret_cast<const float4 *>(mu + blk0));
                 const float mx[4] = {m4.x, m4.y, m4.z, m4.w};
                 if (a.geo_only) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) U[j] = geo_scale * mx[j];
                 } else {
-                    const float4 v4 = ld_stream(reinterpret_cast<const float4 *>(vu + blk0));
                     const float vx[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -332,6 +336,12 @@ __global__ __launch_bounds__(kGroupMaxWaves *kWave) void screen_group_kernel(Scr
         float acc[G][4];
 #pragma unroll
         for (int j = 0; j < G; ++j) acc[j][0] = acc[j][1] = acc[j][2] = acc[j][3] = 0.f;
+        // max norms and variances first: their loads overlap the centroid rows'
+        float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f), v4 = m4;
+        if (active) {
+            m4 = ld_stream(reinterpret_cast<const float4 *>(mu + blk0));
+            if (!a.geo_only) v4 = ld_stream(reinterpret_cast<const float4 *>(vu + blk0));
+        }
         if (active && !a.geo_only) {
             // centroid rows in batches of kDimBatch dimensions, the next batch's loads
             // in flight while the current one is used
@@ -363,15 +373,8 @@ __global__ __launch_bounds__(kGroupMaxWaves *kWave) void screen_group_kernel(Scr
                 }
             }
         }
-        float mx[4] = {0.f, 0.f, 0.f, 0.f}, vx[4] = {0.f, 0.f, 0.f, 0.f};
-        if (active) {
-            const float4 m4 = ld_stream(reinterpret_cast<const float4 *>(mu + blk0));
-            mx[0] = m4.x; mx[1] = m4.y; mx[2] = m4.z; mx[3] = m4.w;
-            if (!a.geo_only) {
-                const float4 v4 = ld_stream(reinterpret_cast<const float4 *>(vu + blk0));
-                vx[0] = v4.x; vx[1] = v4.y; vx[2] = v4.z; vx[3] = v4.w;
-            }
-        }
+        const float mx[4] = {m4.x, m4.y, m4.z, m4.w};
+        const float vx[4] = {v4.x, v4.y, v4.z, v4.w};
         int before[G];
         bool uadm[4] = {false, false, false, false};
 #pragma unroll
