@@ -261,6 +261,28 @@ def test_split_size_independence_and_determinism():
         assert torch.max(torch.abs(o[1] - outs[0][1])).item() <= 1e-5
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_grouped_split_default_and_independence(G):
+    """Grouped heads: the default item length (split_blocks = 0) is the one
+    eta_split_blocks reports (8 per query head) and gives bitwise the same step as
+    passing it explicitly; other lengths agree to 1e-5."""
+    _announce(f"grouped split G={G}")
+    w = workloads.custom("gs", B=2, H=2 * G, H_kv=2, d=128, T=7000, kv_dtype=torch.bfloat16,
+                         group_corr=0.9, seed=42 + G)
+    default = _lib.split_blocks(w.B, w.H, w.kv_heads, w.T_cap, _lib.default_params())
+    assert default == 8 * G
+    outs = {}
+    for split in (0, default, 1, 3, 4096):
+        case = Case(w, params=_lib.default_params(split_blocks=split), fused=True).run()
+        outs[split] = (case.step.out.clone(), case.step.lse.clone(), case.step.uni_cnt.clone())
+        case.free()
+    assert all(torch.equal(a, b) for a, b in zip(outs[0], outs[default]))
+    for split in (1, 3, 4096):
+        assert torch.equal(outs[split][2], outs[0][2])
+        assert torch.max(torch.abs(outs[split][0] - outs[0][0])).item() <= 1e-5
+        assert torch.max(torch.abs(outs[split][1] - outs[0][1])).item() <= 1e-5
+
+
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
 def test_append_equals_rebuild_bitwise(dtype, d):
     _announce(f"append vs rebuild {dtype} d={d}")
