@@ -23,7 +23,7 @@ constexpr int kMetaBlocksPerGroup = 64;
 // Statistics of the block at Kb (its first token row) holding n >= 1 tokens,
 // computed by the calling wave. cen: the lane's EPL centroid dimensions
 // (identical in all four rows); var and maxnorm are wave-uniform.
-template <typename KV, int D>
+template <typename KV, int D, bool PART>
 __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
                                             float (&cen)[D / 16], float &var, float &maxnorm) {
     constexpr int EPL = D / 16;
@@ -45,7 +45,7 @@ __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
     for (int i = 0; i < 16; ++i) {
         float x[EPL];
         ld[i].widen(x);
-        const bool valid = 4 * i + row < n;
+        const bool valid = !PART || 4 * i + row < n;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) sum[e] += valid ? x[e] : 0.f;
     }
@@ -59,7 +59,7 @@ __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
     for (int i = 0; i < 16; ++i) {
         float x[EPL];
         ld[i].widen(x);
-        const bool valid = 4 * i + row < n;
+        const bool valid = !PART || 4 * i + row < n;
         float dev2 = 0.f, nrm2 = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -117,7 +117,12 @@ __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
         float v = 0.f, m = 0.f;
         const long long off = lay.block_offset(b, k, blk, D);
         if (off >= 0) {
-            block_stats<KV, D>(K + off, min(len - blk * kBlockTokens, kBlockTokens), cen, v, m);
+            const int n = min(len - blk * kBlockTokens, kBlockTokens);
+            if (n == kBlockTokens) {  // a whole block: no row masks
+                block_stats<KV, D, false>(K + off, n, cen, v, m);
+            } else {
+                block_stats<KV, D, true>(K + off, n, cen, v, m);
+            }
         } else {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) cen[e] = 0.f;
