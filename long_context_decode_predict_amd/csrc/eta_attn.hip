@@ -1054,9 +1054,10 @@ hipError_t launch_partial_t(const AttnArgs &a, bool hard, int workers, hipStream
     return hipGetLastError();
 }
 
-// Tile rows per K/V register buffer: smaller tiles for wider rows and more
-// query heads per key/value head keep every instance but fp32 d = 128 with
-// G = 2 at two or three waves per SIMD.
+// Tile rows per K/V register buffer of the vector-ALU paths: smaller tiles for
+// wider rows and more query heads per key/value head keep every instance but
+// fp32 d = 128 with G = 2 at two or three waves per SIMD. (bf16 with grouped
+// heads takes the matrix-core path, whose 32-token tile does not depend on it.)
 template <typename KV, int D>
 hipError_t launch_partial_g(const AttnArgs &a, bool hard, int workers, hipStream_t st) {
     constexpr bool wide = sizeof(KV) * D > 256;  // fp32 rows of 128
