@@ -61,12 +61,18 @@ def admitted_bytes(w, cnt, idx, lens):
 
 
 def attn_source_sha(sources=ATTN_SOURCES) -> str:
+    """Hash of the kernel sources' code: comments and layout are dropped, so an edit
+    that cannot change the compiled kernel keeps the committed counters valid."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for f in sources:
-        with open(os.path.join(ROOT, "long_context_decode_predict_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "long_context_decode_predict_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
