@@ -652,7 +652,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": ("bf16 MFMA on split fp32 operands, f32 accumulate"
+                  if w.G > 1 and w.kv_dtype == torch.bfloat16 else "f32"),
         "data": "synthetic (seeded clustered keys; see DESIGN.md)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
                    "T": w.T, "paged": w.paged, "var_len": w.var_len,
