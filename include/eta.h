@@ -41,7 +41,9 @@
  *       uni_cnt   int32   [B][H_kv]
  *       out       float32 [B][H][d],  lse float32 [B][H]
  *     where nblk_cap = eta_nblk_cap(T_cap) = ceil(T_cap/64) rounded up to a
- *     multiple of 4.
+ *     multiple of 4. K and V (or their pools) start on a 16-byte boundary;
+ *     bfloat16 with d = 64 needs only 8 bytes, except for K under grouped
+ *     heads in the attention calls.
  *   - Block beta of a unit covers tokens [64*beta, min(T_b, 64*beta + 64)) of
  *     its row b (T_b = seq_lens[b], or T); the last block may be partial.
  *     Tokens at or beyond T_b are never read. Block metadata, admitted lists

@@ -12,9 +12,6 @@
 namespace {
 
 constexpr int kBlock = 64;
-// Default blocks per split-KV work item: smaller items balance the persistent
-// workers better under multi-head attention; with grouped heads an item already
-// carries G heads' work (and G partials), so larger items pay off there.
 // Default split-KV item: 8 admitted blocks per query head of the key/value
 // unit, i.e. 8 * G (an item carries the state and partials of G heads, so its
 // fixed cost grows with G and so should its length), doubled for caches of at
@@ -302,6 +299,8 @@ eta_status eta_decode_attn_partial(const eta_shape *s, const float *q, const voi
     if (q == nullptr || K == nullptr || V == nullptr || tau == nullptr || adm_idx == nullptr)
         return ETA_ERR_INVALID_ARG;
     if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
+    // grouped heads with bf16 K read whole 16-byte chunks of every row (d = 64 too)
+    if (g.G > 1 && g.bf16 && !aligned(K, 16)) return ETA_ERR_INVALID_ARG;
     return from_hip(eta::launch_attn_partial(g, q, K, V, tau, adm_idx, adm_cnt, p->gate_beta,
                                              p->gate_hard != 0, split_of(s, p), max_chunks, out, lse,
                                              ws, stream));

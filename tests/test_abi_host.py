@@ -194,6 +194,13 @@ def test_decode_attn_errors(L):
     assert call(cnt=None) == INV
     assert L.eta_decode_attn(BY(shape(d=48)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BY(p), FAKE,
                              None, FAKE, need, None) == UNS
+    # bf16, d = 64: rows are 8-byte aligned, but grouped heads read K in 16-byte chunks
+    g = BY(shape(H=4, H_kv=2, d=64))
+    need_g = L.eta_decode_attn_workspace_size(g, BY(p))
+    assert L.eta_decode_attn(g, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, BY(p), FAKE, None, FAKE,
+                             need_g, None) == INV
+    assert L.eta_decode_attn_partial(g, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, BY(p), FAKE, None,
+                                     FAKE, need_g, None) == INV
 
 
 def test_binding_refuses_host_tensors():
