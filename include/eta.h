@@ -135,7 +135,8 @@ int eta_nblk_cap(int T_cap);
 /* The split-KV item length the attention calls use for this shape and these
  * parameters: p->split_blocks if nonzero, else the default (8 * G, twice that
  * for caches of at least 2^20 unit blocks). Returns 0 if
- * s or p is null or p->split_blocks is out of range. Host-only, no GPU work. */
+ * s or p is null, the shape is invalid or unsupported, or p->split_blocks is
+ * out of range. Host-only, no GPU work. */
 int eta_split_blocks(const eta_shape *s, const eta_params *p);
 
 /* Human-readable name of a status code (static storage). */

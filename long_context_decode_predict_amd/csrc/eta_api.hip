@@ -168,7 +168,9 @@ eta_params eta_default_params(void) {
 int eta_nblk_cap(int T_cap) { return T_cap < 1 ? 0 : nblk_cap_of(T_cap); }
 
 int eta_split_blocks(const eta_shape *s, const eta_params *p) {
-    if (s == nullptr || p == nullptr || p->split_blocks < 0 || p->split_blocks > kMaxSplit) return 0;
+    if (check_shape(s) != ETA_OK || p == nullptr || p->split_blocks < 0 ||
+        p->split_blocks > kMaxSplit)
+        return 0;
     return split_of(s, p);
 }
 

@@ -53,6 +53,9 @@ def test_defaults_and_strings(L):
     assert _lib.split_blocks(32, 32, 8, 32768, _lib.default_params(split_blocks=5)) == 5
     assert _lib.split_blocks(32, 32, 8, 32768, _lib.default_params(split_blocks=-1)) == 0
     assert L.eta_split_blocks(None, BY(d)) == 0
+    assert L.eta_split_blocks(BY(shape(H=8, H_kv=3)), BY(d)) == 0  # invalid shape
+    assert L.eta_split_blocks(BY(shape(H=24, H_kv=2)), BY(d)) == 0  # unsupported G
+    assert L.eta_split_blocks(BY(shape()), None) == 0
 
 
 def shape(**kw):
