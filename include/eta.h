@@ -120,7 +120,7 @@ typedef struct {
     int split_blocks;   /* admitted blocks per split-KV work item (1..4096);
                            0 = library default, 8 per query head of a
                            key/value unit (8 * G), doubled when
-                           B * H_kv * nblk_cap >= 2^20; see eta_split_blocks */
+                           B * H_kv * nblk_cap >= 2^21; see eta_split_blocks */
 } eta_params;
 
 /* Defaults: beta = 5 (the end of the 1 -> 5 anneal of Eq. 2), z = 4, soft
@@ -134,7 +134,7 @@ int eta_nblk_cap(int T_cap);
 
 /* The split-KV item length the attention calls use for this shape and these
  * parameters: p->split_blocks if nonzero, else the default (8 * G, twice that
- * for caches of at least 2^20 unit blocks). Returns 0 if
+ * for caches of at least 2^21 unit blocks). Returns 0 if
  * s or p is null, the shape is invalid or unsupported, or p->split_blocks is
  * out of range. Host-only, no GPU work. */
 int eta_split_blocks(const eta_shape *s, const eta_params *p);

@@ -15,10 +15,10 @@ constexpr int kBlock = 64;
 // Default split-KV item: 8 admitted blocks per query head of the key/value
 // unit, i.e. 8 * G (an item carries the state and partials of G heads, so its
 // fixed cost grows with G and so should its length), doubled for caches of at
-// least 2^20 unit blocks, where there are items enough to keep the grid busy
+// least 2^21 unit blocks, where there are items enough to keep the grid busy
 // with longer ones.
 constexpr int kDefaultSplitPerHead = 8;
-constexpr long long kLongItemSlots = 1ll << 20;
+constexpr long long kLongItemSlots = 1ll << 21;
 constexpr int kMaxSplit = 4096;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

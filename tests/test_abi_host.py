@@ -47,9 +47,9 @@ def test_defaults_and_strings(L):
     d = L.eta_default_params()
     assert [_lib.split_blocks(32, H, Hkv, 32768, d)
             for H, Hkv in ((16, 0), (16, 16), (8, 4), (32, 8), (64, 8))] == [8, 8, 16, 32, 64]
-    # doubled from 2^20 unit blocks (B * H_kv * nblk_cap) on
-    assert [_lib.split_blocks(B, 16, 16, T, d) for B, T in ((64, 131072), (64, 65536),
-                                                          (63, 65536))] == [16, 16, 8]
+    # doubled from 2^21 unit blocks (B * H_kv * nblk_cap) on
+    assert [_lib.split_blocks(B, 16, 16, T, d) for B, T in ((64, 131072), (128, 65536),
+                                                          (63, 131072), (64, 65536))] == [16, 16, 8, 8]
     assert _lib.split_blocks(32, 32, 8, 32768, _lib.default_params(split_blocks=5)) == 5
     assert _lib.split_blocks(32, 32, 8, 32768, _lib.default_params(split_blocks=-1)) == 0
     assert L.eta_split_blocks(None, BY(d)) == 0
