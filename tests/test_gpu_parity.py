@@ -162,6 +162,10 @@ GQA = [
     ("g4_static", dict(B=2, H=16, H_kv=4, d=128, T=4096, kv_dtype=torch.bfloat16,
                        sigma_range=(0.1, 0.6), head_densities=tuple(0.1 + 0.05 * h for h in range(16)),
                        seed=97), "static", {}),
+    # 9376 blocks: several passes of the grouped screen (2048 blocks each) and two
+    # of the union bitmap (8192 blocks each), a ragged last block
+    ("g4_bf16_d64_long", dict(B=1, H=8, H_kv=2, d=64, T=600_001, kv_dtype=torch.bfloat16,
+                              seed=104), "predictor", {}),
     ("g4_tau_neg_inf", dict(B=1, H=8, H_kv=2, d=128, T=2000, kv_dtype=torch.bfloat16, seed=98),
      "neg_inf", {}),
     ("g4_tau_pos_inf", dict(B=1, H=8, H_kv=2, d=128, T=2000, kv_dtype=torch.bfloat16, seed=99),
