@@ -1,10 +1,12 @@
 """Benchmark of the ETA block-sparse decode step on one MI355X.
 
 A step is one pass of the whole hot path over one synthetic batch resident in
-HBM: eta_predict_tau -> eta_screen -> eta_decode_attn (split-KV attention with
-the fused log-sum-exp combine). W untimed warm-up steps, then K timed steps
-between device synchronisations, timed with HIP events on the launch stream.
-Prints ONE JSON line.
+HBM: eta_predict_screen (Eq. 1 and the screen in one launch, with the union of
+grouped heads; --unfused: eta_predict_tau -> eta_screen [-> eta_admit_union])
+-> eta_decode_attn_partial (split-KV attention) -> eta_decode_attn_combine
+(log-sum-exp merge). W untimed warm-up steps, then K timed steps between device
+synchronisations, timed with HIP events on the launch stream. Prints ONE JSON
+line; `--workload prefill_...` times the training-time forward instead.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
