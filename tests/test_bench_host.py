@@ -1,0 +1,87 @@
+"""Host logic of bench.py (no GPU): the one-GPU guard, the byte and flop counts
+behind the reported rooflines, and the validity check of the committed counter
+summaries."""
+import dataclasses
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from long_context_decode_predict_amd import workloads  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_admitted_bytes_counts_the_partial_last_block():
+    # two rows: 130 tokens (blocks 0, 1 full, block 2 holds 2 tokens) and 128 (two full)
+    w = workloads.custom("ab", B=2, H=2, d=64, T=130, kv_dtype=torch.bfloat16)
+    cnt = np.array([[2, 1], [2, 0]])
+    idx = np.zeros((2, 2, 4), dtype=np.int64)
+    idx[0, 0, :2] = [0, 2]  # ends on the partial block: 64 + 2 tokens
+    idx[0, 1, :1] = [1]     # 64 tokens
+    idx[1, 0, :2] = [0, 1]  # 128 tokens (row of 128: no partial block)
+    got = bench.admitted_bytes(w, cnt, idx, [130, 128])
+    assert got == 2 * (66 + 64 + 128) * 64 * 2  # K and V, bf16
+
+
+def test_prefill_flops_closed_form():
+    w = workloads.PREFILL_WORKLOADS["prefill_b4_h16_d128_t8k_bf16"]
+    T = w.T_q
+    assert w.T_k == T
+    assert bench.prefill_flops(w) == 4 * w.d * (T * (T + 1) // 2) * w.B * w.H
+    # a chunk of 100 queries after a prefix of 900 keys: 100 * 900 + 100 * 101 / 2 pairs
+    c = dataclasses.replace(w, T_q=100, T_k=1000)
+    assert bench.prefill_flops(c) == 4 * w.d * (100 * 900 + 5050) * w.B * w.H
+
+
+def test_source_hash_ignores_comments_and_layout(tmp_path, monkeypatch):
+    csrc = tmp_path / "long_context_decode_predict_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (csrc / "a.hip").write_text("int f(int x) {\n    return x + 1;  // one\n}\n")
+    h0 = bench.attn_source_sha(("a.hip",))
+    (csrc / "a.hip").write_text("/* header */\nint f(int x) { return x + 1; }   // other\n")
+    assert bench.attn_source_sha(("a.hip",)) == h0
+    (csrc / "a.hip").write_text("int f(int x) { return x + 2; }\n")
+    assert bench.attn_source_sha(("a.hip",)) != h0
+
+
+def test_committed_counter_summaries_parse(monkeypatch):
+    """Every attention / prefill profile summary names its workload and carries the
+    traffic and source hash that bench.py reads; a different hash makes the traffic
+    null instead of stale."""
+    names = sorted(os.listdir(os.path.join(ROOT, "profiles")))
+    attn = [n for n in names if n.startswith("attn_partial_")]
+    pre = [n for n in names if n.startswith("prefill_attn_")]
+    assert attn and pre
+    for n in attn + pre:
+        wl = n.split("_", 2)[2][:-3]
+        assert wl in workloads.WORKLOADS or wl in workloads.PREFILL_WORKLOADS, n
+        text = open(os.path.join(ROOT, "profiles", n)).read()
+        assert "rocprofv3" in text and "traffic_bytes_per_launch:" in text
+        sha = [ln.split(":", 1)[1].strip() for ln in text.splitlines()
+               if ln.startswith("attn_source_sha256:")]
+        assert len(sha) == 1 and len(sha[0]) == 64
+    wl = attn[0][len("attn_partial_"):-3]
+    monkeypatch.setattr(bench, "attn_source_sha", lambda sources=None: "0" * 64)
+    assert bench.counter_traffic(wl) is None
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_metadata_bytes_per_block(name):
+    w = workloads.WORKLOADS[name]
+    lens = workloads.row_lengths(w)
+    blocks = w.kv_heads * sum((t + 63) // 64 for t in lens)
+    assert bench.meta_bytes(w, lens) == blocks * (w.d + 2) * 4
