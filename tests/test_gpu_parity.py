@@ -55,6 +55,11 @@ SMALL = [
     ("bf16_two_screen_passes", workloads.custom("r7", B=1, H=1, d=128, T=300_000,
                                                 kv_dtype=torch.bfloat16, seed=17),
      "predictor", {}, None),
+    # one unit of 2.1M tokens (32813 blocks): 16 screen passes, ~1560 work items merged
+    # by one combine workgroup in tiles of 256
+    ("bf16_2m_tokens_one_unit", workloads.custom("r16", B=1, H=1, d=128, T=2_100_001,
+                                                 kv_dtype=torch.bfloat16, seed=26),
+     "predictor", {}, None),
     ("bf16_hard_gate", workloads.custom("r8", B=2, H=4, d=128, T=3000, kv_dtype=torch.bfloat16,
                                         seed=18), "predictor", {"gate_hard": 1}, None),
     ("bf16_geo_bound", workloads.custom("r9", B=2, H=4, d=128, T=3000, kv_dtype=torch.bfloat16,
