@@ -51,6 +51,7 @@ class Workload:
     append: int = 0             # tokens appended one by one before the step
     H_kv: int = 0               # key/value heads (0: multi-head, H_kv = H)
     group_corr: float = 0.0     # shared direction of a group's queries (grouped heads)
+    head_corr: float = 0.0      # multi-head: block structure shared by a row's heads
     var_len: float = 0.0        # row lengths ~ U[(1 - var_len) T, T] (0: every row holds T)
     paged: bool = False         # K/V in a shuffled page pool with a page table
     seed: int = SEED_BASE
@@ -84,7 +85,8 @@ WORKLOADS = {
         seed=SEED_BASE + 0, note="tiny single decode step, fp32 K/V"),
     "llama_b32_h16_d128_t32k_bf16": Workload(
         "llama_b32_h16_d128_t32k_bf16", B=32, H=16, d=128, T=32768, kv_dtype=torch.bfloat16,
-        seed=SEED_BASE + 1, note="LLaMA-style layer decode"),
+        head_corr=0.992, seed=SEED_BASE + 1,
+        note="LLaMA-style layer decode, heads of a row selecting overlapping blocks"),
     "headline_b64_h16_d128_t128k_bf16": Workload(
         "headline_b64_h16_d128_t128k_bf16", B=64, H=16, d=128, T=131072,
         kv_dtype=torch.bfloat16, needle_frac=0.01, seed=SEED_BASE + 2,
@@ -152,11 +154,20 @@ def generate(w: Workload, device="cuda", T_cap: int | None = None) -> dict:
         base = torch.randn((B, Hk, 1, d), generator=g, device=device, dtype=torch.float32)
         c = float(w.group_corr)
         q = (c * base + math.sqrt(1.0 - c * c) * q.view(B, Hk, w.G, d)).reshape(B, H, d)
+    hc = float(w.head_corr) if w.G == 1 else 0.0
+    if hc > 0:  # the heads of a row share a query direction (and, below, block centroids)
+        base = torch.randn((B, 1, d), generator=g, device=device, dtype=torch.float32)
+        q = hc * base + math.sqrt(1.0 - hc * hc) * q
     sig = head_sigmas(w).to(device)
     K = torch.empty((B, Hk, T_cap, d), dtype=w.kv_dtype, device=device)
     V = torch.empty((B, Hk, T_cap, d), dtype=w.kv_dtype, device=device)
     for b in range(B):  # one batch row at a time keeps fp32 temporaries small
         cen = torch.randn((Hk, nblk_cap, 1, d), generator=g, device=device, dtype=torch.float32)
+        if hc > 0:
+            shared = torch.randn((1, nblk_cap, 1, d), generator=g, device=device,
+                                 dtype=torch.float32)
+            cen.mul_(math.sqrt(1.0 - hc * hc)).add_(shared, alpha=hc)
+            del shared
         noise = torch.randn((Hk, nblk_cap, BLOCK, d), generator=g, device=device,
                             dtype=torch.float32)
         noise.mul_(sig.view(Hk, 1, 1, 1)).add_(cen)
@@ -173,6 +184,9 @@ def generate(w: Workload, device="cuda", T_cap: int | None = None) -> dict:
             wb = torch.randn((Hk, 1, d), generator=g, device=device, dtype=torch.float32) / math.sqrt(d)
             c = float(w.group_corr)
             wdiag = (c * wb + math.sqrt(1.0 - c * c) * wdiag.view(Hk, w.G, d)).reshape(H, d)
+        if hc > 0:  # and so do the heads' predictor columns
+            wb = torch.randn((1, d), generator=g, device=device, dtype=torch.float32) / math.sqrt(d)
+            wdiag = hc * wb + math.sqrt(1.0 - hc * hc) * wdiag
         for h in range(H):
             W[h * d:(h + 1) * d, h] = wdiag[h]
     needles = None
