@@ -9,8 +9,10 @@
 //   U_prob = s * (q . centroid + z * |q| * sqrt(var))
 //   U = min(U_geo, U_prob), or U_geo alone; admit iff U >= tau.
 //
-// One workgroup per (batch, query head) unit, up to 8 waves; with grouped
-// heads each query head screens the metadata of its key/value head. The centroids are
+// Multi-head attention: one workgroup per (batch, head) unit, up to 8 waves.
+// Grouped heads: one workgroup per key/value unit screens its G query heads,
+// each with its own query and threshold, from one read of the shared metadata
+// (screen_group_kernel, below). The centroids are
 // dimension-major per unit, so lane l of a wave handles four consecutive
 // blocks and every load of one dimension is a contiguous 1 KiB run across the
 // wave (float4 per lane), with no cross-lane reduction. When a unit has few
