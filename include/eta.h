@@ -213,7 +213,9 @@ eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W
  * abstract: the gate's floor makes tokens that only ride along with a selected
  * block harmless). uni_idx[k] = ascending union of adm_idx[k*G + j][0..cnt)
  * over j < G, uni_cnt[k] its length. Deterministic. With G = 1 it copies the
- * lists. Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_HIP.
+ * lists. The input lists must be ascending (as eta_screen writes them); ids
+ * outside [0, ceil(T/64)) are dropped and counts are clamped to [0, nblk_cap].
+ * Errors: ETA_ERR_INVALID_ARG, ETA_ERR_UNSUPPORTED, ETA_ERR_HIP.
  */
 eta_status eta_admit_union(const eta_shape *s, const int32_t *adm_idx, const int32_t *adm_cnt,
                            int32_t *uni_idx, int32_t *uni_cnt, hipStream_t stream);
@@ -250,8 +252,10 @@ size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);
  * The admitted list is cut into work items of split_blocks blocks. This call
  * is eta_decode_attn_partial followed by eta_decode_attn_combine on the same
  * stream. A unit with adm_cnt == 0 gets out = 0 and lse = -inf. lse is
- * nullable. adm_idx entries must be valid ascending block ids < ceil(T/64)
- * (eta_screen writes such lists); an id out of range is skipped.
+ * nullable. adm_idx entries are the unit's admitted block ids (eta_screen and
+ * eta_admit_union write them ascending); an entry that is not a block of the
+ * unit's row (negative, or >= ceil(T_b/64)) is skipped, and a count outside
+ * [0, nblk_cap] is clamped to it, so no read leaves the buffers.
  * ws: device workspace of at least eta_decode_attn_workspace_size() bytes,
  * 256-byte aligned; it needs no initialisation and is clobbered. Calls that
  * share a workspace must not overlap in time. Deterministic for a fixed

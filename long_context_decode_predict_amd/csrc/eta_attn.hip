@@ -39,10 +39,12 @@
 // a whole block (paged layout), so the rows of a partial last block past the
 // row's length are inside the allocation: they are loaded unclamped and masked
 // (their logits become -inf and their values are zeroed before use). For a
-// block whose page id is out of range no byte of the pool outside its pages is
-// touched: the tiles load from the first page instead and are masked whole, so
-// the block contributes nothing (a unit left with no token gets out = 0,
-// lse = -inf, as an empty list does).
+// block whose page id is out of range, or a list entry that is not a block of
+// the row (negative, or at or past ceil(T_b / 64)), no byte outside the K/V
+// buffers is touched: the tiles load from the start of K/V instead and are
+// masked whole, so the entry contributes nothing (a unit left with no token
+// gets out = 0, lse = -inf, as an empty list does). Counts are clamped to
+// [0, nblk_cap], so no list read leaves the unit's row of the list.
 #include "eta_device.hpp"
 #include "eta_launch.hpp"
 
@@ -70,6 +72,13 @@ struct AttnArgs {
     int2 *ws_items;  // compacted (unit, item index) list
     KVLayout lay;    // dense or paged rows, per-row lengths
 };
+
+// Admitted blocks of key/value unit u as every kernel here counts them: clamped
+// to the list capacity, so no list read leaves the unit's row of the list.
+__device__ __forceinline__ int unit_count(const AttnArgs &a, int u) {
+    const int c = a.cnt[u];
+    return c < 0 ? 0 : (c > a.nblk_cap ? a.nblk_cap : c);
+}
 
 // Zero the raw bits of a row held in registers (used for rows past T).
 template <typename KV, int EPL>
@@ -107,7 +116,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     constexpr int L = TS / 4;                 // row loads per lane per tile
     constexpr int TPB = kBlockTokens / TS;    // tiles per block
     constexpr int ROW = D;                    // elements per token row
-    const int c = a.cnt[u];
+    const int c = unit_count(a, u);
     const int nchunks = (c + a.split - 1) / a.split;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -130,6 +139,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     const int rb = u / a.lay.H_kv;          // batch row of the unit
     const int kh = u - rb * a.lay.H_kv;     // its key/value head
     const int Tb = a.lay.row_len(rb);       // tokens present in the row
+    const int nblk_row = (Tb + kBlockTokens - 1) / kBlockTokens;  // ids past it are skipped
     const int lane_off = row * ROW + col * EPL;  // element offset inside a 4-row group
     const int32_t *iu = a.idx + (size_t)u * a.nblk_cap;
 
@@ -149,10 +159,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     }
 
     // Element offset of tile tt and the number of its rows below the row's length
-    // (TS or more for every tile but a partial last block's; 0 for a bad page).
+    // (TS or more for every tile but a partial last block's; 0 for a bad page or
+    // an id outside the row's blocks).
     auto tile_at = [&](int tt, size_t &off, int &valid) {
         const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
-        const long long bo = a.lay.block_offset(rb, kh, blk, D);
+        const long long bo =
+            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
         const int sub = (tt % TPB) * TS;
         off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * ROW;
         valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
@@ -423,7 +435,7 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
     constexpr int M = P / 16;               // pairs owned per lane
     constexpr int GS = 16 / G;              // lanes of a row that own one head
     static_assert(P >= 16 && P <= 64 && P % 16 == 0 && L % M == 0, "pair layout");
-    const int c = a.cnt[u];
+    const int c = unit_count(a, u);
     const int nchunks = (c + a.split - 1) / a.split;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -448,6 +460,7 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
     const int rb = u / a.lay.H_kv;
     const int kh = u - rb * a.lay.H_kv;
     const int Tb = a.lay.row_len(rb);
+    const int nblk_row = (Tb + kBlockTokens - 1) / kBlockTokens;  // ids past it are skipped
     const int lane_off = row * ROW + col * EPL;
     const int32_t *iu = a.idx + (size_t)u * a.nblk_cap;
 
@@ -465,7 +478,8 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
 
     auto tile_at = [&](int tt, size_t &off, int &valid) {
         const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
-        const long long bo = a.lay.block_offset(rb, kh, blk, D);
+        const long long bo =
+            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
         const int sub = (tt % TPB) * TS;
         off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * ROW;
         valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
@@ -665,7 +679,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     constexpr int TPB = kBlockTokens / TT;
     static_assert(G >= 2 && G <= 8, "two operand columns per head");
     using VRow = RowLoad<uint16_t, EPL>;
-    const int c = a.cnt[u];
+    const int c = unit_count(a, u);
     const int nchunks = (c + a.split - 1) / a.split;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -701,6 +715,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     const int rb = u / a.lay.H_kv;
     const int kh = u - rb * a.lay.H_kv;
     const int Tb = a.lay.row_len(rb);
+    const int nblk_row = (Tb + kBlockTokens - 1) / kBlockTokens;  // ids past it are skipped
     // K tile: loaded row by row (CPR lanes per token row, TPI rows per load), kept
     // in this wave's LDS with 16-byte chunk c of token t at slot c ^ (t % CPR), and
     // read back in the A-operand layout (both directions free of bank conflicts)
@@ -720,7 +735,8 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
 
     auto tile_at = [&](int tt, size_t &off, int &valid) {
         const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
-        const long long bo = a.lay.block_offset(rb, kh, blk, D);
+        const long long bo =
+            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
         const int sub = (tt % TPB) * TT;
         off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * D;
         valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
@@ -895,7 +911,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     const int wave = tid / kWave;
     static_assert(kPlanUnits == kWave, "one lane per unit of the tile");
     const int u0 = blockIdx.x * kPlanUnits;
-    auto items_of = [&](int u) { return (a.cnt[u] + a.split - 1) / a.split; };
+    auto items_of = [&](int u) { return (unit_count(a, u) + a.split - 1) / a.split; };
 
     int before = 0;  // items of units [0, u0)
 #pragma unroll 4
@@ -905,7 +921,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     if (lane == 0) red[wave] = before;
     if (wave == 0) {
         const int u = u0 + lane;
-        const int c = u < a.units ? a.cnt[u] : 0;
+        const int c = u < a.units ? unit_count(a, u) : 0;
         const int n = (c + a.split - 1) / a.split;
         cnt_s[lane] = c;
         int x = n;  // inclusive scan over the tile's units
@@ -957,7 +973,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     const int uq = blockIdx.x;     // query unit
     const int u = uq / a.G;        // its key/value unit
     const int hj = uq - u * a.G;   // head within the group
-    const int c = a.cnt[u];
+    const int c = unit_count(a, u);
     const int nchunks = (c + a.split - 1) / a.split;
     if (nchunks <= 1) return;
     const int tid = threadIdx.x;

@@ -47,12 +47,13 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(int G, int nblk, i
         for (int j = 0; j < G; ++j) {
             const int h = u * G + j;
             const int32_t *lst = adm_idx + (size_t)h * nblk_cap;
-            const int cnt = adm_cnt[h];
+            const int cnt = min(max(adm_cnt[h], 0), nblk_cap);  // reads stay in the list row
             int mine = 0;
             for (int i = cursor[j] + tid; i < cnt; i += kUnionThreads) {
                 const int b = lst[i];
                 if (b >= r0 + kUnionRange) break;  // sorted: later entries are past this pass
-                atomicOr(&bits[(b - r0) >> 5], 1u << ((b - r0) & 31));
+                if (b >= r0 && b < nblk)  // an id outside [0, ceil(T / 64)) is dropped
+                    atomicOr(&bits[(b - r0) >> 5], 1u << ((b - r0) & 31));
                 ++mine;
             }
             if (mine) atomicAdd(&seen[j], mine);

@@ -351,3 +351,97 @@ def test_empty_cache_and_shared_workspace():
     case.free()
     cb.free()
     cs.free()
+
+
+def _attend_lists_vs_oracle(case, idx, cnt, O):
+    """eta_decode_attn over the given per-key/value-unit lists; every query head
+    against the oracle over the valid entries (ids of the row within the clamped count)."""
+    from gpu_util import kv_host
+    w, s = case.w, case.step
+    ncap, nblk = idx.shape[2], (case.T + 63) // 64
+    out = torch.empty_like(s.out)
+    lse = torch.empty_like(s.lse)
+    K, V = case.kv()
+    _lib.eta_decode_attn(case.data["q"], K, V, case.T, s.tau, idx, cnt, case.params, out, lse,
+                         s.ws)
+    torch.cuda.synchronize()
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    q = case.data["q"].cpu().numpy()
+    tau = s.tau.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.H):
+            k = h // w.G
+            c = min(max(int(cnt_h[b, k]), 0), ncap)
+            valid = np.array([x for x in idx_h[b, k, :c] if 0 <= x < nblk], dtype=np.int32)
+            if len(valid) == 0:
+                assert torch.all(out[b, h] == 0) and torch.isneginf(lse[b, h]), (b, h)
+                continue
+            Kh, Vh = kv_host(case.data["K"][b, k]), kv_host(case.data["V"][b, k])
+            out_o, lse_o = O.attend(q[b, h], Kh, Vh, case.T, float(tau[b, h]), valid,
+                                    beta=case.params.gate_beta)
+            assert np.max(np.abs(out[b, h].cpu().numpy() - out_o)) <= 2e-3, (b, h)
+            assert abs(float(lse[b, h]) - lse_o) <= 1e-4, (b, h)
+
+
+def _corrupt(idx, cnt, ncap):
+    """Unit 0: count past the capacity, the entries after its list not blocks of the
+    row; unit 1: a negative count; the longest other list: two entries replaced by
+    ids outside the row."""
+    idx, cnt = idx.clone(), cnt.clone()
+    c0 = int(cnt[0, 0])
+    fill = [16, 17, 1000, -7, 2**31 - 1, -2**31, 19, 16, 40, 99] * 2
+    idx[0, 0, c0:] = torch.tensor(fill[:ncap - c0], dtype=torch.int32, device="cuda")
+    cnt[0, 0] = ncap + 5
+    cnt[0, 1] = -3
+    flat = cnt.flatten().clone()
+    flat[:2] = -1
+    u = int(torch.argmax(flat))
+    b, k = divmod(u, cnt.shape[1])
+    assert int(cnt[b, k]) >= 4
+    idx[b, k, 1] = -1
+    idx[b, k, 3] = 99999
+    return idx, cnt
+
+
+@pytest.mark.parametrize("H_kv", [0, 2], ids=["mha", "g2_matrix_cores"])
+def test_invalid_list_entries_are_skipped(H_kv):
+    """A list entry that is not a block of its row (negative, or at or past
+    ceil(T_b / 64)) is skipped and a count outside [0, nblk_cap] is clamped, by the
+    attention (multi-head and matrix-core grouped paths) and by the union: the
+    result equals the oracle over the valid entries, and no byte outside the
+    buffers is read."""
+    _announce(f"invalid list entries H_kv={H_kv}")
+    O = oracle_mod.default()
+    w = workloads.custom("bad", B=2, H=6 if H_kv else 4, H_kv=3 if H_kv else 0, d=128, T=1000,
+                         kv_dtype=torch.bfloat16, seed=105)
+    case = Case(w, T_cap=1152).run()  # 16 blocks in the row, list capacity 20
+    ncap = case.step.uni_idx.shape[2]
+    assert ncap == 20
+    idx, cnt = _corrupt(case.step.uni_idx, case.step.uni_cnt, ncap)
+    _attend_lists_vs_oracle(case, idx, cnt, O)
+    case.free()
+
+
+def test_union_drops_invalid_entries():
+    """eta_admit_union: ids outside [0, ceil(T / 64)) are dropped and counts are
+    clamped to [0, nblk_cap] (ascending lists)."""
+    _announce("union of lists with invalid entries")
+    ncap, nblk = 20, 16
+    lists = [[-9, -1, 2, 5, 9, 16, 40, 100000], [0, 5, 15], [3, 4], [-4, 1, 17]]
+    counts = [8, 3 + ncap, -1, 3]  # the second count is clamped to the capacity
+    a_idx = torch.full((1, 4, ncap), 2**31 - 1, dtype=torch.int32)
+    for j, lst in enumerate(lists):
+        a_idx[0, j, :len(lst)] = torch.tensor(lst, dtype=torch.int32)
+    a_idx = a_idx.cuda()
+    a_cnt = torch.tensor([counts], dtype=torch.int32, device="cuda")
+    u_idx = torch.empty((1, 2, ncap), dtype=torch.int32, device="cuda")
+    u_cnt = torch.empty((1, 2), dtype=torch.int32, device="cuda")
+    _lib.eta_admit_union(a_idx, a_cnt, u_idx, u_cnt, 1000, 1152, 128, torch.bfloat16)
+    torch.cuda.synchronize()
+    for k in range(2):
+        want = set()
+        for j in (2 * k, 2 * k + 1):
+            c = min(max(counts[j], 0), ncap)
+            want |= {x for x in a_idx[0, j, :c].cpu().tolist() if 0 <= x < nblk}
+        got = u_idx[0, k, :int(u_cnt[0, k])].cpu().tolist()
+        assert got == sorted(want), (k, got, sorted(want))
