@@ -309,3 +309,28 @@ def test_predict_screen_union_errors(L):
     assert call(g, q=None) == INV
     assert call(g, bias=None) == INV
     assert call(shape(H=8, H_kv=3)) == INV
+
+
+def test_head_correlated_rows():
+    """Multi-head rows with head_corr c: every query and block centroid stays
+    N(0, I) per element while the heads of a row share direction c^2 (host only)."""
+    import torch
+    from long_context_decode_predict_amd import workloads
+    w = workloads.custom("hc", B=16, H=8, d=128, T=64 * 64, kv_dtype=torch.float32,
+                         head_corr=0.9, sigma=0.0, seed=3)
+    data = workloads.generate(w, "cpu")
+    q = data["q"].double()
+    assert abs(float(q.var()) - 1.0) < 0.1
+    qn = q / q.norm(dim=2, keepdim=True)
+    cos = (qn[:, :, None, :] * qn[:, None, :, :]).sum(-1)  # [B, H, H]
+    off = cos[:, ~torch.eye(w.H, dtype=torch.bool)]
+    assert abs(float(off.mean()) - 0.81) < 0.1
+    K = data["K"].double().view(w.B, w.H, -1, 64, w.d)[:, :, :, 0]  # sigma 0: keys = centroids
+    assert abs(float(K.var()) - 1.0) < 0.05
+    kc = (K[:, 0] * K[:, 1]).sum(-1) / (K[:, 0].norm(dim=-1) * K[:, 1].norm(dim=-1))
+    assert abs(float(kc.mean()) - 0.81) < 0.05
+    # without it the heads are independent
+    w0 = workloads.custom("hc0", B=2, H=8, d=128, T=64 * 64, kv_dtype=torch.float32, seed=3)
+    q0 = workloads.generate(w0, "cpu")["q"].double()
+    q0n = q0 / q0.norm(dim=2, keepdim=True)
+    assert abs(float((q0n[:, 0] * q0n[:, 1]).sum(-1).mean())) < 0.2
