@@ -363,7 +363,7 @@ def _attend_lists_vs_oracle(case, idx, cnt, O):
     lse = torch.empty_like(s.lse)
     K, V = case.kv()
     _lib.eta_decode_attn(case.data["q"], K, V, case.T, s.tau, idx, cnt, case.params, out, lse,
-                         s.ws)
+                         s.ws, layout=case.layout)
     torch.cuda.synchronize()
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
     q = case.data["q"].cpu().numpy()
@@ -403,18 +403,19 @@ def _corrupt(idx, cnt, ncap):
     return idx, cnt
 
 
-@pytest.mark.parametrize("H_kv", [0, 2], ids=["mha", "g2_matrix_cores"])
-def test_invalid_list_entries_are_skipped(H_kv):
+@pytest.mark.parametrize("H_kv,paged", [(0, False), (2, False), (0, True)],
+                         ids=["mha", "g2_matrix_cores", "mha_paged"])
+def test_invalid_list_entries_are_skipped(H_kv, paged):
     """A list entry that is not a block of its row (negative, or at or past
     ceil(T_b / 64)) is skipped and a count outside [0, nblk_cap] is clamped, by the
-    attention (multi-head and matrix-core grouped paths) and by the union: the
-    result equals the oracle over the valid entries, and no byte outside the
-    buffers is read."""
-    _announce(f"invalid list entries H_kv={H_kv}")
+    attention (multi-head and matrix-core grouped paths, dense and paged) and by the
+    union: the result equals the oracle over the valid entries, and no byte outside
+    the buffers (the page table included) is read."""
+    _announce(f"invalid list entries H_kv={H_kv} paged={paged}")
     O = oracle_mod.default()
     w = workloads.custom("bad", B=2, H=6 if H_kv else 4, H_kv=3 if H_kv else 0, d=128, T=1000,
                          kv_dtype=torch.bfloat16, seed=105)
-    case = Case(w, T_cap=1152).run()  # 16 blocks in the row, list capacity 20
+    case = Case(w, T_cap=1152, paged=paged).run()  # 16 blocks in the row, list capacity 20
     ncap = case.step.uni_idx.shape[2]
     assert ncap == 20
     idx, cnt = _corrupt(case.step.uni_idx, case.step.uni_cnt, ncap)
