@@ -255,7 +255,7 @@ size_t eta_decode_attn_workspace_size(const eta_shape *s, const eta_params *p);
  * nullable. adm_idx entries are the unit's admitted block ids (eta_screen and
  * eta_admit_union write them ascending); an entry that is not a block of the
  * unit's row (negative, or >= ceil(T_b/64)) is skipped, and a count outside
- * [0, nblk_cap] is clamped to it, so no read leaves the buffers.
+ * [0, T_cap/64] is clamped to it, so no read or write leaves the buffers.
  * ws: device workspace of at least eta_decode_attn_workspace_size() bytes,
  * 256-byte aligned; it needs no initialisation and is clobbered. Calls that
  * share a workspace must not overlap in time. Deterministic for a fixed

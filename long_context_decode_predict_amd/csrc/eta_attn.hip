@@ -44,7 +44,9 @@
 // buffers is touched: the tiles load from the start of K/V instead and are
 // masked whole, so the entry contributes nothing (a unit left with no token
 // gets out = 0, lse = -inf, as an empty list does). Counts are clamped to
-// [0, nblk_cap], so no list read leaves the unit's row of the list.
+// [0, T_cap / 64], the most blocks a list of distinct ids can hold: no list read
+// leaves the unit's row of the list, and no unit has more work items than the
+// workspace is sized for (ceil(T_cap / 64 / split) per unit).
 #include "eta_device.hpp"
 #include "eta_launch.hpp"
 
@@ -74,10 +76,13 @@ struct AttnArgs {
 };
 
 // Admitted blocks of key/value unit u as every kernel here counts them: clamped
-// to the list capacity, so no list read leaves the unit's row of the list.
+// to the blocks of the capacity (T_cap / 64 <= nblk_cap), so no list read leaves
+// the unit's row of the list and no item index reaches past the unit's
+// workspace slots.
 __device__ __forceinline__ int unit_count(const AttnArgs &a, int u) {
     const int c = a.cnt[u];
-    return c < 0 ? 0 : (c > a.nblk_cap ? a.nblk_cap : c);
+    const int cap = a.lay.max_pages;
+    return c < 0 ? 0 : (c > cap ? cap : c);
 }
 
 // Zero the raw bits of a row held in registers (used for rows past T).

@@ -16,7 +16,13 @@
 // operand of the P.V product (the product's reduction runs over keys in any
 // fixed order, and both operands use the same key order), so P never leaves
 // the registers. V is staged into LDS transposed and converted to fp16 (exact
-// for |v| in [2^-14, 65504]); P in fp16 keeps 11 significant bits.
+// for |v| in [2^-14, 65504]). The weights enter the product rounded toward
+// zero to fp16 (one conversion instruction per pair), and out is divided by
+// the sum of those same rounded weights (one fp16 dot2 per pair), so the
+// rounding perturbs each weight's share by at most 2^-11 around their common
+// part and cannot bias the output: constant value rows come out exactly, and
+// |out error| <= 2^-11 * sum_j w_j |v_j - out|, whatever the mean of V. The
+// fp32 sum of the unrounded weights gives lse.
 //
 // Workgroup = 4 waves = 128 consecutive queries of one (row, head); wave w owns
 // queries 32w .. 32w + 31. Key tiles of 64 are staged into LDS (K row-major,
@@ -33,6 +39,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPfWaves = 4;
 constexpr int kPfQ = 32 * kPfWaves;  // queries per workgroup
@@ -68,7 +75,8 @@ __device__ __forceinline__ float bf16_elem(const uint4 &r, int e) {
     return (e & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
-// Two floats to packed fp16 (exact for values representable in fp16).
+// Two floats to packed fp16, rounded toward zero (exact for values representable
+// in fp16).
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
@@ -220,7 +228,10 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
     f32x16 o[NMD];
 #pragma unroll
     for (int m = 0; m < NMD; ++m) o[m] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f, g_sum = 0.f;  // m_run in acc units
+    float m_run = -INFINITY, g_sum = 0.f;  // m_run in acc units
+    float l_run = 0.f;   // sum of the fp32 weights: lse
+    float lh_run = 0.f;  // sum of the weights as rounded to fp16 for P.V: out's divisor
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
     uint4 kr[StageShape<D>::KLD], vr[StageShape<D>::KPT];
     stage_load<D>(a, Kh, Vh, 0, kr, vr);
@@ -266,6 +277,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
         const float corr = __builtin_amdgcn_exp2f((m_run - m_ref) * a.c_soft);
         m_run = m_new;
         l_run *= corr;
+        lh_run *= corr;
         if (__any(corr != 1.f)) {  // the running maximum moved for some query of the wave
 #pragma unroll
             for (int m = 0; m < NMD; ++m) o[m] *= corr;
@@ -282,7 +294,9 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(g[mt][j], a.c_soft, -mref_c));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(g[mt][j + 1], a.c_soft, -mref_c));
                 l_run += p0 + p1;
-                pw[mt * 2 + j / 8][(j % 8) / 2] = pack_f16(p0, p1);
+                const uint32_t pk = pack_f16(p0, p1);
+                lh_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, lh_run, false);
+                pw[mt * 2 + j / 8][(j % 8) / 2] = pk;
             }
         }
 #pragma unroll
@@ -305,10 +319,11 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
 
     // the two halves of a query's keys meet
     const float l_tot = half_pair_sum(l_run);
+    const float lh_tot = half_pair_sum(lh_run);  // >= 1 once a key is visible (its max weighs 1)
     const float gs_tot = GSUM ? half_pair_sum(g_sum) : 0.f;
     if (qi < a.T_q) {
         const size_t uq = (size_t)bh * a.T_q + qi;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv = l_tot > 0.f ? 1.f / lh_tot : 0.f;
         float *orow = a.out + uq * D;
 #pragma unroll
         for (int m = 0; m < NMD; ++m) {

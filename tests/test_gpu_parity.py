@@ -355,10 +355,11 @@ def test_empty_cache_and_shared_workspace():
 
 def _attend_lists_vs_oracle(case, idx, cnt, O):
     """eta_decode_attn over the given per-key/value-unit lists; every query head
-    against the oracle over the valid entries (ids of the row within the clamped count)."""
+    against the oracle over the valid entries (ids of the row within the count
+    clamped to [0, T_cap / 64])."""
     from gpu_util import kv_host
     w, s = case.w, case.step
-    ncap, nblk = idx.shape[2], (case.T + 63) // 64
+    ncap, nblk = case.T_cap // 64, (case.T + 63) // 64
     out = torch.empty_like(s.out)
     lse = torch.empty_like(s.lse)
     K, V = case.kv()
@@ -419,6 +420,30 @@ def test_invalid_list_entries_are_skipped(H_kv, paged):
     ncap = case.step.uni_idx.shape[2]
     assert ncap == 20
     idx, cnt = _corrupt(case.step.uni_idx, case.step.uni_cnt, ncap)
+    _attend_lists_vs_oracle(case, idx, cnt, O)
+    case.free()
+
+
+@pytest.mark.parametrize("H_kv", [0, 2], ids=["mha", "g2_matrix_cores"])
+def test_count_clamp_keeps_items_in_workspace(H_kv):
+    """Regression: with one block per work item and a capacity of 18 blocks (list
+    rows of 20), a count of 19 or 20 is clamped to 18, so a unit never has more
+    items than the workspace holds for it (18) and cannot write into the next
+    unit's partials; the entries past 18 are valid-looking ids that must not be
+    attended. Every unit of the row against the oracle over its first 18 entries."""
+    _announce(f"count clamp vs workspace H_kv={H_kv}")
+    O = oracle_mod.default()
+    w = workloads.custom("clamp", B=2, H=6 if H_kv else 4, H_kv=3 if H_kv else 0, d=128,
+                         T=1150, kv_dtype=torch.bfloat16, seed=106)
+    params = _lib.default_params(split_blocks=1)
+    case = Case(w, T_cap=1152, params=params).run()
+    idx, cnt = case.step.uni_idx.clone(), case.step.uni_cnt.clone()
+    assert idx.shape[2] == 20 and case.T_cap // 64 == 18
+    units = cnt.shape[0] * cnt.shape[1]
+    for u in range(units - 1):  # every unit but the last: count 20 (even) or 19 (odd)
+        b, k = divmod(u, cnt.shape[1])
+        idx[b, k, :] = torch.arange(20, dtype=torch.int32, device="cuda") % 18
+        cnt[b, k] = 20 - (u % 2)
     _attend_lists_vs_oracle(case, idx, cnt, O)
     case.free()
 

@@ -1,8 +1,11 @@
 """GPU parity of the training-time (prefill) gated forward against the fp64 oracle.
 
 Every (row, head) of each case is compared query by query: out max-abs <= 2e-3
-(bf16 Q/K/V; the kernel's softmax weights and V enter the P.V product as fp16,
-rounding error <= 2^-11 relative per weight, far inside the bar), lse <= 1e-4,
+(bf16 Q/K/V; the kernel's softmax weights enter the P.V product rounded toward
+zero to fp16 and out is divided by the sum of those rounded weights, so each
+weight's share moves by at most 2^-11 around their common part and
+|out error| <= 2^-11 * sum_j w_j |v_j - out| whatever the mean of V; V itself
+is exact in fp16), lse <= 1e-4,
 gate_sum <= 1e-4 relative + 1e-3 absolute (fp32 sums of up to T_k gates).
 With the hard gate a query whose fp64 logits lie within 1e-5 of its tau may
 legitimately differ (fp32 vs fp64 decides the step); such queries are checked
@@ -162,3 +165,43 @@ def test_prefill_predictor_and_end_to_end():
     worst, _ = compare(w, data, params, got,
                        tau=torch.from_numpy(np.ascontiguousarray(tau_o)).float())
     print(f"  end-to-end max|dout| {worst:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("c", [8.0, -8.0, 32.0], ids=["v_plus8", "v_minus8", "v_plus32"])
+def test_prefill_value_offset(c):
+    """V = c + N(0, 1): the fp16 rounding of the weights must not scale the output
+    (a bias of the weights' sum would show as an error proportional to c)."""
+    _announce(f"prefill V offset {c}")
+    for kw in (dict(B=1, H=2, d=128, T_q=1000, T_k=1000),
+               dict(B=1, H=4, H_kv=2, d=64, T_q=300, T_k=1200)):
+        w = workloads.PrefillWorkload(f"voff{c}", seed=420 + int(c), **kw)
+        data = workloads.generate_prefill(w)
+        data["V"] = (data["V"].float() + c).to(torch.bfloat16)
+        params = _lib.default_params()
+        worst, _ = compare(w, data, params, run(w, data, params))
+        print(f"  {kw} max|dout| {worst:.2e}", flush=True)
+
+
+def test_prefill_constant_value_rows():
+    """Closed form: when every visible value row of a head is the same vector, every
+    query's output is that vector (softmax weights sum to one), for any gate and
+    offset. The kernel normalises by the very weights it multiplies with, so only
+    the fp32 accumulation remains: <= 1e-5 * max|v|. Also against the oracle."""
+    _announce("prefill constant V rows")
+    w = workloads.PrefillWorkload("vconst", B=2, H=4, H_kv=2, d=128, T_q=700, T_k=900, seed=430)
+    data = workloads.generate_prefill(w)
+    g = torch.Generator(device="cuda").manual_seed(431)
+    rows = 8.0 + 4.0 * torch.randn((w.B, w.kv_heads, 1, w.d), generator=g, device="cuda")
+    rows[1] = -32.0 + torch.randn((w.kv_heads, 1, w.d), generator=g, device="cuda")
+    data["V"] = rows.expand(w.B, w.kv_heads, w.T_k, w.d).to(torch.bfloat16).contiguous()
+    ref = data["V"][:, :, :1].float().cpu().numpy()  # [B, H_kv, 1, d]
+    for pkw in ({}, {"gate_hard": 1}, {"gate_beta": 1.0}):
+        params = _lib.default_params(**pkw)
+        out, lse, _ = run(w, data, params)
+        for b in range(w.B):
+            for h in range(w.H):
+                want = ref[b, h // w.G]
+                err = float(np.max(np.abs(out[b, h] - want)))
+                assert err <= 1e-5 * float(np.max(np.abs(want))), (pkw, b, h, err)
+    worst, _ = compare(w, data, _lib.default_params(), run(w, data, _lib.default_params()))
+    print(f"  oracle max|dout| {worst:.2e}", flush=True)
