@@ -293,6 +293,36 @@ eta_status eta_decode_attn_combine(const eta_shape *s, const int32_t *adm_cnt,
                                    const eta_params *p, float *out, float *lse, void *ws,
                                    size_t ws_bytes, hipStream_t stream);
 
+/* Largest workspace eta_decode_attn_noalloc can provide (128 MiB per GPU). At
+ * the default split and d = 128 that covers caches of up to about 2^27.9
+ * tokens in all (B * H * T_cap), e.g. B = 64, H = 16, T_cap = 128K. */
+#define ETA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * eta_decode_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, semantics and results as eta_decode_attn (same kernels, same
+ * split), but the workspace is a library-owned device array of
+ * ETA_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends. The
+ * call allocates and frees nothing and needs no memset: every byte of the
+ * array that a call reads it has first written itself. The kernels run on the
+ * current device's copy of the array, so `stream` must belong to the current
+ * device (checked when non-null). The first call on a device looks up that
+ * device's address of the array (a host-side query, no launch); later calls
+ * reuse it.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (on different streams, or
+ * from different host threads) race and must be serialised by the caller.
+ * Errors: as eta_decode_attn; ETA_ERR_WORKSPACE when the shape and split need
+ * more than ETA_NOALLOC_SCRATCH_BYTES (eta_decode_attn_workspace_size tells);
+ * ETA_ERR_INVALID_ARG for a stream of another device; ETA_ERR_HIP when the
+ * device or the array's address cannot be queried, or a launch fails.
+ */
+eta_status eta_decode_attn_noalloc(const eta_shape *s, const float *q, const void *K,
+                                   const void *V, const float *tau, const int32_t *adm_idx,
+                                   const int32_t *adm_cnt, const eta_params *p, float *out,
+                                   float *lse, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Training-time (prefill) forward
  *

@@ -89,6 +89,8 @@ SIGNATURES = {
                                                _vp]),
     "eta_decode_attn_combine": (ctypes.c_int, [_P(eta_shape), _vp, _P(eta_params), _vp, _vp, _vp,
                                                ctypes.c_size_t, _vp]),
+    "eta_decode_attn_noalloc": (ctypes.c_int, [_P(eta_shape), _vp, _vp, _vp, _vp, _vp, _vp,
+                                               _P(eta_params), _vp, _vp, _vp]),
     "eta_prefill_predict_tau": (ctypes.c_int, [_P(eta_prefill_shape), _vp, _vp, _vp, _vp, _vp]),
     "eta_prefill_attn": (ctypes.c_int, [_P(eta_prefill_shape), _vp, _vp, _vp, _vp,
                                         _P(eta_params), _vp, _vp, _vp, _vp]),
@@ -419,6 +421,9 @@ def attn_shape(q: torch.Tensor, K: torch.Tensor, T: int,
     return make_shape(B, H, d, T, T_cap, K.dtype, H_kv if H_kv != H else 0, layout, P)
 
 
+NOALLOC_SCRATCH_BYTES = 128 << 20  # ETA_NOALLOC_SCRATCH_BYTES
+
+
 def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws, layout=None):
     _check_kv(K)
     _check_kv(V, "V")
@@ -436,7 +441,8 @@ def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws, layout=None):
     _need(out, "out", torch.float32, (s.B, s.H, s.d))
     if lse is not None:
         _need(lse, "lse", torch.float32, (s.B, s.H))
-    _need(ws, "ws", torch.uint8)
+    if ws is not None:
+        _need(ws, "ws", torch.uint8)
     return s
 
 
@@ -450,6 +456,25 @@ def eta_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
                                  tau.data_ptr(), adm_idx.data_ptr(), adm_cnt.data_ptr(),
                                  ctypes.byref(params), out.data_ptr(), _ptr(lse),
                                  ws.data_ptr(), ws.numel(), _stream(stream)))
+
+
+def eta_decode_attn_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,
+                            tau: torch.Tensor, adm_idx: torch.Tensor, adm_cnt: torch.Tensor,
+                            params: eta_params, out: torch.Tensor, lse, stream=None,
+                            layout: KVLayout | None = None):
+    """eta_decode_attn with the library's own per-GPU workspace (no allocation by the
+    library or here). Calls that overlap in time on one GPU race."""
+    s = _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, None, layout)
+    st = lib().eta_decode_attn_noalloc(ctypes.byref(s), q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                       tau.data_ptr(), adm_idx.data_ptr(), adm_cnt.data_ptr(),
+                                       ctypes.byref(params), out.data_ptr(), _ptr(lse),
+                                       _stream(stream))
+    if st == ETA_ERR_WORKSPACE:
+        need = lib().eta_decode_attn_workspace_size(ctypes.byref(s), ctypes.byref(params))
+        raise EtaError("eta_decode_attn_noalloc", st,
+                       f"this shape needs {need} bytes of workspace, more than the "
+                       f"{NOALLOC_SCRATCH_BYTES} the library holds per GPU")
+    _check("eta_decode_attn_noalloc", st)
 
 
 def eta_decode_attn_partial(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, T: int,

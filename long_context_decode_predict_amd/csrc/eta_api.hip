@@ -7,6 +7,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "eta_launch.hpp"
 
 namespace {
@@ -128,6 +130,50 @@ eta_status check_attn(const eta_shape *s, const eta_params *p, const int32_t *ad
     if ((long long)s->B * s->H * mc > 0x7fffffffll) return ETA_ERR_INVALID_ARG;
     *g = geometry(s, nblk_cap_of(s->T_cap));
     *max_chunks = (int)mc;
+    return ETA_OK;
+}
+
+// The attention operands other than the workspace (shape already checked).
+eta_status check_attn_operands(const eta_shape *s, const float *q, const void *K, const void *V,
+                               const float *tau, const int32_t *adm_idx) {
+    if (q == nullptr || K == nullptr || V == nullptr || tau == nullptr || adm_idx == nullptr)
+        return ETA_ERR_INVALID_ARG;
+    if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
+    // grouped heads with bf16 K read whole 16-byte chunks of every row (d = 64 too)
+    const bool grouped = kv_heads_of(s) < s->H;
+    if (grouped && s->kv_dtype == ETA_BF16 && !aligned(K, 16)) return ETA_ERR_INVALID_ARG;
+    return ETA_OK;
+}
+
+// Workspace of eta_decode_attn_noalloc: one copy per GPU, in device memory the
+// code object reserves when the library's kernels are loaded on that GPU. Host
+// code never uses the array's name as an address (on the host it names a
+// stand-in): every use goes through the device address looked up below.
+static __device__ __align__(256) unsigned char scratch[ETA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_addr[kMaxDevices] = {};  // per device, looked up once
+
+// The current device's address of `scratch` (looked up on first use, with that
+// device current); `stream`, when non-null, must belong to the same device.
+eta_status scratch_for_stream(hipStream_t stream, void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ETA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return ETA_ERR_UNSUPPORTED;
+    if (stream != nullptr) {
+        int sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return ETA_ERR_HIP;
+        if (sdev != dev) return ETA_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_addr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return ETA_ERR_HIP;
+        scratch_addr[dev] = p;
+    }
+    *ptr = scratch_addr[dev];
     return ETA_OK;
 }
 
@@ -298,11 +344,7 @@ eta_status eta_decode_attn_partial(const eta_shape *s, const float *q, const voi
     int max_chunks = 0;
     eta_status st = check_attn(s, p, adm_cnt, out, ws, ws_bytes, &g, &max_chunks);
     if (st != ETA_OK) return st;
-    if (q == nullptr || K == nullptr || V == nullptr || tau == nullptr || adm_idx == nullptr)
-        return ETA_ERR_INVALID_ARG;
-    if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
-    // grouped heads with bf16 K read whole 16-byte chunks of every row (d = 64 too)
-    if (g.G > 1 && g.bf16 && !aligned(K, 16)) return ETA_ERR_INVALID_ARG;
+    if ((st = check_attn_operands(s, q, K, V, tau, adm_idx)) != ETA_OK) return st;
     return from_hip(eta::launch_attn_partial(g, q, K, V, tau, adm_idx, adm_cnt, p->gate_beta,
                                              p->gate_hard != 0, split_of(s, p), max_chunks, out, lse,
                                              ws, stream));
@@ -327,6 +369,22 @@ eta_status eta_decode_attn(const eta_shape *s, const float *q, const void *K, co
                                             ws_bytes, stream);
     if (st != ETA_OK) return st;
     return eta_decode_attn_combine(s, adm_cnt, p, out, lse, ws, ws_bytes, stream);
+}
+
+eta_status eta_decode_attn_noalloc(const eta_shape *s, const float *q, const void *K,
+                                   const void *V, const float *tau, const int32_t *adm_idx,
+                                   const int32_t *adm_cnt, const eta_params *p, float *out,
+                                   float *lse, hipStream_t stream) {
+    eta_status st = check_shape(s);
+    if (st != ETA_OK) return st;
+    if ((st = check_params(p)) != ETA_OK) return st;
+    if (adm_cnt == nullptr || out == nullptr) return ETA_ERR_INVALID_ARG;
+    if ((st = check_attn_operands(s, q, K, V, tau, adm_idx)) != ETA_OK) return st;
+    if (eta_decode_attn_workspace_size(s, p) > ETA_NOALLOC_SCRATCH_BYTES) return ETA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((st = scratch_for_stream(stream, &ws)) != ETA_OK) return st;
+    return eta_decode_attn(s, q, K, V, tau, adm_idx, adm_cnt, p, out, lse, ws,
+                           ETA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 eta_status eta_prefill_predict_tau(const eta_prefill_shape *s, const void *Q, const float *W,

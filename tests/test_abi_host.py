@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
@@ -204,6 +204,34 @@ def test_decode_attn_errors(L):
                              need_g, None) == INV
     assert L.eta_decode_attn_partial(g, FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, BY(p), FAKE, None,
                                      FAKE, need_g, None) == INV
+
+
+def test_decode_attn_noalloc_errors(L):
+    """The allocation-free variant validates everything before its first HIP call
+    (the device query): invalid operands, and a shape whose workspace exceeds the
+    library's per-GPU array, return without touching the runtime."""
+    p = params()
+    s = BY(shape())
+    ok = dict(q=FAKE, K=FAKE, V=FAKE, tau=FAKE, idx=FAKE, cnt=FAKE, out=FAKE)
+
+    def call(sh=s, **kw):
+        a = dict(ok, **kw)
+        return L.eta_decode_attn_noalloc(sh, a["q"], a["K"], a["V"], a["tau"], a["idx"],
+                                         a["cnt"], BY(p), a["out"], None, None)
+    assert call(q=None) == INV
+    assert call(out=None) == INV
+    assert call(cnt=None) == INV
+    assert call(idx=None) == INV
+    assert call(K=FAKE + 8) == INV
+    assert call(sh=BY(shape(d=48))) == UNS
+    assert L.eta_decode_attn_noalloc(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                     None) == INV
+    # B = 64, H = 16, T_cap = 128K fits (d = 128, default split); 4x the cache does not
+    fits = BY(shape(B=64, H=16, d=128, T=0, T_cap=131072))
+    big = BY(shape(B=64, H=16, d=128, T=0, T_cap=4 * 131072))
+    assert 0 < L.eta_decode_attn_workspace_size(fits, BY(p)) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert L.eta_decode_attn_workspace_size(big, BY(p)) > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(sh=big) == WSP
 
 
 def test_binding_refuses_host_tensors():
