@@ -10,6 +10,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libeta.so")
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libeta_probe.so")  # measurement aid (bench.py)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
@@ -22,10 +23,9 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build_lib(out: str = LIB_PATH, verbose: bool = False) -> str:
-    """Compile every ``csrc/*.hip`` into one shared library (always recompiles)."""
+def _hipcc(srcs: list[str], out: str, verbose: bool) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
+    cmd = [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,8 +35,16 @@ def build_lib(out: str = LIB_PATH, verbose: bool = False) -> str:
     return out
 
 
+def build_lib(out: str = LIB_PATH, verbose: bool = False) -> str:
+    """Compile every ``csrc/*.hip`` into one shared library, and the read probe
+    ``csrc/probe/*.hip`` into its own (always recompiles both)."""
+    _hipcc(sources(), out, verbose)
+    _hipcc(sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip"))), PROBE_LIB_PATH, verbose)
+    return out
+
+
 def ensure_built() -> str:
-    """Build the library only if it is absent (tests and benchmarks use this)."""
-    if not os.path.exists(LIB_PATH):
+    """Build the libraries only if one is absent (tests and benchmarks use this)."""
+    if not os.path.exists(LIB_PATH) or not os.path.exists(PROBE_LIB_PATH):
         build_lib()
     return LIB_PATH

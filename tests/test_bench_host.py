@@ -85,3 +85,38 @@ def test_metadata_bytes_per_block(name):
     lens = workloads.row_lengths(w)
     blocks = w.kv_heads * sum((t + 63) // 64 for t in lens)
     assert bench.meta_bytes(w, lens) == blocks * (w.d + 2) * 4
+
+
+def test_step_stats_median_and_spread():
+    st = bench.step_stats([4.0, 1.0, 3.0, 2.0, 100.0], total_ms=110.0)
+    assert st["median"] == 3.0 and st["min"] == 1.0 and st["max"] == 100.0
+    assert st["mean"] == 22.0 and st["n"] == 5
+    assert st["p10"] <= st["median"] <= st["p90"]
+
+
+def test_cpu_baseline_threads_and_host_counts():
+    cpus = bench.host_cpus()
+    assert cpus["os_cpu_count"] == os.cpu_count()
+    n = bench.host_threads()
+    assert 1 <= n <= bench.CPU_SHARE
+    assert n <= (cpus["affinity"] or os.cpu_count())
+
+
+def test_read_probe_library_exports_and_rejects_bad_sizes():
+    """libeta_probe.so is built beside libeta.so and refuses invalid arguments before
+    any launch (a size that is not whole 32 KiB chunks, null or misaligned pointers)."""
+    import ctypes
+
+    from long_context_decode_predict_amd.build import PROBE_LIB_PATH, ensure_built
+    ensure_built()
+    L = ctypes.CDLL(PROBE_LIB_PATH)
+    f = L.eta_probe_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    fake = 0x100000
+    assert f(fake, 32768 + 16, 1, fake, None) == -1
+    assert f(fake, 0, 1, fake, None) == -1
+    assert f(None, 32768, 1, fake, None) == -1
+    assert f(fake, 32768, 0, None, None) == -1
+    assert f(fake + 8, 32768, 1, fake, None) == -1
