@@ -101,6 +101,36 @@ def test_parity_small(name, w, mode, pkw, T_cap):
     case.free()
 
 
+def test_parity_needles_at_z16():
+    """The screen's needle-preserving operating point: the combined bound at z = 16 with
+    the threshold calibrated for z = 4 (the planted needle blocks are admitted, at a
+    near-dense cost), and z = 16 with the threshold re-calibrated for ~38 % density;
+    every unit against the oracle both times, and the needle recall of the first."""
+    from long_context_decode_predict_amd import calibrate
+    _announce("needles at z = 16")
+    w = workloads.custom("r6z", B=2, H=4, d=128, T=8192, kv_dtype=torch.bfloat16,
+                         needle_frac=0.02, seed=27)
+    p16 = _lib.default_params(z=16.0)
+    case = Case(w, params=p16, fused=True)  # bias calibrated at z = 16
+    held = case.bias.clone()
+    case.bias = calibrate.bias_for(w, case.data["q"], case.data["W"], z=4.0)
+    for label, bias in (("tau of z = 4", case.bias), ("density held", held)):
+        case.bias = bias
+        case.run()
+        st = compare_units(case, _all_units(w))
+        assert st["units"] == w.B * w.H
+        assert st["band_mismatch_units"] <= 1, st
+        nd = case.data["needles"].cpu().numpy()
+        idx, cnt = case.step.adm_idx.cpu().numpy(), case.step.adm_cnt.cpu().numpy()
+        hit = sum(int(np.isin(blk, idx[u // w.H, u % w.H, :cnt[u // w.H, u % w.H]]))
+                  for u, blk, _ in nd)
+        print(f"  {label}: density {np.mean(st['density']):.3f}, needle blocks admitted "
+              f"{hit} of {len(nd)}, max|dout| {st['max_out_err']:.2e}", flush=True)
+        if label == "tau of z = 4":
+            assert hit >= 0.9 * len(nd)
+    case.free()
+
+
 FUSED = [c for c in SMALL if c[0] in ("tiny_config", "bf16_d128_ragged", "f32_d128_ragged",
                                       "bf16_static_heads", "bf16_two_screen_passes",
                                       "bf16_geo_bound", "bf16_tau_nan", "f32_d64_many_units")]
