@@ -719,15 +719,18 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         append_ms = ev0.elapsed_time(ev1) / w.append
-    # the first build also loads the kernel's code object: time three more
+    # the first build also loads the kernel's code object: time five more, each
+    # between its own events, and take the median
     _lib.eta_build_block_meta(K0, w.T, meta, layout=layout)
-    ev0.record()
-    for _ in range(3):
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    bev[0].record()
+    for i in range(5):
         _lib.eta_build_block_meta(K0, w.T, meta, layout=layout)
-    ev1.record()
+        bev[i + 1].record()
     torch.cuda.synchronize()
-    build_ms = ev0.elapsed_time(ev1) / 3
-    log(f"[bench] metadata build {build_ms:.2f} ms")
+    build_all = [bev[i].elapsed_time(bev[i + 1]) for i in range(5)]
+    build_ms = float(np.median(build_all))
+    log(f"[bench] metadata build {build_ms:.2f} ms (median of {build_all})")
 
     step = DecodeStep(w.B, w.H, w.d, w.T_cap, w.kv_dtype, params, H_kv=w.kv_heads,
                       layout=layout)

@@ -2,10 +2,26 @@
 //
 // The cached block metadata is what makes the screen O(1) per block
 // (arXiv:2609.20888 abstract; evolve.pub review "Summary": centroid /
-// variance / max-norm). One wave computes one 64-token block entirely from
-// registers (a single read of the keys); a workgroup of four waves covers 64
-// consecutive blocks of one unit and writes the dimension-major centroid tile
-// through LDS so that every global store is a contiguous 64-float run.
+// variance / max-norm). One wave computes one block from a single read of its
+// keys held in registers; a workgroup of 16 waves covers 256 consecutive blocks
+// of one unit and writes the dimension-major centroid tile through LDS, so
+// every dimension's row of the tile leaves as one contiguous 1 KiB run of
+// 16-byte stores.
+//
+// Statistics in one pass over the keys, shifted by the block's first key k0:
+// with d_j = k_j - k0, the centroid is k0 + mean(d) and
+//   sum_j |k_j - c|^2 = sum_j |d_j|^2 - n |mean(d)|^2,
+// which is exact algebra; the shift keeps the two terms of the difference of
+// the size of the in-block spread, so fp32 loses no more than in a two-pass
+// sum (the shifted-data method for the variance). Each row load is consumed
+// as it arrives, so no widened copy of the block stays live. Rows of a
+// partial last block past its end load token 0 again: their d is exactly 0
+// and token 0's norm is already in the maximum, so no row needs a mask.
+//
+// The metadata stores leave with the non-temporal hint (like the key loads):
+// interleaved with the key stream, cached stores of the 520 bytes per block
+// slowed the build by a fifth, and longer runs per dimension (256 blocks per
+// workgroup instead of 64) recovered the rest.
 //
 // The build and the incremental append launch the same kernel (only the block
 // range differs), so an append is bitwise equal to a rebuild. Rows may hold
@@ -17,13 +33,24 @@
 namespace eta {
 namespace {
 
-constexpr int kMetaWaves = 4;
-constexpr int kMetaBlocksPerGroup = 64;
+constexpr int kMetaWaves = 16;
+constexpr int kMetaBlocksPerGroup = 256;
+
+typedef float f32x4_st __attribute__((ext_vector_type(4)));
+
+// Row 0's value of x in every row of the wave: the odd rows take the even rows'
+// values (16-lane swap), then the upper half of the wave takes the lower half's
+// (32-lane swap).
+__device__ __forceinline__ float bcast_row0(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+    return __uint_as_float(b[0]);
+}
 
 // Statistics of the block at Kb (its first token row) holding n >= 1 tokens,
 // computed by the calling wave. cen: the lane's EPL centroid dimensions
 // (identical in all four rows); var and maxnorm are wave-uniform.
-template <typename KV, int D, bool PART>
+template <typename KV, int D>
 __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
                                             float (&cen)[D / 16], float &var, float &maxnorm) {
     constexpr int EPL = D / 16;
@@ -34,50 +61,48 @@ __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
     RowLoad<KV, EPL> ld[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int t = min(4 * i + row, n - 1);  // clamp: never read past the row's end
+        const int t = 4 * i + row < n ? 4 * i + row : 0;  // past the end: token 0 again
         ld[i].load(Kb + (size_t)t * D + col * EPL);
     }
 
-    float sum[EPL];
+    float k0[EPL];  // token 0: row 0 of the first load
+    ld[0].widen(k0);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) sum[e] = 0.f;
+    for (int e = 0; e < EPL; ++e) k0[e] = bcast_row0(k0[e]);
+    float s[EPL];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float x[EPL];
-        ld[i].widen(x);
-        const bool valid = !PART || 4 * i + row < n;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sum[e] += valid ? x[e] : 0.f;
-    }
-    const float fn = (float)n;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) cen[e] = xrow_sum(sum[e]) / fn;
-
-    float sq = 0.f;
-    float nmax = 0.f;
+    for (int e = 0; e < EPL; ++e) s[e] = 0.f;
+    float q = 0.f, nmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         float x[EPL];
         ld[i].widen(x);
-        const bool valid = !PART || 4 * i + row < n;
-        float dev2 = 0.f, nrm2 = 0.f;
+        float dd2 = 0.f, nrm2 = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const float dd = x[e] - cen[e];
-            dev2 += dd * dd;
-            nrm2 += x[e] * x[e];
+            const float dv = x[e] - k0[e];
+            s[e] += dv;
+            dd2 = fmaf(dv, dv, dd2);
+            nrm2 = fmaf(x[e], x[e], nrm2);
         }
-        sq += valid ? dev2 : 0.f;
-        nrm2 = row_sum16(nrm2);  // squared norm of this row's token
-        nmax = valid ? fmaxf(nmax, nrm2) : nmax;
+        q += dd2;
+        nmax = fmaxf(nmax, row_sum16(nrm2));  // squared norm of this row's token
     }
-    sq = xrow_sum(row_sum16(sq));
-    nmax = xrow_max(nmax);
-    var = sq / (fn * (float)D);
-    maxnorm = sqrtf(nmax);
+    const float fn = (float)n;
+    float m2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const float me = xrow_sum(s[e]) / fn;  // mean of k - k0, this lane's dimensions
+        cen[e] = k0[e] + me;
+        m2 = fmaf(me, me, m2);
+    }
+    q = xrow_sum(row_sum16(q));
+    m2 = row_sum16(m2);
+    var = fmaxf(q - fn * m2, 0.f) / (fn * (float)D);
+    maxnorm = sqrtf(xrow_max(nmax));
 }
 
-// One workgroup per (key/value unit, group of 64 blocks). Build (n_new = 0):
+// One workgroup per (key/value unit, group of 256 blocks). Build (n_new = 0):
 // blocks [blk_begin, blk_end) clipped to the row's blocks. Append (n_new > 0):
 // the blocks touched by tokens [T_b, T_b + n_new) of row b, counted from the
 // block holding token T_b. A block whose page id is out of range gets zero
@@ -117,12 +142,7 @@ __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
         float v = 0.f, m = 0.f;
         const long long off = lay.block_offset(b, k, blk, D);
         if (off >= 0) {
-            const int n = min(len - blk * kBlockTokens, kBlockTokens);
-            if (n == kBlockTokens) {  // a whole block: no row masks
-                block_stats<KV, D, false>(K + off, n, cen, v, m);
-            } else {
-                block_stats<KV, D, true>(K + off, n, cen, v, m);
-            }
+            block_stats<KV, D>(K + off, min(len - blk * kBlockTokens, kBlockTokens), cen, v, m);
         } else {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) cen[e] = 0.f;
@@ -138,15 +158,28 @@ __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
     }
     __syncthreads();
 
+    // four consecutive blocks of one dimension per thread: 16-byte stores when the
+    // group starts on a multiple of 4 blocks (every build; the centroid rows are
+    // 16-byte aligned since nblk_cap is a multiple of 4), else one float per store
+    // (an append, which starts at the block holding its first new token)
     float *cu = centroid + (size_t)u * D * nblk_cap;
-    for (int i = threadIdx.x; i < D * kMetaBlocksPerGroup; i += kMetaWaves * kWave) {
-        const int dim = i / kMetaBlocksPerGroup;
-        const int j = i - dim * kMetaBlocksPerGroup;
-        if (j < count) cu[(size_t)dim * nblk_cap + first + j] = tile_c[dim][j];
+    constexpr int kQuads = kMetaBlocksPerGroup / 4;
+    const bool vec = (first & 3) == 0;
+    for (int i = threadIdx.x; i < D * kQuads; i += kMetaWaves * kWave) {
+        const int dim = i / kQuads;
+        const int j = (i - dim * kQuads) * 4;
+        float *dst = cu + (size_t)dim * nblk_cap + first + j;
+        if (vec && j + 4 <= count) {
+            const f32x4_st v = {tile_c[dim][j], tile_c[dim][j + 1], tile_c[dim][j + 2],
+                                tile_c[dim][j + 3]};
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_st *>(dst));
+        } else {
+            for (int e = 0; j + e < count; ++e) __builtin_nontemporal_store(tile_c[dim][j + e], dst + e);
+        }
     }
     for (int j = threadIdx.x; j < count; j += kMetaWaves * kWave) {
-        var[(size_t)u * nblk_cap + first + j] = tile_v[j];
-        maxnorm[(size_t)u * nblk_cap + first + j] = tile_m[j];
+        __builtin_nontemporal_store(tile_v[j], var + (size_t)u * nblk_cap + first + j);
+        __builtin_nontemporal_store(tile_m[j], maxnorm + (size_t)u * nblk_cap + first + j);
     }
 }
 
