@@ -70,13 +70,20 @@ typedef enum {
     ETA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned buffer */
     ETA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, block != 64, bad dtype */
     ETA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
-    ETA_ERR_HIP = -4          /* a kernel launch failed */
+    ETA_ERR_HIP = -4,         /* a kernel launch failed */
+    /* range guard (never returned): every int is a valid eta_status, so the
+       library reads whatever value a caller passes without undefined behaviour */
+    ETA_STATUS_MAX_ENUM = 0x7fffffff
 } eta_status;
 
-typedef enum { ETA_F32 = 0, ETA_BF16 = 1 } eta_dtype;
+typedef enum { ETA_F32 = 0, ETA_BF16 = 1, ETA_DTYPE_MAX_ENUM = 0x7fffffff } eta_dtype;
 
 /* Bound used by the screen (see eta_screen). */
-typedef enum { ETA_BOUND_COMBINED = 0, ETA_BOUND_GEO = 1 } eta_bound_mode;
+typedef enum {
+    ETA_BOUND_COMBINED = 0,
+    ETA_BOUND_GEO = 1,
+    ETA_BOUND_MAX_ENUM = 0x7fffffff
+} eta_bound_mode;
 
 typedef struct {
     int B, H;           /* batch rows and heads (MHA)                          */

@@ -97,14 +97,21 @@ SIGNATURES = {
 }
 
 
+def lib_path() -> str:
+    """The library to load: ``libeta.so`` in the package, or another build of the same
+    sources named by ETA_LIB_PATH (a host-instrumented one, for instance)."""
+    return os.environ.get("ETA_LIB_PATH") or LIB_PATH
+
+
 def lib() -> ctypes.CDLL:
     """Load ``libeta.so`` (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "long_context_decode_predict_amd.build.build_lib()")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(L, name)
             f.restype = res

@@ -32,10 +32,11 @@ _ip = ctypes.POINTER(ctypes.c_int32)
 _vp = ctypes.c_void_p
 
 
-def compile_oracle(src: str = SRC, out: str = LIB_PATH) -> str:
-    """Compile an oracle C source into a shared library with gcc (plain -O2)."""
+def compile_oracle(src: str = SRC, out: str = LIB_PATH, extra=()) -> str:
+    """Compile an oracle C source into a shared library with gcc (plain -O2; `extra`
+    flags are appended, e.g. sanitizers)."""
     cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fPIC", "-shared",
-           "-I", HERE, src, "-o", out, "-lm"]
+           "-I", HERE, *extra, src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -214,10 +215,14 @@ _default = None
 
 
 def default() -> OracleLib:
-    """The oracle built from ``eta_oracle.c`` (compiled on first use if absent)."""
+    """The oracle built from ``eta_oracle.c`` (compiled on first use if absent), or the
+    build of it that ETA_ORACLE_LIB names (a sanitizer-instrumented one, for instance)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB_PATH):
-            compile_oracle()
-        _default = OracleLib(LIB_PATH)
+        path = os.environ.get("ETA_ORACLE_LIB")
+        if not path:
+            path = LIB_PATH
+            if not os.path.exists(path):
+                compile_oracle()
+        _default = OracleLib(path)
     return _default
