@@ -14,8 +14,13 @@ PROBE_LIB_PATH = os.path.join(PKG_DIR, "libeta_probe.so")  # measurement aid (be
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
+# atomic optimizer off: for an atomic issued by one lane, the optimizer broadcasts
+# the returned value to the wave at once, so the wave waits for the atomic's round
+# trip where it is issued; the attention fetches its next work item's ticket at an
+# item's start and reads it only at the item's end.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
              "-Wall", "-Wno-unused-command-line-argument"]
 
 

@@ -50,6 +50,8 @@
 #include "eta_device.hpp"
 #include "eta_launch.hpp"
 
+#include <type_traits>
+
 namespace eta {
 namespace {
 
@@ -80,7 +82,7 @@ struct AttnArgs {
 // the unit's row of the list and no item index reaches past the unit's
 // workspace slots.
 __device__ __forceinline__ int unit_count(const AttnArgs &a, int u) {
-    const int c = a.cnt[u];
+    const int c = ld_const(a.cnt + u);
     const int cap = a.lay.max_pages;
     return c < 0 ? 0 : (c > cap ? cap : c);
 }
@@ -105,7 +107,18 @@ struct AttnShared {
     float m[kAttnWaves][G];
     float l[kAttnWaves][G];
     float o[kAttnWaves][G][D];
-    uint4 kt[KT ? kAttnWaves : 1][KT ? 4 * D : 1];  // matrix-core path: each wave's K tile
+    int ticket;
+};
+// Matrix-core path: each wave's two K tiles (the one being multiplied and the next);
+// the item's merge reuses their space once every wave has left its tile loop.
+template <int D, int G>
+struct AttnShared<D, G, true> {
+    float m[kAttnWaves][G];
+    float l[kAttnWaves][G];
+    union {
+        float o[kAttnWaves][G][D];
+        uint4 kt[kAttnWaves][2][4 * D];
+    };
     int ticket;
 };
 
@@ -124,7 +137,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     const int c = unit_count(a, u);
     const int nchunks = (c + a.split - 1) / a.split;
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = wave_id();
     const int lane = tid & (kWave - 1);
     const int row = lane >> 4;
     const int col = lane & 15;
@@ -135,7 +148,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         const size_t uq = (size_t)u * G + j;  // query unit
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qr[j][e] = a.q[uq * D + col * EPL + e] * a.s;
-        t[j] = a.tau[uq];
+        t[j] = ld_const(a.tau + uq);
         nbt[j] = -a.nbl2e * t[j];  // gate exponent = nbl2e * S + nbt
     }
 
@@ -167,7 +180,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     // (TS or more for every tile but a partial last block's; 0 for a bad page or
     // an id outside the row's blocks).
     auto tile_at = [&](int tt, size_t &off, int &valid) {
-        const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
+        const int blk = ld_const(iu + j0 + wave + (tt / TPB) * kAttnWaves);
         const long long bo =
             (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
         const int sub = (tt % TPB) * TS;
@@ -443,7 +456,7 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
     const int c = unit_count(a, u);
     const int nchunks = (c + a.split - 1) / a.split;
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = wave_id();
     const int lane = tid & (kWave - 1);
     const int row = lane >> 4;
     const int col = lane & 15;
@@ -482,7 +495,7 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
         for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
 
     auto tile_at = [&](int tt, size_t &off, int &valid) {
-        const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
+        const int blk = ld_const(iu + j0 + wave + (tt / TPB) * kAttnWaves);
         const long long bo =
             (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
         const int sub = (tt % TPB) * TS;
@@ -687,7 +700,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     const int c = unit_count(a, u);
     const int nchunks = (c + a.split - 1) / a.split;
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = wave_id();
     const int lane = tid & (kWave - 1);
     const int g = lane >> 4;
     const int n = lane & 15;
@@ -729,7 +742,6 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     constexpr int NLD = TT / TPI;      // loads per tile
     const int ld_tok = lane / CPR, ld_ch = lane % CPR;
     const int k_off = ld_tok * D + ld_ch * 8;  // + TPI*D*i
-    uint4 *kt = sm.kt[wave];
     const int v_off = 4 * g * D + EPL * n;  // + (j + (j >= 4 ? 12 : 0)) * D
     const int32_t *iu = a.idx + (size_t)u * a.nblk_cap;
 
@@ -739,7 +751,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     const int ntiles = nb > 0 ? nb * TPB : 0;
 
     auto tile_at = [&](int tt, size_t &off, int &valid) {
-        const int blk = iu[j0 + wave + (tt / TPB) * kAttnWaves];
+        const int blk = ld_const(iu + j0 + wave + (tt / TPB) * kAttnWaves);
         const long long bo =
             (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
         const int sub = (tt % TPB) * TT;
@@ -752,32 +764,39 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+    // Pipeline: while tile t is multiplied from LDS buffer t % 2, the K of tile
+    // t + 1 waits in registers (stored to the other buffer right after the q.K
+    // products), the K loads of tile t + 2 and the V loads of tile t are in flight;
+    // V of tile t + 1 is issued once tile t's P.V products have read V. Every load
+    // thus has about one whole tile of work to arrive in.
     uint4 kr[NLD];
     VRow vr[8];
-    auto k_store = [&]() {
+    auto k_load = [&](size_t off) {
+        const uint16_t *p = Kp + off + k_off;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) kr[i] = ld_stream(reinterpret_cast<const uint4 *>(p + TPI * D * i));
+    };
+    auto k_store = [&](uint4 *kt) {
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
             const int t = i * TPI + ld_tok;
             kt[t * CPR + (ld_ch ^ (t % CPR))] = kr[i];
         }
     };
-    size_t next_off = 0;
-    int next_valid = 0;
-    if (ntiles > 0) {
-        tile_at(0, next_off, next_valid);
-        const uint16_t *p = Kp + next_off + k_off;
+    auto v_load = [&](size_t off) {
+        const uint16_t *p = Vp + off + v_off;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) kr[i] = ld_stream(reinterpret_cast<const uint4 *>(p + TPI * D * i));
-        k_store();
-    }
-    for (int tt = 0; tt < ntiles; ++tt) {
-        const size_t base = next_off;
-        const int valid = next_valid;
-        {
-            const uint16_t *p = Vp + base + v_off;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vr[j].load(p + (j + (j >= 4 ? 12 : 0)) * D);
-        }
+        for (int j = 0; j < 8; ++j) vr[j].load(p + (j + (j >= 4 ? 12 : 0)) * D);
+    };
+    // One tile. NEXT: a tile t + 1 exists (store its K, issue its V); NEXT2: a tile
+    // t + 2 exists (issue its K). The steady-state loop issues every load without a
+    // branch, so the compiler's wait counts stay exact (a load skipped on some path
+    // makes it wait for all loads in flight).
+    size_t nxt_off = 0;  // tile t + 1
+    int cur_valid = 0, nxt_valid = 0;
+    auto tile = [&](int tt, auto NEXT, auto NEXT2) {
+        const int valid = cur_valid;
+        const uint4 *kt = sm.kt[wave][tt & 1];
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -789,13 +808,14 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qt[kc], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qt[kc], s1, 0, 0, 0);
         }
-        // the tile's K is read: start the next tile's K loads (into LDS at the end)
-        if (tt + 1 < ntiles) {
-            tile_at(tt + 1, next_off, next_valid);
-            const uint16_t *p = Kp + next_off + k_off;
-#pragma unroll
-            for (int i = 0; i < NLD; ++i)
-                kr[i] = ld_stream(reinterpret_cast<const uint4 *>(p + TPI * D * i));
+        // K of tile t + 1 into the other buffer (last read for tile t - 1), then the
+        // K loads of tile t + 2 into the freed registers
+        size_t nn_off = 0;
+        int nn_valid = 0;
+        if constexpr (decltype(NEXT)::value) k_store(sm.kt[wave][(tt + 1) & 1]);
+        if constexpr (decltype(NEXT2)::value) {
+            tile_at(tt + 2, nn_off, nn_valid);
+            k_load(nn_off);
         }
         // logits of tok(g, j) for column n: value (+ third) part + residual part
         float gv[8];
@@ -847,7 +867,30 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
             o[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pB, o[e],
                                                            0, 0, 0);
         }
-        if (tt + 1 < ntiles) k_store();
+        if constexpr (decltype(NEXT)::value) v_load(nxt_off);
+        cur_valid = nxt_valid;
+        nxt_off = nn_off;
+        nxt_valid = nn_valid;
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    if (ntiles > 0) {
+        size_t cur_off;
+        tile_at(0, cur_off, cur_valid);
+        k_load(cur_off);
+        k_store(sm.kt[wave][0]);
+        if (ntiles > 1) {
+            tile_at(1, nxt_off, nxt_valid);
+            k_load(nxt_off);
+            v_load(cur_off);
+            int tt = 0;
+            for (; tt + 2 < ntiles; ++tt) tile(tt, yes{}, yes{});
+            tile(tt, yes{}, no{});
+            tile(tt + 1, no{}, no{});
+        } else {
+            v_load(cur_off);
+            tile(0, no{}, no{});
+        }
     }
 
     // value + residual columns; then lane (g, n < G) holds elements
@@ -857,6 +900,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     for (int e = 0; e < EPL; ++e)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[e][i] += dpp_for_add<kRowRor8>(o[e][i]);
+    __syncthreads();  // sm.o shares its space with the waves' K tiles
     if (n < G) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -873,14 +917,15 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
 
 // Persistent workers: each workgroup takes item tickets until the list is done.
 template <typename KV, int D, int TS, bool HARD, int G>
-__global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves *kWave, 2) void attn_partial_kernel(AttnArgs a) {
     __shared__ AttnShared<D, G, (G > 1 && sizeof(KV) == 2)> sm;
-    const int total = a.ws_hdr[0];
+    const int total = ld_const(a.ws_hdr);
     if (threadIdx.x == 0) sm.ticket = atomicAdd(&a.ws_hdr[1], 1);
     __syncthreads();
-    int ticket = sm.ticket;
+    int ticket = uniform(sm.ticket);  // the item's unit, list and lengths: scalar loads
     while (ticket < total) {
-        const int2 it = a.ws_items[ticket];
+        const int *itp = reinterpret_cast<const int *>(a.ws_items + ticket);
+        const int2 it = make_int2(ld_const(itp), ld_const(itp + 1));
         int next = 0;
         if (threadIdx.x == 0) next = atomicAdd(&a.ws_hdr[1], 1);  // fetched early
         if constexpr (G > 1 && sizeof(KV) == 2) {  // grouped heads, bf16: matrix cores
@@ -892,7 +937,7 @@ __global__ __launch_bounds__(kAttnWaves *kWave) void attn_partial_kernel(AttnArg
         }
         if (threadIdx.x == 0) sm.ticket = next;
         __syncthreads();
-        ticket = sm.ticket;
+        ticket = uniform(sm.ticket);
     }
 }
 
@@ -913,7 +958,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan_kernel(AttnArgs a, int
     __shared__ int tile_total;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = wave_id();
     static_assert(kPlanUnits == kWave, "one lane per unit of the tile");
     const int u0 = blockIdx.x * kPlanUnits;
     auto items_of = [&](int u) { return (unit_count(a, u) + a.split - 1) / a.split; };
@@ -983,7 +1028,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     if (nchunks <= 1) return;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = wave_id();
     const size_t s0 = (size_t)u * a.ws_chunks * a.G + hj;  // partial of item i: s0 + i * G
     const int gs = a.G;
 

@@ -101,6 +101,26 @@ __device__ __forceinline__ float half_pair_sum(float x) {
 __device__ __forceinline__ float xrow_sum(float x) { return half_pair_sum(row_pair_sum(x)); }
 __device__ __forceinline__ float xrow_max(float x) { return half_pair_max(row_pair_max(x)); }
 
+// ---- wave-uniform values ----
+// The compiler cannot tell that threadIdx.x / 64, or a value read back from LDS,
+// is the same on every lane of a wave. Addresses formed from such values are then
+// read with vector loads, and waiting for one of those (vmcnt counts in issue
+// order) also waits for every K/V load issued before it. Passed through
+// readfirstlane, the value is known to be uniform: list entries, page ids and
+// lengths indexed by it are read with scalar loads, whose wait does not touch the
+// vector loads in flight.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int wave_id() { return uniform((int)threadIdx.x / kWave); }
+// A read of memory that no thread writes while the kernel runs (its inputs, and
+// what an earlier launch on the stream wrote). Stores elsewhere in the kernel
+// keep the compiler from proving that on its own; through the constant address
+// space a wave-uniform address becomes a scalar load, a per-lane one stays a
+// vector load.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
@@ -115,14 +135,14 @@ struct KVLayout {
 
     __device__ __forceinline__ int row_len(int b) const {
         if (seq_lens == nullptr) return T;
-        const int t = seq_lens[b];
+        const int t = ld_const(seq_lens + b);
         return t < 0 ? 0 : (t > T ? T : t);
     }
     // Element offset of logical block j of key/value unit (b, k); -1 when the
     // block's page is out of range.
     __device__ __forceinline__ long long block_offset(int b, int k, int j, int d) const {
         if (pages != nullptr) {
-            const int p = pages[(size_t)b * max_pages + j];
+            const int p = ld_const(pages + (size_t)b * max_pages + j);
             if ((unsigned)p >= (unsigned)num_pages) return -1;
             return ((long long)p * H_kv + k) * kBlockTokens * d;
         }
