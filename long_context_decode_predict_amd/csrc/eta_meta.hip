@@ -3,7 +3,7 @@
 // The cached block metadata is what makes the screen O(1) per block
 // (arXiv:2609.20888 abstract; evolve.pub review "Summary": centroid /
 // variance / max-norm). One wave computes one block from a single read of its
-// keys held in registers; a workgroup of 16 waves covers 256 consecutive blocks
+// keys held in registers; a workgroup of 8 waves covers 256 consecutive blocks
 // of one unit and writes the dimension-major centroid tile through LDS, so
 // every dimension's row of the tile leaves as one contiguous 1 KiB run of
 // 16-byte stores.
@@ -33,7 +33,10 @@
 namespace eta {
 namespace {
 
-constexpr int kMetaWaves = 16;
+// 8 waves (each with one block's 16 KiB of key rows in flight) rather than 16:
+// past ~128 KiB in flight per CU the memory system only lengthens its queues
+// (5.30 vs 5.36 ms at the headline, same process; 4 waves: 6.22 ms).
+constexpr int kMetaWaves = 8;
 constexpr int kMetaBlocksPerGroup = 256;
 
 typedef float f32x4_st __attribute__((ext_vector_type(4)));
