@@ -43,7 +43,10 @@
  *     where nblk_cap = eta_nblk_cap(T_cap) = ceil(T_cap/64) rounded up to a
  *     multiple of 4. K and V (or their pools) start on a 16-byte boundary;
  *     bfloat16 with d = 64 needs only 8 bytes, except for K under grouped
- *     heads in the attention calls.
+ *     heads in the attention calls. Every other array starts on a 4-byte
+ *     boundary at least (the attention calls check q, tau, adm_idx and
+ *     adm_cnt: they are read with scalar loads where the index is the same
+ *     across a wave).
  *   - Block beta of a unit covers tokens [64*beta, min(T_b, 64*beta + 64)) of
  *     its row b (T_b = seq_lens[b], or T); the last block may be partial.
  *     Tokens at or beyond T_b are never read. Block metadata, admitted lists

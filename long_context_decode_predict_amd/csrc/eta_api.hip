@@ -122,7 +122,7 @@ eta_status check_attn(const eta_shape *s, const eta_params *p, const int32_t *ad
     eta_status st = check_shape(s);
     if (st != ETA_OK) return st;
     if ((st = check_params(p)) != ETA_OK) return st;
-    if (adm_cnt == nullptr || out == nullptr) return ETA_ERR_INVALID_ARG;
+    if (adm_cnt == nullptr || out == nullptr || !aligned(adm_cnt, 4)) return ETA_ERR_INVALID_ARG;
     const size_t need = eta_decode_attn_workspace_size(s, p);
     if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return ETA_ERR_WORKSPACE;
     long long mc = ceil_div(ceil_div(s->T_cap, kBlock), split_of(s, p));
@@ -139,6 +139,8 @@ eta_status check_attn_operands(const eta_shape *s, const float *q, const void *K
     if (q == nullptr || K == nullptr || V == nullptr || tau == nullptr || adm_idx == nullptr)
         return ETA_ERR_INVALID_ARG;
     if (!kv_aligned(s, K) || !kv_aligned(s, V)) return ETA_ERR_INVALID_ARG;
+    // read with scalar loads where the index is wave-uniform: whole words only
+    if (!aligned(q, 4) || !aligned(tau, 4) || !aligned(adm_idx, 4)) return ETA_ERR_INVALID_ARG;
     // grouped heads with bf16 K read whole 16-byte chunks of every row (d = 64 too)
     const bool grouped = kv_heads_of(s) < s->H;
     if (grouped && s->kv_dtype == ETA_BF16 && !aligned(K, 16)) return ETA_ERR_INVALID_ARG;
@@ -378,7 +380,7 @@ eta_status eta_decode_attn_noalloc(const eta_shape *s, const float *q, const voi
     eta_status st = check_shape(s);
     if (st != ETA_OK) return st;
     if ((st = check_params(p)) != ETA_OK) return st;
-    if (adm_cnt == nullptr || out == nullptr) return ETA_ERR_INVALID_ARG;
+    if (adm_cnt == nullptr || out == nullptr || !aligned(adm_cnt, 4)) return ETA_ERR_INVALID_ARG;
     if ((st = check_attn_operands(s, q, K, V, tau, adm_idx)) != ETA_OK) return st;
     if (eta_decode_attn_workspace_size(s, p) > ETA_NOALLOC_SCRATCH_BYTES) return ETA_ERR_WORKSPACE;
     void *ws = nullptr;

@@ -195,6 +195,9 @@ def test_decode_attn_errors(L):
     assert call(q=None) == INV
     assert call(K=FAKE + 8) == INV
     assert call(cnt=None) == INV
+    # arrays read with scalar loads (wave-uniform index) must be word aligned
+    for name in ("q", "tau", "idx", "cnt"):
+        assert call(**{name: FAKE + 2}) == INV, name
     assert L.eta_decode_attn(BY(shape(d=48)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, BY(p), FAKE,
                              None, FAKE, need, None) == UNS
     # bf16, d = 64: rows are 8-byte aligned, but grouped heads read K in 16-byte chunks
@@ -223,6 +226,8 @@ def test_decode_attn_noalloc_errors(L):
     assert call(cnt=None) == INV
     assert call(idx=None) == INV
     assert call(K=FAKE + 8) == INV
+    assert call(tau=FAKE + 2) == INV
+    assert call(cnt=FAKE + 2) == INV
     assert call(sh=BY(shape(d=48))) == UNS
     assert L.eta_decode_attn_noalloc(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
                                      None) == INV
