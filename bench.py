@@ -564,7 +564,7 @@ def bench_prefill(args, w):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 (q.k), fp16 (p.v), f32 accumulate",
-        "data": "synthetic (seeded clustered keys; see DESIGN.md)",
+        "data": "synthetic (seeded: per-block key clusters, N(0,1) values and queries, planted needles where the workload has them)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
                    "T_q": w.T_q, "T_k": w.T_k, "gate": "hard" if args.hard else "sigmoid",
                    "parallelism": "single GPU"},
@@ -671,8 +671,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the step is data-parallel over (batch, head) units; see DESIGN.md for how it "
-              "would shard)", file=sys.stderr)
+              "(the step is data-parallel over (batch, head) units: it shards by batch or "
+              "head with no exchange, or by sequence with one exchange of the per-unit "
+              "(max, sum, output) partials before the combine)", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe > 0:
         copy_probe(args.copy_probe, args.steps)
@@ -845,7 +846,7 @@ def main():
         "vs_baseline": None,
         "dtype": ("bf16 MFMA on split fp32 operands, f32 accumulate"
                   if w.G > 1 and w.kv_dtype == torch.bfloat16 else "f32"),
-        "data": "synthetic (seeded clustered keys; see DESIGN.md)",
+        "data": "synthetic (seeded: per-block key clusters, N(0,1) values and queries, planted needles where the workload has them)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
                    "T": w.T, "paged": w.paged, "var_len": w.var_len,
                    "tokens_cached": int(sum(lens)),
