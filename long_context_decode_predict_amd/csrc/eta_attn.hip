@@ -59,10 +59,12 @@ constexpr int kAttnWaves = 4;
 // Persistent workgroups per CU: the memory system saturates at about 64-128 KiB
 // in flight per CU, and more only lengthens its queues (a read kernel with 16
 // waves x 16 KiB per CU streams ~7 % slower than 8 x 16 KiB). One workgroup of
-// four waves at d = 128 keeps up to 4 x 32 KiB of K/V tiles in flight; d = 64
-// rows are half as long, so two.
-constexpr int kWorkersPerCU128 = 1;
-constexpr int kWorkersPerCU64 = 2;
+// four waves keeps up to 4 x 32 KiB of K/V tiles in flight on the multi-head
+// path, except with bf16 rows of 64, whose tile pair is 16 KiB: two workgroups
+// there (B = 64, 128K: 1.96 vs 2.36 ms with one). The grouped-head path runs
+// fastest with one at d = 64 and 128 alike (G = 8: 0.652 vs 0.671 ms at d = 64).
+constexpr int kWorkersPerCU = 1;
+constexpr int kWorkersPerCUSmallTiles = 2;
 
 struct AttnArgs {
     int units, G, nblk, nblk_cap, split, ws_chunks;  // units: key/value units
@@ -1173,7 +1175,8 @@ hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K,
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
         return e;
-    long long workers = (long long)cus * (g.d == 128 ? kWorkersPerCU128 : kWorkersPerCU64);
+    const bool small_tiles = g.G == 1 && g.bf16 && g.d == 64;
+    long long workers = (long long)cus * (small_tiles ? kWorkersPerCUSmallTiles : kWorkersPerCU);
     const long long most = (long long)g.kv_units * ((g.nblk + split_blocks - 1) / split_blocks);
     if (workers > most) workers = most > 0 ? most : 1;
     const int wk = (int)workers;
