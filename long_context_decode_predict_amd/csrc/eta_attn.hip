@@ -9,10 +9,10 @@
 // Work decomposition. A unit's ascending admitted list is cut into work items
 // of `split` blocks. A plan kernel (one workgroup per 64 units) scans the
 // per-unit item counts into a compacted item list (and settles empty units
-// directly); a persistent
-// grid of a few workgroups per CU then takes items from the list through a
-// device-scope ticket counter, so no workgroup is launched for an absent item
-// and the load balances itself whatever the per-unit densities. A workgroup of
+// directly); a persistent grid of one workgroup per CU (two for the smallest
+// tiles) then takes items from the list through a device-scope ticket counter,
+// so no workgroup is launched for an absent item and the load balances itself
+// whatever the per-unit densities. A workgroup of
 // four waves processes one item at a time; wave w walks the item's blocks
 // w, w+4, ... in tiles of TS tokens:
 //   - row r of the wave owns one token and lane c of the row the EPL = d/16
