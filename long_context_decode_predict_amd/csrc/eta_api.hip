@@ -229,6 +229,7 @@ const char *eta_status_string(eta_status st) {
         case ETA_ERR_UNSUPPORTED: return "ETA_ERR_UNSUPPORTED";
         case ETA_ERR_WORKSPACE: return "ETA_ERR_WORKSPACE";
         case ETA_ERR_HIP: return "ETA_ERR_HIP";
+        case ETA_STATUS_MAX_ENUM: break;  // a range guard, not a status
     }
     return "ETA_ERR_UNKNOWN";
 }
