@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kPredThreads) void predict_tau_kernel(
     const int wave = threadIdx.x / kWave;
 
     if (W == nullptr) {
-        if (threadIdx.x < nh) tau[(size_t)b * H + h0 + threadIdx.x] = bias[h0 + threadIdx.x];
+        if ((int)threadIdx.x < nh) tau[(size_t)b * H + h0 + threadIdx.x] = bias[h0 + threadIdx.x];
         return;
     }
 
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kPredThreads) void predict_tau_kernel(
         if (lane == 0) part[wave][j] = r;
     }
     __syncthreads();
-    if (threadIdx.x < nh) {
+    if ((int)threadIdx.x < nh) {
         float t = bias[h0 + threadIdx.x];
         float s = 0.f;
 #pragma unroll

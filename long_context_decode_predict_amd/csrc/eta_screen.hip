@@ -458,7 +458,7 @@ __global__ __launch_bounds__(kGroupMaxWaves *kWave) void screen_group_kernel(Scr
     }
 #pragma unroll
     for (int j = 0; j < G; ++j)
-        if (threadIdx.x == j) a.adm_cnt[u0 + j] = base[j];
+        if ((int)threadIdx.x == j) a.adm_cnt[u0 + j] = base[j];
     if (with_union && threadIdx.x == 0) a.uni_cnt[ukv] = base_u;
 }
 
