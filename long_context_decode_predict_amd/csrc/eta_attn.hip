@@ -1170,7 +1170,7 @@ hipError_t launch_attn_partial(const Geometry &g, const float *q, const void *K,
                        dim3(kPlanThreads), 0, st, a, g.d, g.G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // persistent workers: a few per CU, never more than the largest possible item count
+    // persistent workers: one or two per CU, never more than the largest possible item count
     int dev = 0, cus = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
