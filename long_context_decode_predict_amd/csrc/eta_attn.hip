@@ -20,7 +20,9 @@
 //     four whole token rows; every load is a uniform block base plus a fixed
 //     per-lane offset plus an immediate, so no per-load address arithmetic;
 //   - software pipeline per wave: the V tile of tile t and the K tile of tile
-//     t+1 are in flight while tile t's logits and weighted values are formed;
+//     t+1 are in flight while tile t's logits and weighted values are formed,
+//     and the scalar reads that locate the tiles run ahead of them (list
+//     entries two blocks ahead, page ids one block ahead);
 //   - dot products reduce over the 16 lanes of a DPP row; the gated logits of
 //     a whole tile are formed first, so the running (max, sum, weighted V)
 //     state is rescaled once per tile, not per token.
@@ -184,14 +186,30 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
     }
 
-    // Element offset of tile tt and the number of its rows below the row's length
-    // (TS or more for every tile but a partial last block's; 0 for a bad page or
-    // an id outside the row's blocks).
-    auto tile_at = [&](int tt, size_t &off, int &valid) {
-        const int blk = ld_const(iu + j0 + wave + (tt / TPB) * kAttnWaves);
-        const long long bo =
-            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
-        const int sub = (tt % TPB) * TS;
+    // The scalar reads that locate a tile run ahead of its K loads: list entries
+    // two blocks ahead, page ids one block ahead (page_of issues the read, base_of
+    // first uses its value a tile later), so no scalar round trip stands between a
+    // tile's logits and the next tile's K loads. blk_id: the wave's k-th block (-1
+    // past its last); page_of: page id of a block (the block id itself when dense,
+    // -1 outside the row's blocks); base_of: element offset of a block, -1 for a
+    // bad page or an id outside the row; tile_of: offset of a tile and the number
+    // of its rows below the row's length (TS or more for every tile but a partial
+    // last block's; 0 when the block is bad).
+    auto blk_id = [&](int k) { return k < nb ? ld_const(iu + j0 + wave + k * kAttnWaves) : -1; };
+    auto page_of = [&](int blk) -> int {
+        if ((unsigned)blk >= (unsigned)nblk_row) return -1;
+        return a.lay.pages != nullptr ? ld_const(a.lay.pages + (size_t)rb * a.lay.max_pages + blk) : blk;
+    };
+    auto base_of = [&](int blk, int pg) -> long long {
+        if ((unsigned)blk >= (unsigned)nblk_row) return -1;
+        if (a.lay.pages != nullptr) {
+            return (unsigned)pg < (unsigned)a.lay.num_pages
+                       ? ((long long)pg * a.lay.H_kv + kh) * kBlockTokens * D : -1;
+        }
+        return a.lay.block_offset(rb, kh, blk, D);
+    };
+    auto tile_of = [&](int blk, long long bo, int part, size_t &off, int &valid) {
+        const int sub = part * TS;
         off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * ROW;
         valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
     };
@@ -199,11 +217,17 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     RowLoad<KV, EPL> kb[L], vb[L];
     size_t next_off = 0;
     int next_valid = 0;
+    int blk_c = -1, blk_n = -1, blk_nn = -1;  // block of the last K tile, the next two
+    int pg_n = -1;
+    long long bo_c = -1;
     if (ntiles > 0) {
-        tile_at(0, next_off, next_valid);
+        blk_c = blk_id(0);
+        bo_c = base_of(blk_c, page_of(blk_c));
+        tile_of(blk_c, bo_c, 0, next_off, next_valid);
         const KV *p = Kp + next_off + lane_off;
 #pragma unroll
         for (int i = 0; i < L; ++i) kb[i].load(p + i * 4 * ROW);
+        blk_n = blk_id(1);
     }
     for (int tt = 0; tt < ntiles; ++tt) {
         const size_t base = next_off;
@@ -212,6 +236,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
             const KV *p = Vp + base + lane_off;
 #pragma unroll
             for (int i = 0; i < L; ++i) vb[i].load(p + i * 4 * ROW);
+        }
+        const bool cross = (tt + 1) % TPB == 0;  // the next K tile starts a new block
+        if (cross && tt + 1 < ntiles) {
+            pg_n = page_of(blk_n);
+            blk_nn = blk_id((tt + 1) / TPB + 1);
         }
         // gated logits of the tile, per head
         float sg[G][L];
@@ -244,7 +273,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         }
         // the K registers are free: start the next tile's K loads
         if (tt + 1 < ntiles) {
-            tile_at(tt + 1, next_off, next_valid);
+            if (cross) {
+                bo_c = base_of(blk_n, pg_n);
+                blk_c = blk_n;
+                blk_n = blk_nn;
+            }
+            tile_of(blk_c, bo_c, (tt + 1) % TPB, next_off, next_valid);
             const KV *p = Kp + next_off + lane_off;
 #pragma unroll
             for (int i = 0; i < L; ++i) kb[i].load(p + i * 4 * ROW);
