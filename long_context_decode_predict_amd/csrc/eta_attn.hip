@@ -197,16 +197,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
     // last block's; 0 when the block is bad).
     auto blk_id = [&](int k) { return k < nb ? ld_const(iu + j0 + wave + k * kAttnWaves) : -1; };
     auto page_of = [&](int blk) -> int {
-        if ((unsigned)blk >= (unsigned)nblk_row) return -1;
-        return a.lay.pages != nullptr ? ld_const(a.lay.pages + (size_t)rb * a.lay.max_pages + blk) : blk;
+        return (unsigned)blk < (unsigned)nblk_row ? a.lay.page_of(rb, blk) : -1;
     };
     auto base_of = [&](int blk, int pg) -> long long {
-        if ((unsigned)blk >= (unsigned)nblk_row) return -1;
-        if (a.lay.pages != nullptr) {
-            return (unsigned)pg < (unsigned)a.lay.num_pages
-                       ? ((long long)pg * a.lay.H_kv + kh) * kBlockTokens * D : -1;
-        }
-        return a.lay.block_offset(rb, kh, blk, D);
+        return (unsigned)blk < (unsigned)nblk_row ? a.lay.page_offset(rb, kh, pg, D) : -1;
     };
     auto tile_of = [&](int blk, long long bo, int part, size_t &off, int &valid) {
         const int sub = part * TS;

@@ -138,15 +138,25 @@ struct KVLayout {
         const int t = ld_const(seq_lens + b);
         return t < 0 ? 0 : (t > T ? T : t);
     }
+    // Where logical block j of row b lives: its page id (paged), or j itself
+    // (dense). Split from page_offset so that a caller can read the page table
+    // well before it needs the address.
+    __device__ __forceinline__ int page_of(int b, int j) const {
+        return pages != nullptr ? ld_const(pages + (size_t)b * max_pages + j) : j;
+    }
+    // Element offset of key/value unit (b, k)'s block at pg (from page_of); -1
+    // when the page id is out of range.
+    __device__ __forceinline__ long long page_offset(int b, int k, int pg, int d) const {
+        if (pages != nullptr) {
+            if ((unsigned)pg >= (unsigned)num_pages) return -1;
+            return ((long long)pg * H_kv + k) * kBlockTokens * d;
+        }
+        return ((long long)(b * H_kv + k) * T_cap + (long long)pg * kBlockTokens) * d;
+    }
     // Element offset of logical block j of key/value unit (b, k); -1 when the
     // block's page is out of range.
     __device__ __forceinline__ long long block_offset(int b, int k, int j, int d) const {
-        if (pages != nullptr) {
-            const int p = ld_const(pages + (size_t)b * max_pages + j);
-            if ((unsigned)p >= (unsigned)num_pages) return -1;
-            return ((long long)p * H_kv + k) * kBlockTokens * d;
-        }
-        return ((long long)(b * H_kv + k) * T_cap + (long long)j * kBlockTokens) * d;
+        return page_offset(b, k, page_of(b, j), d);
     }
 };
 
