@@ -372,6 +372,44 @@ def density_sweep(step, data, w, meta, W, params, lens, steps, fused):
     return out
 
 
+def kv_pair_probe(K: torch.Tensor, V: torch.Tensor, reps: int = 3) -> float:
+    """GB/s of a plain read of the attention's own K and V buffers, chunk c of both
+    together (libeta_probe.so eta_probe_pair_read: the attention's access pattern
+    without its arithmetic, over every block). Two buffers read together stream
+    faster or slower depending on where the driver placed them relative to each
+    other, which a one-buffer read does not show; this is the ceiling that
+    placement allows."""
+    import ctypes
+
+    from long_context_decode_predict_amd.build import PROBE_LIB_PATH
+
+    L = ctypes.CDLL(PROBE_LIB_PATH)
+    L.eta_probe_pair_read.restype = ctypes.c_int
+    L.eta_probe_pair_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    assert K.is_contiguous() and V.is_contiguous() and K.numel() == V.numel()
+    nbytes = K.numel() * K.element_size() // 16384 * 16384
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def go():
+        rc = L.eta_probe_pair_read(K.data_ptr(), V.data_ptr(), nbytes, sink.data_ptr(),
+                                   stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"eta_probe_pair_read returned {rc}")
+    go()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        go()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    log(f"[bench] K/V pair read probe: {gbs:.0f} GB/s")
+    return gbs
+
+
 def read_probe(gib: float = 16.0, reps: int = 5) -> dict:
     """GB/s that a plain streaming read kernel (libeta_probe.so: the kernels' 16-byte
     loads, one 32 KiB chunk per workgroup) sustains in this process and machine
@@ -740,6 +778,7 @@ def main():
     timing = time_steps(step, data, w, meta, W, bias, args.steps, args.warmup, fused)
     ms, attn_ms, front_ms, comb_ms = timing.ms, timing.attn_ms, timing.front_ms, timing.comb_ms
     probe_after = None if args.no_probe else read_probe()
+    kv_probe = None if args.no_probe else kv_pair_probe(*kv_of(data))
     graph_ms = graph_step_ms(step, data, w, meta, W, bias, args.steps, fused)
     cnt = step.adm_cnt.cpu().numpy()      # per query head
     idx = step.adm_idx.cpu().numpy()
@@ -796,6 +835,10 @@ def main():
             "before_timed_steps": probe_before, "after_timed_steps": probe_after,
             "what": "plain streaming read kernel, 16-byte loads, 32 KiB per workgroup, "
                     "16 GiB x 5 reads, same process (libeta_probe.so)"}
+        extra["kv_pair_read_gbs"] = {
+            "value": kv_probe,
+            "what": "plain read of this run's own K and V buffers, 16 KiB chunk c of both "
+                    "per workgroup, every block, 3 reads (libeta_probe.so)"}
 
     if not args.no_frontier:
         extra["screen_frontier"] = screen_frontier(step, data, w, meta, W, bias, params, lens,
@@ -833,6 +876,10 @@ def main():
         practical = max(probe_before["nt"], probe_after["nt"])
         roofline["practical_peak"] = practical
         roofline["frac_of_practical"] = attn_gbs / practical
+        # the same read of the attention's own K and V buffers, whose relative
+        # physical placement moves the rate of two-buffer reads by several percent
+        roofline["kv_pair_read"] = kv_probe
+        roofline["frac_of_kv_pair_read"] = attn_gbs / kv_probe
     result = {
         "metric": METRIC,
         "value": 1000.0 / ms,

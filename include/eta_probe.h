@@ -14,6 +14,18 @@
  * buf: device pointer, 16-byte aligned; bytes: a non-zero multiple of 32768
  * (at most 2^31 - 1 chunks). Enqueues one launch on `stream` and returns 0;
  * -1 for invalid arguments (nothing enqueued), -4 if the launch fails.
+ *
+ * eta_probe_pair_read: the decode attention's access pattern stripped of its
+ * arithmetic: workgroup c of 256 threads reads 16 KiB chunk c of `a` and chunk c
+ * of `b` together (non-temporal 16-byte loads), as the attention reads the K and
+ * V rows of one block, and folds them like eta_probe_stream_read. Run on the
+ * attention's own K and V buffers it gives the rate their physical placement
+ * allows: two buffers read together can stream several percent slower or
+ * faster depending on where the driver placed them, which one buffer read alone
+ * does not show. a, b: device pointers, 16-byte aligned, each at least `bytes`
+ * long; bytes: a non-zero multiple of 16384 (at most 2^31 - 1 chunks); sink as
+ * above. Enqueues one launch on `stream` and returns 0; -1 for invalid
+ * arguments (nothing enqueued), -4 if the launch fails.
  */
 #ifndef ETA_PROBE_H
 #define ETA_PROBE_H
@@ -29,6 +41,8 @@ extern "C" {
 
 int eta_probe_stream_read(const void *buf, size_t bytes, int nontemporal, uint32_t *sink,
                           hipStream_t stream);
+int eta_probe_pair_read(const void *a, const void *b, size_t bytes, uint32_t *sink,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -3,6 +3,7 @@ behind the reported rooflines, and the validity check of the committed counter
 summaries."""
 import dataclasses
 import os
+import re
 import subprocess
 import sys
 
@@ -104,12 +105,18 @@ def test_cpu_baseline_threads_and_host_counts():
 
 def test_read_probe_library_exports_and_rejects_bad_sizes():
     """libeta_probe.so is built beside libeta.so and refuses invalid arguments before
-    any launch (a size that is not whole 32 KiB chunks, null or misaligned pointers)."""
+    any launch (a size that is not whole chunks, null or misaligned pointers)."""
     import ctypes
 
     from long_context_decode_predict_amd.build import PROBE_LIB_PATH, ensure_built
     ensure_built()
     L = ctypes.CDLL(PROBE_LIB_PATH)
+    text = open(os.path.join(os.path.dirname(PROBE_LIB_PATH), "..", "include", "eta_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(eta_probe_\w+)\s*\(", text, flags=re.M)))
+    assert declared == ["eta_probe_pair_read", "eta_probe_stream_read"], declared
+    for n in declared:
+        assert hasattr(L, n), n
     f = L.eta_probe_stream_read
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
@@ -120,3 +127,13 @@ def test_read_probe_library_exports_and_rejects_bad_sizes():
     assert f(None, 32768, 1, fake, None) == -1
     assert f(fake, 32768, 0, None, None) == -1
     assert f(fake + 8, 32768, 1, fake, None) == -1
+    g = L.eta_probe_pair_read
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    assert g(fake, fake, 16384 + 16, fake, None) == -1
+    assert g(fake, fake, 0, fake, None) == -1
+    assert g(None, fake, 16384, fake, None) == -1
+    assert g(fake, None, 16384, fake, None) == -1
+    assert g(fake, fake, 16384, None, None) == -1
+    assert g(fake, fake + 8, 16384, fake, None) == -1
