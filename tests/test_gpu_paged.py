@@ -14,6 +14,7 @@ import torch
 from gpu_util import Case, compare_gqa_units, compare_units, kv_host
 from long_context_decode_predict_amd import _lib, workloads
 from long_context_decode_predict_amd.build import ensure_built
+from long_context_decode_predict_amd.decode import DecodeStep
 from oracle import oracle as oracle_mod
 
 pytestmark = pytest.mark.gpu
@@ -215,4 +216,34 @@ def test_paged_graph_follows_layout_updates():
     st = compare_units(case, range(w.B * w.H))
     assert st["band_mismatch_units"] <= 1
     del graph
+    case.free()
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_interleaved_pages_in_one_buffer(G):
+    """K and V pools may share one allocation with their pages interleaved: K page p
+    at even page 2p, V page p right after it (V pointer = K pointer + one page, page
+    ids doubled). The metadata, the screen and the attention read through the same
+    page table, so every result equals the separate-pool run bitwise."""
+    _announce(f"interleaved pool pages G={G}")
+    w = workloads.custom("ip", B=3, H=4 * G, H_kv=4, d=128, T=5000, kv_dtype=torch.bfloat16,
+                         seed=251 + G)
+    lens = [5000, 1, 3333]
+    case = Case(w, seq_lens=lens, paged=True, fused=True).run()
+    ref = {k: v.clone() for k, v in _results(case).items()}
+    Kp, Vp = case.kv()
+    P = Kp.shape[0]
+    buf = torch.empty((2 * P + 1,) + tuple(Kp.shape[1:]), dtype=Kp.dtype, device="cuda")
+    buf[0:2 * P:2] = Kp
+    buf[1:2 * P:2] = Vp
+    buf[2 * P] = float("nan")
+    tab = case.layout.page_table
+    case.layout = _lib.KVLayout(case.layout.seq_lens,
+                                torch.where(tab >= 0, tab * 2, tab).to(torch.int32).contiguous())
+    case.data["Kp"], case.data["Vp"] = buf[0:2 * P], buf[1:2 * P + 1]
+    case.meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, case.T_cap)
+    case.step = DecodeStep(w.B, w.H, w.d, case.T_cap, w.kv_dtype, case.params, with_bounds=True,
+                           H_kv=w.kv_heads, layout=case.layout)
+    case.run()
+    _assert_same(ref, _results(case), case)
     case.free()
