@@ -30,7 +30,9 @@
  *     head h / G, G = H / H_kv.
  *   - Layouts (query unit u = b*H + h, key/value unit k = b*H_kv + h/G):
  *       q         float32 [B][H][d]        post-RoPE query (RoPE is the caller's)
- *       K, V      [B][H_kv][T_cap][d]      float32 or bfloat16 (kv_dtype)
+ *       K, V      [B][H_kv][T_cap][d]      float32 or bfloat16 (kv_dtype);
+ *                 with kv_block_stride, blocks of 64 rows kv_block_stride
+ *                 elements apart (e.g. K and V interleaved block by block)
  *       tau       float32 [B][H]
  *       centroid  float32 [B][H_kv][d][nblk_cap]   dimension-major per unit
  *       var       float32 [B][H_kv][nblk_cap]
@@ -117,6 +119,19 @@ typedef struct {
                                   counting both (measured 2-4 % faster than
                                   two separate pools)                        */
     int num_pages;             /* pages in the K/V pools (page_table only)   */
+    int kv_block_stride;       /* dense layout only: elements from one
+                                  64-token block of a key/value unit to the
+                                  next, so block j of unit u starts at
+                                  (u*T_cap/64 + j)*kv_block_stride; 0 means
+                                  64*d (rows back to back). A positive
+                                  multiple of 64*d otherwise; 128*d with V =
+                                  K + 64*d keeps K and V interleaved block by
+                                  block in one allocation, which streams at
+                                  the same rate wherever the driver places it
+                                  (two separate K and V allocations read
+                                  together stream faster or slower by several
+                                  percent depending on their relative
+                                  placement). Must be 0 with a page_table.   */
 } eta_shape;
 
 typedef struct {

@@ -40,7 +40,7 @@ class eta_shape(ctypes.Structure):
                 ("T", ctypes.c_int), ("T_cap", ctypes.c_int), ("block", ctypes.c_int),
                 ("kv_dtype", ctypes.c_int), ("H_kv", ctypes.c_int),
                 ("seq_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
-                ("num_pages", ctypes.c_int)]
+                ("num_pages", ctypes.c_int), ("kv_block_stride", ctypes.c_int)]
 
 
 class eta_meta(ctypes.Structure):
@@ -187,9 +187,11 @@ class KVLayout:
 
 
 def make_shape(B, H, d, T, T_cap, kv_dtype: torch.dtype, H_kv: int = 0,
-               layout: KVLayout | None = None, num_pages: int = 0) -> eta_shape:
+               layout: KVLayout | None = None, num_pages: int = 0,
+               block_stride: int = 0) -> eta_shape:
     s = eta_shape(int(B), int(H), int(d), int(T), int(T_cap), BLOCK, kv_code(kv_dtype),
                   int(H_kv))
+    s.kv_block_stride = int(block_stride)
     if layout is not None:
         if layout.seq_lens is not None:
             _need(layout.seq_lens, "seq_lens", torch.int32, (B,))
@@ -201,9 +203,28 @@ def make_shape(B, H, d, T, T_cap, kv_dtype: torch.dtype, H_kv: int = 0,
     return s
 
 
+def kv_block_view(K: torch.Tensor) -> bool:
+    """True for a dense cache given block by block: a 5-d view [B, H_kv, T_cap/64, 64, d]
+    whose 64-row blocks lie K.stride(2) elements apart (for example K = kv[..., 0, :, :]
+    and V = kv[..., 1, :, :] of kv [B, H_kv, T_cap/64, 2, 64, d], K and V interleaved
+    block by block in one allocation)."""
+    return K.dim() == 5
+
+
+def kv_block_stride(K: torch.Tensor) -> int:
+    """eta_shape.kv_block_stride of a K/V tensor: 0 for a 4-d cache or pool."""
+    return int(K.stride(2)) if kv_block_view(K) else 0
+
+
 def kv_dims(K: torch.Tensor, layout: KVLayout | None = None):
-    """(B, H_kv, T_cap, d, num_pages) of a dense [B,H_kv,T_cap,d] cache, or of a page
-    pool [num_pages,H_kv,64,d] addressed through layout.page_table [B, T_cap/64]."""
+    """(B, H_kv, T_cap, d, num_pages) of a dense [B,H_kv,T_cap,d] cache (or its 5-d block
+    view, see kv_block_view), or of a page pool [num_pages,H_kv,64,d] addressed through
+    layout.page_table [B, T_cap/64]."""
+    if kv_block_view(K):
+        if layout is not None and layout.paged:
+            raise ValueError("a block view of K/V is a dense layout; a page pool is 4-d")
+        B, H_kv, nb, blk, d = K.shape
+        return B, H_kv, nb * blk, d, 0
     if K.dim() != 4:
         raise ValueError("K/V must be 4-d: [B,H_kv,T_cap,d] or a page pool [P,H_kv,64,d]")
     if layout is not None and layout.paged:
@@ -221,7 +242,7 @@ def kv_dims(K: torch.Tensor, layout: KVLayout | None = None):
 def shape_of(K: torch.Tensor, T: int, layout: KVLayout | None = None) -> eta_shape:
     """Shape descriptor of a multi-head K/V cache holding T tokens."""
     B, H, T_cap, d, P = kv_dims(K, layout)
-    return make_shape(B, H, d, T, T_cap, K.dtype, 0, layout, P)
+    return make_shape(B, H, d, T, T_cap, K.dtype, 0, layout, P, kv_block_stride(K))
 
 
 def default_params(**kw) -> eta_params:
@@ -261,8 +282,20 @@ def _check_meta(meta: Meta, B, H, d, T_cap):
 
 
 def _check_kv(K: torch.Tensor, name="K"):
+    if kv_block_view(K):
+        # [B, H_kv, nblk, 64, d]: rows of a block back to back, blocks of a unit S apart
+        # (S a positive multiple of 64*d), units nblk*S apart
+        B, H_kv, nb, blk, d = K.shape
+        S = K.stride(2)
+        if blk != BLOCK or K.stride(3) != d or K.stride(4) != 1 or S <= 0 \
+                or S % (BLOCK * d) != 0 or K.stride(1) != nb * S or K.stride(0) != H_kv * nb * S:
+            raise ValueError(f"{name} as a block view must be [B,H_kv,T_cap/64,64,d] with "
+                             "blocks a multiple of 64*d elements apart and units packed")
+        _need(K[0, 0, 0], name)  # device tensor
+        kv_code(K.dtype)
+        return
     if K.dim() != 4:
-        raise ValueError(f"{name} must be [B,H,T_cap,d]")
+        raise ValueError(f"{name} must be [B,H,T_cap,d] (or its block view)")
     _need(K, name)
     kv_code(K.dtype)
 
@@ -425,7 +458,8 @@ def attn_shape(q: torch.Tensor, K: torch.Tensor, T: int,
     """Shape of an attention call: H query heads from q, H_kv key/value heads from K."""
     B, H_kv, T_cap, d, P = kv_dims(K, layout)
     H = q.shape[1]
-    return make_shape(B, H, d, T, T_cap, K.dtype, H_kv if H_kv != H else 0, layout, P)
+    return make_shape(B, H, d, T, T_cap, K.dtype, H_kv if H_kv != H else 0, layout, P,
+                      kv_block_stride(K))
 
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # ETA_NOALLOC_SCRATCH_BYTES
@@ -434,8 +468,8 @@ NOALLOC_SCRATCH_BYTES = 128 << 20  # ETA_NOALLOC_SCRATCH_BYTES
 def _attn_checks(q, K, V, T, tau, adm_idx, adm_cnt, out, lse, ws, layout=None):
     _check_kv(K)
     _check_kv(V, "V")
-    if V.shape != K.shape or V.dtype != K.dtype:
-        raise ValueError("K and V must have the same shape and dtype")
+    if V.shape != K.shape or V.dtype != K.dtype or V.stride() != K.stride():
+        raise ValueError("K and V must have the same shape, strides and dtype")
     if q.dim() != 3:
         raise ValueError("q must be [B,H,d]")
     s = attn_shape(q, K, T, layout)

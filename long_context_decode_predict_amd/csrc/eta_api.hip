@@ -56,6 +56,10 @@ eta_status check_shape(const eta_shape *s) {
     } else if (s->num_pages != 0) {
         return ETA_ERR_INVALID_ARG;
     }
+    if (s->kv_block_stride < 0) return ETA_ERR_INVALID_ARG;
+    if (s->kv_block_stride > 0 &&
+        (s->page_table != nullptr || s->kv_block_stride % (kBlock * s->d) != 0))
+        return ETA_ERR_INVALID_ARG;
     return ETA_OK;
 }
 
@@ -92,6 +96,7 @@ eta::Geometry geometry(const eta_shape *s, int nblk_cap) {
     g.lay.H_kv = kv_heads_of(s);
     g.lay.max_pages = s->T_cap / kBlock;
     g.lay.num_pages = s->page_table != nullptr ? s->num_pages : 0;
+    g.lay.block_stride = s->kv_block_stride > 0 ? s->kv_block_stride : (long long)kBlock * s->d;
     return g;
 }
 

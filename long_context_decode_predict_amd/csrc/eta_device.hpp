@@ -125,13 +125,16 @@ __device__ __forceinline__ T ld_const(const T *p) {
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
 // ---- where the rows of a key/value unit live ----
-// Dense: K[(b*H_kv + k)][T_cap][d]. Paged: pools [num_pages][H_kv][64][d] and a
-// page table [B][max_pages] (logical block -> page). Rows may hold different
-// numbers of tokens (seq_lens).
+// Dense: block j of unit (b, k) at ((b*H_kv + k)*T_cap/64 + j)*block_stride, its
+// 64 rows of d elements back to back (block_stride = 64*d: K[(b*H_kv + k)][T_cap][d];
+// 128*d with V = K + 64*d: K and V interleaved block by block). Paged: pools
+// [num_pages][H_kv][64][d] and a page table [B][max_pages] (logical block ->
+// page). Rows may hold different numbers of tokens (seq_lens).
 struct KVLayout {
     const int32_t *seq_lens;  // null: every row holds T
     const int32_t *pages;     // null: dense layout
     int T, T_cap, H_kv, max_pages, num_pages;
+    long long block_stride;   // dense layout: elements from one block of a unit to the next
 
     __device__ __forceinline__ int row_len(int b) const {
         if (seq_lens == nullptr) return T;
@@ -151,7 +154,7 @@ struct KVLayout {
             if ((unsigned)pg >= (unsigned)num_pages) return -1;
             return ((long long)pg * H_kv + k) * kBlockTokens * d;
         }
-        return ((long long)(b * H_kv + k) * T_cap + (long long)pg * kBlockTokens) * d;
+        return ((long long)(b * H_kv + k) * (T_cap / kBlockTokens) + pg) * block_stride;
     }
     // Element offset of logical block j of key/value unit (b, k); -1 when the
     // block's page is out of range.

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from long_context_decode_predict_amd import _lib
 from long_context_decode_predict_amd.build import ensure_built
@@ -265,6 +266,37 @@ def test_layout_errors(L):
     assert (L.eta_decode_attn_workspace_size(BY(shape(seq_lens=FAKE, page_table=FAKE,
                                                       num_pages=9)), p)
             == L.eta_decode_attn_workspace_size(BY(shape()), p))
+    # the dense layout's block stride: 0, or a positive multiple of 64*d, no page table
+    for bad in (-64 * 128, 64 * 128 + 8, 64 * 64):
+        assert L.eta_build_block_meta(BY(shape(kv_block_stride=bad)), FAKE, m, None) == INV, bad
+    assert L.eta_build_block_meta(BY(shape(kv_block_stride=128 * 128, page_table=FAKE,
+                                           num_pages=4)), FAKE, m, None) == INV
+    assert L.eta_decode_attn_workspace_size(BY(shape(kv_block_stride=100)), p) == 0
+    assert (L.eta_decode_attn_workspace_size(BY(shape(kv_block_stride=128 * 128)), p)
+            == L.eta_decode_attn_workspace_size(BY(shape()), p))
+    assert (L.eta_decode_attn_workspace_size(BY(shape(d=64, kv_block_stride=64 * 64 * 3)), p)
+            > 0)
+
+
+def test_block_view_binding_checks():
+    """The binding derives kv_block_stride from a 5-d block view of K/V and refuses
+    views whose blocks are not whole multiples of 64*d apart, or whose units are not
+    packed (host-side checks only; the tensors are never handed to the library)."""
+    B, Hk, nb, d = 2, 3, 4, 64
+    kv = torch.empty((B, Hk, nb, 2, 64, d), dtype=torch.bfloat16, device="meta")
+    K, V = kv[:, :, :, 0], kv[:, :, :, 1]
+    assert _lib.kv_block_view(K) and _lib.kv_block_stride(K) == 2 * 64 * d
+    assert _lib.kv_dims(K) == (B, Hk, nb * 64, d, 0)
+    assert _lib.kv_block_stride(torch.empty((B, Hk, nb * 64, d), device="meta")) == 0
+    with pytest.raises(ValueError):  # a block view is a dense layout, not a pool
+        _lib.kv_dims(K, _lib.KVLayout(None, torch.zeros((B, nb), dtype=torch.int32)))
+    for bad in (torch.empty((B, Hk, 64, nb, d), device="meta").transpose(2, 3),  # rows apart
+                torch.empty((B, Hk, nb, 64, d + 8), device="meta")[..., :d],      # padded rows
+                torch.empty((Hk, B, nb, 64, d), device="meta").transpose(0, 1)):  # units apart
+        with pytest.raises(ValueError, match="block view"):
+            _lib._check_kv(bad)
+    with pytest.raises(ValueError, match="device tensor"):  # a good view, but on the host
+        _lib._check_kv(torch.empty((B, Hk, nb, 2, 64, d))[:, :, :, 0])
 
 
 def test_page_pool_round_trip():

@@ -247,3 +247,49 @@ def test_interleaved_pages_in_one_buffer(G):
     case.run()
     _assert_same(ref, _results(case), case)
     case.free()
+
+
+@pytest.mark.parametrize("name,kw,lens", [
+    ("mha_bf16_d128_varlen", dict(B=3, H=4, d=128, T=5000, kv_dtype=torch.bfloat16), [5000, 64, 2999]),
+    ("mha_f32_d64", dict(B=2, H=3, d=64, T=3000, kv_dtype=torch.float32), None),
+    ("gqa4_bf16_d128", dict(B=2, H=16, H_kv=4, d=128, T=4100, kv_dtype=torch.bfloat16), None),
+    ("gqa2_f32_d128_varlen", dict(B=2, H=8, H_kv=4, d=128, T=3000, kv_dtype=torch.float32),
+     [3000, 1]),
+])
+def test_block_interleaved_dense_layout(name, kw, lens):
+    """K and V interleaved block by block in one allocation (kv [B,H_kv,T_cap/64,2,64,d],
+    passed as the block views kv[..., 0, :, :] and kv[..., 1, :, :], kv_block_stride =
+    128*d): the metadata, the screen and the attention equal the run on separate
+    [B,H_kv,T_cap,d] buffers bitwise, and an append equals a rebuild."""
+    _announce(f"block-interleaved {name}")
+    w = workloads.custom(name, seed=261, **kw)
+    case = Case(w, seq_lens=lens, fused=True).run()
+    ref = {k: v.clone() for k, v in _results(case).items()}
+    K, V = case.data["K"], case.data["V"]
+    B, Hk, Tc, d = K.shape
+    nb = Tc // 64
+    kv = torch.empty((B, Hk, nb, 2, 64, d), dtype=K.dtype, device="cuda")
+    kv[:, :, :, 0] = K.view(B, Hk, nb, 64, d)
+    kv[:, :, :, 1] = V.view(B, Hk, nb, 64, d)
+    K5, V5 = kv[:, :, :, 0], kv[:, :, :, 1]
+    assert _lib.kv_block_stride(K5) == 128 * d
+    case.data["Kp"], case.data["Vp"] = K5, V5  # the K, V the library reads
+    for t in (case.step.out, case.step.lse, case.meta.centroid, case.meta.var, case.meta.maxnorm):
+        t.zero_()
+    case.run()
+    _assert_same(ref, _results(case), case)
+    # the block view also serves appends: every row n tokens shorter, then n more
+    n_new = 77 if lens is None else min(lens)
+    grown = _lib.Meta.alloc(B, Hk, d, Tc)
+    lay = case.layout
+    if lay is not None:
+        lay.seq_lens.copy_(torch.tensor([t - n_new for t in lens], dtype=torch.int32))
+    _lib.eta_build_block_meta(K5, w.T - n_new, grown, layout=lay)
+    _lib.eta_append_meta(K5, w.T - n_new, n_new, grown, layout=lay)
+    torch.cuda.synchronize()
+    for bi in range(B):
+        n = (case.row_len(bi) + 63) // 64
+        assert torch.equal(grown.centroid[bi, ..., :n], case.meta.centroid[bi, ..., :n]), bi
+        assert torch.equal(grown.var[bi, :, :n], case.meta.var[bi, :, :n]), bi
+        assert torch.equal(grown.maxnorm[bi, :, :n], case.meta.maxnorm[bi, :, :n]), bi
+    case.free()
