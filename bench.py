@@ -109,8 +109,29 @@ def meta_bytes(w, lens):
 
 
 def kv_of(data):
-    """The K, V the library reads: page pools for a paged workload, else the cache."""
-    return (data["Kp"], data["Vp"]) if "Kp" in data else (data["K"], data["V"])
+    """The K, V the library reads: page pools for a paged workload, the block views of
+    the interleaved cache, else the separate K and V buffers."""
+    if "Kp" in data:
+        return data["Kp"], data["Vp"]
+    if "Kb" in data:
+        return data["Kb"], data["Vb"]
+    return data["K"], data["V"]
+
+
+def interleave_kv(data):
+    """Move a dense cache into one allocation with K and V interleaved block by block
+    (kv [B, H_kv, T_cap/64, 2, 64, d], read through the block views kv[..., 0, :, :]
+    and kv[..., 1, :, :]) and drop the separate K and V buffers."""
+    K, V = data["K"], data["V"]
+    B, Hk, Tc, d = K.shape
+    nb = Tc // 64
+    kv = torch.empty((B, Hk, nb, 2, 64, d), dtype=K.dtype, device=K.device)
+    for b in range(B):  # row by row: no second full-size copy at once
+        kv[b, :, :, 0] = K[b].view(Hk, nb, 64, d)
+        kv[b, :, :, 1] = V[b].view(Hk, nb, 64, d)
+    data["K"] = data["V"] = None
+    data["kv"], data["Kb"], data["Vb"] = kv, kv[:, :, :, 0], kv[:, :, :, 1]
+    torch.cuda.empty_cache()
 
 
 def run_steps(step, data, w, meta, W, bias, n, stream, evs=None, fused=True):
@@ -237,11 +258,7 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, lens, max_units=256, thr
     for u in units:
         b, k = divmod(int(u), w.kv_heads)
         T_b = lens[b]
-        if "Kp" in data:  # logical keys of the unit, read through the page table
-            Ku = workloads.gather_unit(data["Kp"], data["table"], b, k, T_b)
-            Vu = workloads.gather_unit(data["Vp"], data["table"], b, k, T_b)
-        else:
-            Ku, Vu = data["K"][b, k, :T_b], data["V"][b, k, :T_b]
+        Ku, Vu = unit_kv(data, b, k, T_b)
         slabs.append((b, k, host(Ku), host(Vu)))
     threads = threads or host_threads()
     with ThreadPoolExecutor(threads) as ex:
@@ -313,10 +330,13 @@ def row_rooflines(w, lens, params, build_ms, front_ms, attn_ms, attn_alg, comb_m
 
 
 def unit_kv(data, b, k, T_b):
-    """Device K, V [T_b, d] of key/value head k of row b, in either layout."""
+    """Device K, V [T_b, d] of key/value head k of row b, in any of the layouts."""
     if "Kp" in data:
         return (workloads.gather_unit(data["Kp"], data["table"], b, k, T_b),
                 workloads.gather_unit(data["Vp"], data["table"], b, k, T_b))
+    if "Kb" in data:  # blocks of the interleaved cache, gathered into rows
+        d = data["Kb"].shape[-1]
+        return (data["Kb"][b, k].reshape(-1, d)[:T_b], data["Vb"][b, k].reshape(-1, d)[:T_b])
     return data["K"][b, k, :T_b], data["V"][b, k, :T_b]
 
 
@@ -372,13 +392,14 @@ def density_sweep(step, data, w, meta, W, params, lens, steps, fused):
     return out
 
 
-def kv_pair_probe(K: torch.Tensor, V: torch.Tensor, reps: int = 3) -> float:
-    """GB/s of a plain read of the attention's own K and V buffers, chunk c of both
-    together (libeta_probe.so eta_probe_pair_read: the attention's access pattern
-    without its arithmetic, over every block). Two buffers read together stream
-    faster or slower depending on where the driver placed them relative to each
-    other, which a one-buffer read does not show; this is the ceiling that
-    placement allows."""
+def kv_read_probe(data, reps: int = 3) -> float:
+    """GB/s of a plain read of the attention's own K and V buffers (libeta_probe.so):
+    chunk c of K and of V together (eta_probe_pair_read) for separate buffers or page
+    pools, the one buffer streamed (eta_probe_stream_read) for the block-interleaved
+    cache, every block in both cases: the attention's access pattern without its
+    arithmetic. Two separate buffers read together stream faster or slower depending
+    on where the driver placed them relative to each other, which a one-buffer read
+    does not show; this is the ceiling that the placement allows."""
     import ctypes
 
     from long_context_decode_predict_amd.build import PROBE_LIB_PATH
@@ -387,26 +408,40 @@ def kv_pair_probe(K: torch.Tensor, V: torch.Tensor, reps: int = 3) -> float:
     L.eta_probe_pair_read.restype = ctypes.c_int
     L.eta_probe_pair_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p, ctypes.c_void_p]
-    assert K.is_contiguous() and V.is_contiguous() and K.numel() == V.numel()
-    nbytes = K.numel() * K.element_size() // 16384 * 16384
+    L.eta_probe_stream_read.restype = ctypes.c_int
+    L.eta_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if "kv" in data:
+        kv = data["kv"]
+        nbytes = kv.numel() * kv.element_size() // 32768 * 32768
+        total = nbytes
 
-    def go():
-        rc = L.eta_probe_pair_read(K.data_ptr(), V.data_ptr(), nbytes, sink.data_ptr(),
-                                   stream.cuda_stream)
-        if rc != 0:
-            raise RuntimeError(f"eta_probe_pair_read returned {rc}")
-    go()
+        def go():
+            return L.eta_probe_stream_read(kv.data_ptr(), nbytes, 1, sink.data_ptr(),
+                                           stream.cuda_stream)
+    else:
+        K, V = kv_of(data)
+        assert K.is_contiguous() and V.is_contiguous() and K.numel() == V.numel()
+        nbytes = K.numel() * K.element_size() // 16384 * 16384
+        total = 2 * nbytes
+
+        def go():
+            return L.eta_probe_pair_read(K.data_ptr(), V.data_ptr(), nbytes, sink.data_ptr(),
+                                         stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if go() != 0:
+        raise RuntimeError("K/V read probe refused its arguments")
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(reps):
-        go()
+        if go() != 0:
+            raise RuntimeError("K/V read probe refused its arguments")
     e1.record(stream)
     torch.cuda.synchronize()
-    gbs = 2 * nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
-    log(f"[bench] K/V pair read probe: {gbs:.0f} GB/s")
+    gbs = total / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    log(f"[bench] K/V read probe: {gbs:.0f} GB/s")
     return gbs
 
 
@@ -698,6 +733,9 @@ def main():
     ap.add_argument("--no-frontier", action="store_true",
                     help="skip the screen's recall / density frontier over z and the GEO bound")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--kv-layout", choices=("interleaved", "separate"), default="interleaved",
+                    help="dense cache: K and V interleaved block by block in one allocation "
+                         "(kv_block_stride = 128*d), or two separate [B,H_kv,T_cap,d] buffers")
     ap.add_argument("--hard", action="store_true",
                     help="the hard gate (step at tau) instead of the sigmoid")
     ap.add_argument("--unfused", action="store_true",
@@ -741,6 +779,8 @@ def main():
             data["K"] = data["V"] = None
             torch.cuda.empty_cache()
         layout = _lib.KVLayout(lens_t, table)
+    if not w.paged and args.kv_layout == "interleaved":
+        interleave_kv(data)
     torch.cuda.synchronize()
     log(f"[bench] generated in {time.time() - t0:.1f}s")
     K0 = kv_of(data)[0]
@@ -778,7 +818,7 @@ def main():
     timing = time_steps(step, data, w, meta, W, bias, args.steps, args.warmup, fused)
     ms, attn_ms, front_ms, comb_ms = timing.ms, timing.attn_ms, timing.front_ms, timing.comb_ms
     probe_after = None if args.no_probe else read_probe()
-    kv_probe = None if args.no_probe else kv_pair_probe(*kv_of(data))
+    kv_probe = None if args.no_probe else kv_read_probe(data)
     graph_ms = graph_step_ms(step, data, w, meta, W, bias, args.steps, fused)
     cnt = step.adm_cnt.cpu().numpy()      # per query head
     idx = step.adm_idx.cpu().numpy()
@@ -835,10 +875,11 @@ def main():
             "before_timed_steps": probe_before, "after_timed_steps": probe_after,
             "what": "plain streaming read kernel, 16-byte loads, 32 KiB per workgroup, "
                     "16 GiB x 5 reads, same process (libeta_probe.so)"}
-        extra["kv_pair_read_gbs"] = {
+        extra["kv_read_gbs"] = {
             "value": kv_probe,
-            "what": "plain read of this run's own K and V buffers, 16 KiB chunk c of both "
-                    "per workgroup, every block, 3 reads (libeta_probe.so)"}
+            "what": "plain read of this run's own K and V (16 KiB chunk c of both per "
+                    "workgroup for separate buffers or pools, the one buffer streamed for "
+                    "the block-interleaved cache), every block, 3 reads (libeta_probe.so)"}
 
     if not args.no_frontier:
         extra["screen_frontier"] = screen_frontier(step, data, w, meta, W, bias, params, lens,
@@ -876,10 +917,10 @@ def main():
         practical = max(probe_before["nt"], probe_after["nt"])
         roofline["practical_peak"] = practical
         roofline["frac_of_practical"] = attn_gbs / practical
-        # the same read of the attention's own K and V buffers, whose relative
-        # physical placement moves the rate of two-buffer reads by several percent
-        roofline["kv_pair_read"] = kv_probe
-        roofline["frac_of_kv_pair_read"] = attn_gbs / kv_probe
+        # a plain read of the attention's own K and V, whose placement sets the rate
+        # two separate buffers can be read at together
+        roofline["kv_read"] = kv_probe
+        roofline["frac_of_kv_read"] = attn_gbs / kv_probe
     result = {
         "metric": METRIC,
         "value": 1000.0 / ms,
@@ -896,6 +937,10 @@ def main():
         "data": "synthetic (seeded: per-block key clusters, N(0,1) values and queries, planted needles where the workload has them)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
                    "T": w.T, "paged": w.paged, "var_len": w.var_len,
+                   "kv_layout": ("page pools" if w.paged else
+                                 "K and V interleaved block by block in one buffer"
+                                 if args.kv_layout == "interleaved" else
+                                 "separate K and V buffers"),
                    "tokens_cached": int(sum(lens)),
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",
