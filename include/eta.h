@@ -116,8 +116,7 @@ typedef struct {
                                   from V, so one allocation may hold both
                                   pools with their pages interleaved: V = K +
                                   H_kv*64*d, even page ids only, num_pages
-                                  counting both (measured 2-4 % faster than
-                                  two separate pools)                        */
+                                  counting both                              */
     int num_pages;             /* pages in the K/V pools (page_table only)   */
     int kv_block_stride;       /* dense layout only: elements from one
                                   64-token block of a key/value unit to the
