@@ -278,6 +278,13 @@ def test_block_interleaved_dense_layout(name, kw, lens):
         t.zero_()
     case.run()
     _assert_same(ref, _results(case), case)
+    # and the allocation-free entry point (same kernels and split)
+    s = case.step
+    out, lse = torch.full_like(s.out, float("nan")), torch.full_like(s.lse, float("nan"))
+    _lib.eta_decode_attn_noalloc(case.data["q"], K5, V5, case.T, s.tau, s.uni_idx, s.uni_cnt,
+                                 case.params, out, lse, layout=case.layout)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"])
     # the block view also serves appends: every row n tokens shorter, then n more
     n_new = 77 if lens is None else min(lens)
     grown = _lib.Meta.alloc(B, Hk, d, Tc)
