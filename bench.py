@@ -734,8 +734,9 @@ def main():
                     help="skip the screen's recall / density frontier over z and the GEO bound")
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--kv-layout", choices=("interleaved", "separate"), default="interleaved",
-                    help="dense cache: K and V interleaved block by block in one allocation "
-                         "(kv_block_stride = 128*d), or two separate [B,H_kv,T_cap,d] buffers")
+                    help="K and V interleaved block by block in one allocation "
+                         "(kv_block_stride = 128*d; dense cache or page pool), or two "
+                         "separate buffers / pools")
     ap.add_argument("--hard", action="store_true",
                     help="the hard gate (step at tau) instead of the sigmoid")
     ap.add_argument("--unfused", action="store_true",
@@ -773,8 +774,10 @@ def main():
         lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda") if w.var_len > 0 else None
         table = None
         if w.paged:  # move the cache into a shuffled page pool and drop the dense copy
-            table, data["Kp"], data["Vp"] = workloads.page_pool(data["K"], data["V"], lens,
-                                                                 w.seed)
+            table, data["Kp"], data["Vp"] = workloads.page_pool(
+                data["K"], data["V"], lens, w.seed, interleaved=args.kv_layout == "interleaved")
+            if args.kv_layout == "interleaved":
+                data["kv"] = data["Kp"]._base  # the one pool allocation, for the read probe
             data["table"] = table
             data["K"] = data["V"] = None
             torch.cuda.empty_cache()
@@ -937,10 +940,10 @@ def main():
         "data": "synthetic (seeded: per-block key clusters, N(0,1) values and queries, planted needles where the workload has them)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.kv_heads, "d": w.d,
                    "T": w.T, "paged": w.paged, "var_len": w.var_len,
-                   "kv_layout": ("page pools" if w.paged else
-                                 "K and V interleaved block by block in one buffer"
+                   "kv_layout": ("K and V interleaved block by block in one "
+                                 + ("page pool" if w.paged else "buffer")
                                  if args.kv_layout == "interleaved" else
-                                 "separate K and V buffers"),
+                                 "separate K and V " + ("page pools" if w.paged else "buffers")),
                    "tokens_cached": int(sum(lens)),
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",

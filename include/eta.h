@@ -32,7 +32,8 @@
  *       q         float32 [B][H][d]        post-RoPE query (RoPE is the caller's)
  *       K, V      [B][H_kv][T_cap][d]      float32 or bfloat16 (kv_dtype);
  *                 with kv_block_stride, blocks of 64 rows kv_block_stride
- *                 elements apart (e.g. K and V interleaved block by block)
+ *                 elements apart (e.g. K and V interleaved block by block;
+ *                 the same holds for the blocks of a page pool)
  *       tau       float32 [B][H]
  *       centroid  float32 [B][H_kv][d][nblk_cap]   dimension-major per unit
  *       var       float32 [B][H_kv][nblk_cap]
@@ -118,19 +119,19 @@ typedef struct {
                                   H_kv*64*d, even page ids only, num_pages
                                   counting both                              */
     int num_pages;             /* pages in the K/V pools (page_table only)   */
-    int kv_block_stride;       /* dense layout only: elements from one
-                                  64-token block of a key/value unit to the
-                                  next, so block j of unit u starts at
-                                  (u*T_cap/64 + j)*kv_block_stride; 0 means
-                                  64*d (rows back to back). A positive
-                                  multiple of 64*d otherwise; 128*d with V =
-                                  K + 64*d keeps K and V interleaved block by
-                                  block in one allocation, which streams at
-                                  the same rate wherever the driver places it
-                                  (two separate K and V allocations read
-                                  together stream faster or slower by several
-                                  percent depending on their relative
-                                  placement). Must be 0 with a page_table.   */
+    int kv_block_stride;       /* elements from one 64-row block of K (or V)
+                                  to the next: dense, block j of unit u starts
+                                  at (u*T_cap/64 + j)*kv_block_stride; paged,
+                                  the block of head k in page p at
+                                  (p*H_kv + k)*kv_block_stride. 0 means 64*d
+                                  (blocks back to back); otherwise a positive
+                                  multiple of 64*d. 128*d with V = K + 64*d
+                                  keeps K and V interleaved block by block in
+                                  one allocation, which streams at the same
+                                  rate wherever the driver places it (two
+                                  separate K and V allocations read together
+                                  stream faster or slower by several percent
+                                  depending on their relative placement).    */
 } eta_shape;
 
 typedef struct {

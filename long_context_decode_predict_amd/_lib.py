@@ -211,9 +211,19 @@ def kv_block_view(K: torch.Tensor) -> bool:
     return K.dim() == 5
 
 
+def kv_pool_view(K: torch.Tensor) -> bool:
+    """True for a page pool given as a strided 4-d view [P, H_kv, 64, d] whose 64-row
+    blocks lie K.stride(1) elements apart (for example K = pool[:, :, 0] and
+    V = pool[:, :, 1] of pool [P, H_kv, 2, 64, d], K and V interleaved block by block);
+    a contiguous 4-d tensor is a dense cache or a plain pool."""
+    return K.dim() == 4 and not K.is_contiguous()
+
+
 def kv_block_stride(K: torch.Tensor) -> int:
-    """eta_shape.kv_block_stride of a K/V tensor: 0 for a 4-d cache or pool."""
-    return int(K.stride(2)) if kv_block_view(K) else 0
+    """eta_shape.kv_block_stride of a K/V tensor: 0 for a contiguous 4-d cache or pool."""
+    if kv_block_view(K):
+        return int(K.stride(2))
+    return int(K.stride(1)) if kv_pool_view(K) else 0
 
 
 def kv_dims(K: torch.Tensor, layout: KVLayout | None = None):
@@ -227,6 +237,9 @@ def kv_dims(K: torch.Tensor, layout: KVLayout | None = None):
         return B, H_kv, nb * blk, d, 0
     if K.dim() != 4:
         raise ValueError("K/V must be 4-d: [B,H_kv,T_cap,d] or a page pool [P,H_kv,64,d]")
+    if kv_pool_view(K) and (layout is None or not layout.paged):
+        raise ValueError("a strided 4-d K/V is a page-pool view; a dense cache given "
+                         "block by block is 5-d")
     if layout is not None and layout.paged:
         P, H_kv, blk, d = K.shape
         if blk != BLOCK:
@@ -296,6 +309,18 @@ def _check_kv(K: torch.Tensor, name="K"):
         return
     if K.dim() != 4:
         raise ValueError(f"{name} must be [B,H,T_cap,d] (or its block view)")
+    if kv_pool_view(K):
+        # [P, H_kv, 64, d]: rows of a block back to back, blocks S apart (a positive
+        # multiple of 64*d), pages H_kv*S apart
+        P, H_kv, blk, d = K.shape
+        S = K.stride(1)
+        if blk != BLOCK or K.stride(2) != d or K.stride(3) != 1 or S <= 0 \
+                or S % (BLOCK * d) != 0 or K.stride(0) != H_kv * S:
+            raise ValueError(f"{name} as a pool view must be [P,H_kv,64,d] with blocks a "
+                             "multiple of 64*d elements apart and pages packed")
+        _need(K[0, 0], name)  # device tensor
+        kv_code(K.dtype)
+        return
     _need(K, name)
     kv_code(K.dtype)
 

@@ -57,8 +57,7 @@ eta_status check_shape(const eta_shape *s) {
         return ETA_ERR_INVALID_ARG;
     }
     if (s->kv_block_stride < 0) return ETA_ERR_INVALID_ARG;
-    if (s->kv_block_stride > 0 &&
-        (s->page_table != nullptr || s->kv_block_stride % (kBlock * s->d) != 0))
+    if (s->kv_block_stride > 0 && s->kv_block_stride % (kBlock * s->d) != 0)
         return ETA_ERR_INVALID_ARG;
     return ETA_OK;
 }

@@ -200,7 +200,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs &a, int u, int chunk,
         return (unsigned)blk < (unsigned)nblk_row ? a.lay.page_of(rb, blk) : -1;
     };
     auto base_of = [&](int blk, int pg) -> long long {
-        return (unsigned)blk < (unsigned)nblk_row ? a.lay.page_offset(rb, kh, pg, D) : -1;
+        return (unsigned)blk < (unsigned)nblk_row ? a.lay.page_offset(rb, kh, pg) : -1;
     };
     auto tile_of = [&](int blk, long long bo, int part, size_t &off, int &valid) {
         const int sub = part * TS;
@@ -533,7 +533,7 @@ __device__ __forceinline__ void attn_item_dist(const AttnArgs &a, int u, int chu
     auto tile_at = [&](int tt, size_t &off, int &valid) {
         const int blk = ld_const(iu + j0 + wave + (tt / TPB) * kAttnWaves);
         const long long bo =
-            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
+            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk) : -1;
         const int sub = (tt % TPB) * TS;
         off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * ROW;
         valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;
@@ -789,7 +789,7 @@ __device__ __forceinline__ void attn_item_mfma(const AttnArgs &a, int u, int chu
     auto tile_at = [&](int tt, size_t &off, int &valid) {
         const int blk = ld_const(iu + j0 + wave + (tt / TPB) * kAttnWaves);
         const long long bo =
-            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk, D) : -1;
+            (unsigned)blk < (unsigned)nblk_row ? a.lay.block_offset(rb, kh, blk) : -1;
         const int sub = (tt % TPB) * TT;
         off = (bo < 0 ? 0 : (size_t)bo) + (size_t)sub * D;
         valid = bo < 0 ? 0 : min(Tb - blk * kBlockTokens, kBlockTokens) - sub;

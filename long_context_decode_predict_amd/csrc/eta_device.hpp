@@ -127,14 +127,15 @@ __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp
 // ---- where the rows of a key/value unit live ----
 // Dense: block j of unit (b, k) at ((b*H_kv + k)*T_cap/64 + j)*block_stride, its
 // 64 rows of d elements back to back (block_stride = 64*d: K[(b*H_kv + k)][T_cap][d];
-// 128*d with V = K + 64*d: K and V interleaved block by block). Paged: pools
-// [num_pages][H_kv][64][d] and a page table [B][max_pages] (logical block ->
-// page). Rows may hold different numbers of tokens (seq_lens).
+// 128*d with V = K + 64*d: K and V interleaved block by block). Paged: a page
+// table [B][max_pages] (logical block -> page) and pools whose block of head k in
+// page p sits at (p*H_kv + k)*block_stride ([num_pages][H_kv][64][d] at 64*d).
+// Rows may hold different numbers of tokens (seq_lens).
 struct KVLayout {
     const int32_t *seq_lens;  // null: every row holds T
     const int32_t *pages;     // null: dense layout
     int T, T_cap, H_kv, max_pages, num_pages;
-    long long block_stride;   // dense layout: elements from one block of a unit to the next
+    long long block_stride;   // elements from one 64-row block to the next
 
     __device__ __forceinline__ int row_len(int b) const {
         if (seq_lens == nullptr) return T;
@@ -149,17 +150,17 @@ struct KVLayout {
     }
     // Element offset of key/value unit (b, k)'s block at pg (from page_of); -1
     // when the page id is out of range.
-    __device__ __forceinline__ long long page_offset(int b, int k, int pg, int d) const {
+    __device__ __forceinline__ long long page_offset(int b, int k, int pg) const {
         if (pages != nullptr) {
             if ((unsigned)pg >= (unsigned)num_pages) return -1;
-            return ((long long)pg * H_kv + k) * kBlockTokens * d;
+            return ((long long)pg * H_kv + k) * block_stride;
         }
         return ((long long)(b * H_kv + k) * (T_cap / kBlockTokens) + pg) * block_stride;
     }
     // Element offset of logical block j of key/value unit (b, k); -1 when the
     // block's page is out of range.
-    __device__ __forceinline__ long long block_offset(int b, int k, int j, int d) const {
-        return page_offset(b, k, page_of(b, j), d);
+    __device__ __forceinline__ long long block_offset(int b, int k, int j) const {
+        return page_offset(b, k, page_of(b, j));
     }
 };
 

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
         const int blk = first + j;
         float cen[EPL];
         float v = 0.f, m = 0.f;
-        const long long off = lay.block_offset(b, k, blk, D);
+        const long long off = lay.block_offset(b, k, blk);
         if (off >= 0) {
             block_stats<KV, D>(K + off, min(len - blk * kBlockTokens, kBlockTokens), cen, v, m);
         } else {

@@ -236,13 +236,16 @@ def row_lengths(w: Workload) -> list[int]:
 
 
 def page_pool(K: torch.Tensor, V: torch.Tensor, lens, seed: int, spare: int = 3,
-              all_blocks: bool = False):
+              all_blocks: bool = False, interleaved: bool = False):
     """Scatter a dense cache [B,H_kv,T_cap,d] into a shuffled page pool.
 
     Returns (page_table int32 [B, T_cap/64], Kp, Vp [P,H_kv,64,d]). Block j of row b
     gets a page when j < ceil(lens[b] / 64) (every block with all_blocks); the
     table holds an out-of-range id (-1, or P + 5 on odd rows) for the others.
-    Unused pages and the rows past lens[b] of a row's last page are NaN."""
+    Unused pages and the rows past lens[b] of a row's last page are NaN.
+    interleaved: one allocation [P, H_kv, 2, 64, d] holding each (page, head) block's
+    K rows then its V rows; Kp and Vp are its strided views [:, :, 0] and [:, :, 1]
+    (kv_block_stride = 128*d)."""
     B, Hk, T_cap, d = K.shape
     mp = T_cap // BLOCK
     dev = K.device
@@ -257,8 +260,12 @@ def page_pool(K: torch.Tensor, V: torch.Tensor, lens, seed: int, spare: int = 3,
         table[b, :need[b]] = perm[nxt:nxt + need[b]].to(torch.int32)
         table[b, need[b]:] = -1 if b % 2 == 0 else P + 5
         nxt += need[b]
-    Kp = torch.full((P, Hk, BLOCK, d), float("nan"), dtype=K.dtype, device=dev)
-    Vp = torch.full((P, Hk, BLOCK, d), float("nan"), dtype=V.dtype, device=dev)
+    if interleaved:
+        pool = torch.full((P, Hk, 2, BLOCK, d), float("nan"), dtype=K.dtype, device=dev)
+        Kp, Vp = pool[:, :, 0], pool[:, :, 1]
+    else:
+        Kp = torch.full((P, Hk, BLOCK, d), float("nan"), dtype=K.dtype, device=dev)
+        Vp = torch.full((P, Hk, BLOCK, d), float("nan"), dtype=V.dtype, device=dev)
     for b in range(B):  # one row at a time: no dense-sized temporaries
         if need[b] == 0:
             continue

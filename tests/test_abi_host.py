@@ -266,11 +266,13 @@ def test_layout_errors(L):
     assert (L.eta_decode_attn_workspace_size(BY(shape(seq_lens=FAKE, page_table=FAKE,
                                                       num_pages=9)), p)
             == L.eta_decode_attn_workspace_size(BY(shape()), p))
-    # the dense layout's block stride: 0, or a positive multiple of 64*d, no page table
+    # the block stride: 0, or a positive multiple of 64*d, in the dense and paged layouts
     for bad in (-64 * 128, 64 * 128 + 8, 64 * 64):
         assert L.eta_build_block_meta(BY(shape(kv_block_stride=bad)), FAKE, m, None) == INV, bad
-    assert L.eta_build_block_meta(BY(shape(kv_block_stride=128 * 128, page_table=FAKE,
-                                           num_pages=4)), FAKE, m, None) == INV
+        assert L.eta_build_block_meta(BY(shape(kv_block_stride=bad, page_table=FAKE,
+                                               num_pages=4)), FAKE, m, None) == INV, bad
+    assert L.eta_decode_attn_workspace_size(BY(shape(kv_block_stride=128 * 128,
+                                                     page_table=FAKE, num_pages=4)), p) > 0
     assert L.eta_decode_attn_workspace_size(BY(shape(kv_block_stride=100)), p) == 0
     assert (L.eta_decode_attn_workspace_size(BY(shape(kv_block_stride=128 * 128)), p)
             == L.eta_decode_attn_workspace_size(BY(shape()), p))
@@ -297,6 +299,21 @@ def test_block_view_binding_checks():
             _lib._check_kv(bad)
     with pytest.raises(ValueError, match="device tensor"):  # a good view, but on the host
         _lib._check_kv(torch.empty((B, Hk, nb, 2, 64, d))[:, :, :, 0])
+    # page pools given block by block: a strided 4-d view [P, H_kv, 64, d]
+    P = 5
+    pool = torch.empty((P, Hk, 2, 64, d), dtype=torch.bfloat16, device="meta")
+    Kp = pool[:, :, 0]
+    assert _lib.kv_pool_view(Kp) and _lib.kv_block_stride(Kp) == 2 * 64 * d
+    table = _lib.KVLayout(None, torch.zeros((B, nb), dtype=torch.int32))
+    assert _lib.kv_dims(Kp, table) == (B, Hk, nb * 64, d, P)
+    with pytest.raises(ValueError, match="page-pool view"):  # strided 4-d without a table
+        _lib.kv_dims(Kp)
+    for bad in (torch.empty((Hk, P, 64, d), device="meta").transpose(0, 1),   # pages apart
+                torch.empty((P, Hk, 64, d + 8), device="meta")[..., :d]):     # padded rows
+        with pytest.raises(ValueError, match="pool view"):
+            _lib._check_kv(bad)
+    with pytest.raises(ValueError, match="device tensor"):
+        _lib._check_kv(torch.empty((P, Hk, 2, 64, d))[:, :, 0])
 
 
 def test_page_pool_round_trip():

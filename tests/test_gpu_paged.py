@@ -300,3 +300,33 @@ def test_block_interleaved_dense_layout(name, kw, lens):
         assert torch.equal(grown.var[bi, :, :n], case.meta.var[bi, :, :n]), bi
         assert torch.equal(grown.maxnorm[bi, :, :n], case.meta.maxnorm[bi, :, :n]), bi
     case.free()
+
+
+@pytest.mark.parametrize("G,dtype", [(1, torch.bfloat16), (4, torch.bfloat16), (2, torch.float32)])
+def test_block_interleaved_page_pool(G, dtype):
+    """A page pool with each (page, head) block's K rows and V rows side by side in one
+    allocation ([P,H_kv,2,64,d], passed as the strided views [:, :, 0] and [:, :, 1],
+    kv_block_stride = 128*d) gives the separate pools' results bitwise, also through
+    the allocation-free entry point; unused pages are NaN in both."""
+    _announce(f"block-interleaved pool G={G} {dtype}")
+    w = workloads.custom("bip", B=3, H=4 * G, H_kv=4, d=128, T=4500, kv_dtype=dtype,
+                         seed=271 + G)
+    lens = [4500, 65, 2000]
+    case = Case(w, seq_lens=lens, paged=True, fused=True).run()
+    ref = {k: v.clone() for k, v in _results(case).items()}
+    table, Kp, Vp = workloads.page_pool(case.data["K"], case.data["V"], lens, w.seed,
+                                        interleaved=True)
+    assert torch.equal(table, case.layout.page_table)
+    assert _lib.kv_pool_view(Kp) and _lib.kv_block_stride(Kp) == 128 * w.d
+    case.data["Kp"], case.data["Vp"] = Kp, Vp
+    for t in (case.step.out, case.step.lse, case.meta.centroid, case.meta.var, case.meta.maxnorm):
+        t.zero_()
+    case.run()
+    _assert_same(ref, _results(case), case)
+    s = case.step
+    out, lse = torch.full_like(s.out, float("nan")), torch.full_like(s.lse, float("nan"))
+    _lib.eta_decode_attn_noalloc(case.data["q"], Kp, Vp, case.T, s.tau, s.uni_idx, s.uni_cnt,
+                                 case.params, out, lse, layout=case.layout)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref["out"]) and torch.equal(lse, ref["lse"])
+    case.free()
