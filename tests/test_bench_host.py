@@ -137,3 +137,25 @@ def test_read_probe_library_exports_and_rejects_bad_sizes():
     assert g(fake, None, 16384, fake, None) == -1
     assert g(fake, fake, 16384, None, None) == -1
     assert g(fake, fake + 8, 16384, fake, None) == -1
+
+
+def test_interleaved_cache_views_hold_the_same_rows():
+    """bench.interleave_kv moves a dense cache into one buffer with K and V interleaved
+    block by block: the block views it hands the library have the block stride the C
+    ABI expects (128*d), and every unit's rows read back through them equal the
+    separate buffers' rows (host tensors; no library call)."""
+    from long_context_decode_predict_amd import _lib
+    B, Hk, Tc, d = 2, 3, 192, 16
+    K = torch.randn(B, Hk, Tc, d)
+    V = torch.randn(B, Hk, Tc, d)
+    data = {"K": K.clone(), "V": V.clone()}
+    bench.interleave_kv(data)
+    Kb, Vb = bench.kv_of(data)
+    assert data["K"] is None and data["V"] is None
+    assert _lib.kv_block_view(Kb) and _lib.kv_block_stride(Kb) == 2 * 64 * d
+    assert Vb.data_ptr() - Kb.data_ptr() == 64 * d * K.element_size()
+    assert _lib.kv_dims(Kb) == (B, Hk, Tc, d, 0)
+    for b in range(B):
+        for k in range(Hk):
+            Ku, Vu = bench.unit_kv(data, b, k, 150)
+            assert torch.equal(Ku, K[b, k, :150]) and torch.equal(Vu, V[b, k, :150])
