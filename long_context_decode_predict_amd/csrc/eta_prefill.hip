@@ -22,7 +22,13 @@
 // rounding perturbs each weight's share by at most 2^-11 around their common
 // part and cannot bias the output: constant value rows come out exactly, and
 // |out error| <= 2^-11 * sum_j w_j |v_j - out|, whatever the mean of V. The
-// fp32 sum of the unrounded weights gives lse.
+// fp32 sum of the unrounded weights gives lse. Both sums (and the gate sum) are
+// formed per tile first and added to the running sums once per tile, so their
+// rounding stays at a few units in the last place however many keys a query
+// sees (a running sum taking every weight drifted by ~1e-4 in lse at 32K keys).
+// The weights are taken against a reference that may trail the running
+// maximum by a bounded amount, so a tile whose maximum stays under that bound
+// needs no rescaling of the output and the sums.
 //
 // Workgroup = 4 waves = 128 consecutive queries of one (row, head); wave w owns
 // queries 32w .. 32w + 31. Key tiles of 64 are staged into LDS (K row-major,
@@ -41,9 +47,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kPfWaves = 4;
 constexpr int kPfQ = 32 * kPfWaves;  // queries per workgroup
 constexpr int kPfKeys = 64;          // keys per tile
+constexpr float kPfSlack = 8.f;      // log2 units the weight reference may trail the maximum
 
 template <int D>
 struct PfShared {
@@ -60,6 +68,7 @@ struct PfShared {
 struct PfArgs {
     int H, Hkv, G, T_q, T_k, q_off;
     float s, c_gate, c_soft;  // 1/sqrt(d), -beta*log2(e)/sqrt(d), log2(e)/sqrt(d)
+    float inv_c;              // 1 / c_soft
     const uint16_t *Q;
     const uint16_t *K;
     const uint16_t *V;
@@ -143,40 +152,48 @@ __device__ __forceinline__ void stage_store(PfShared<D> &sm, int buf,
     }
 }
 
-// Gate, mask and tile maximum of one lane's 32 scores (acc = q.k, unscaled).
-// Returns the gated values in acc units (the 1/sqrt(d) scale is folded into
-// the exponent constants, and a positive scale keeps the order).
+// Gate, mask and exponent of one lane's 32 scores (acc = q.k, unscaled), in
+// log2 units relative to the reference mref: t = log2(e) * S' - mref, with
+// S' = S * sigmoid(beta (S - tau)) and S = s * acc. The soft gate's reciprocal
+// carries the scale: rcp(inv_c * (1 + e)) = c_soft * sigmoid, so the gated
+// exponent is one fma of acc with it. g_sum gains the tile's gates in those
+// scaled units (the caller divides by c_soft), summed within the tile first so
+// that the running sum takes one addition per tile. Returns the tile maximum.
 template <bool HARD, bool GSUM, bool MASK>
 __device__ __forceinline__ float gate_tile(const PfArgs &a, const float (&acc)[2][16], float t_acc,
-                                           float nbt, int lim, float (&g)[2][16], float &g_sum) {
+                                           float nbt, float mref, int lim, float (&tv)[2][16],
+                                           float &g_sum) {
     float mx = -INFINITY;
+    float gp[4] = {0.f, 0.f, 0.f, 0.f};  // the tile's gates, four partial sums
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const float x = acc[mt][j];
-            float gv, gate = 0.f;
+            float t, gate = 0.f;
             if (HARD) {
                 const bool on = x >= t_acc;
-                gv = on ? x : 0.f;
+                t = fmaf(on ? x : 0.f, a.c_soft, -mref);
                 if (GSUM) gate = on ? 1.f : 0.f;
             } else {
-                const float m = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(fmaf(a.c_gate, x, nbt)));
-                gv = x * m;
-                if (GSUM) gate = m;
+                const float e = __builtin_amdgcn_exp2f(fmaf(a.c_gate, x, nbt));
+                const float mc = __builtin_amdgcn_rcpf(fmaf(e, a.inv_c, a.inv_c));
+                t = fmaf(x, mc, -mref);
+                if (GSUM) gate = mc;
             }
             if (MASK) {
                 const int off = mt * 32 + (j >> 2) * 8 + (j & 3);  // key offset minus 4*hl
                 if (off > lim) {
-                    gv = -INFINITY;
+                    t = -INFINITY;
                     gate = 0.f;
                 }
             }
-            if (GSUM) g_sum += gate;
-            g[mt][j] = gv;
-            mx = fmaxf(mx, gv);
+            if (GSUM) gp[j & 3] += gate;
+            tv[mt][j] = t;
+            mx = fmaxf(mx, t);
         }
     }
+    if (GSUM) g_sum += (gp[0] + gp[1]) + (gp[2] + gp[3]);
     return mx;
 }
 
@@ -228,7 +245,13 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
     f32x16 o[NMD];
 #pragma unroll
     for (int m = 0; m < NMD; ++m) o[m] = f32x16{};
-    float m_run = -INFINITY, g_sum = 0.f;  // m_run in acc units
+    // Weights are 2^t with t taken against a reference mref (log2 units) that
+    // trails the running maximum by at most kPfSlack: the first tile sets it to
+    // that tile's maximum, a later tile moves it (and rescales the sums) only
+    // when its own maximum lies more than kPfSlack above it. Every weight is
+    // then at most 2^kPfSlack and the largest one at least 1, so the fp16
+    // weights keep their full precision and the sums stay far from overflow.
+    float mref = 0.f, g_sum = 0.f;
     float l_run = 0.f;   // sum of the fp32 weights: lse
     float lh_run = 0.f;  // sum of the weights as rounded to fp16 for P.V: out's divisor
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
@@ -263,42 +286,56 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[mt][j] = s[mt][j];
 
-        // gate, causal mask (diagonal and last tiles only), tile maximum
+        // gate, causal mask (diagonal and last tiles only), exponents, tile maximum
         float g[2][16];
         float mx;
         if (k0 + kPfKeys - 1 > wave_first_pos || k0 + kPfKeys > a.T_k) {
-            mx = gate_tile<HARD, GSUM, true>(a, acc, t_acc, nbt, qpos - k0 - hl * 4, g, g_sum);
+            mx = gate_tile<HARD, GSUM, true>(a, acc, t_acc, nbt, mref, qpos - k0 - hl * 4, g, g_sum);
         } else {
-            mx = gate_tile<HARD, GSUM, false>(a, acc, t_acc, nbt, 0, g, g_sum);
+            mx = gate_tile<HARD, GSUM, false>(a, acc, t_acc, nbt, mref, 0, g, g_sum);
         }
         mx = half_pair_max(mx);  // the partner lane l ^ 32 holds the other 32 keys
-        const float m_new = fmaxf(m_run, mx);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // nothing visible yet: weights 0
-        const float corr = __builtin_amdgcn_exp2f((m_run - m_ref) * a.c_soft);
-        m_run = m_new;
-        l_run *= corr;
-        lh_run *= corr;
-        if (__any(corr != 1.f)) {  // the running maximum moved for some query of the wave
+        // the first tile holds key 0, which every query sees: its maximum is finite
+        const bool move = tt == 0 || mx > kPfSlack;
+        if (__any(move)) {
+            const float shift = move ? mx : 0.f;
+            mref += shift;
+            if (tt > 0) {  // the sums so far were taken against the old reference
+                const float corr = __builtin_amdgcn_exp2f(-shift);
+                l_run *= corr;
+                lh_run *= corr;
 #pragma unroll
-            for (int m = 0; m < NMD; ++m) o[m] *= corr;
+                for (int m = 0; m < NMD; ++m) o[m] *= corr;
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) g[mt][j] -= shift;
         }
 
         // weights, packed as the fp16 B operand of O^T += V^T P^T: k-step s (keys
         // 16s .. 16s + 15) takes registers 8(s%2) .. 8(s%2) + 7 of key tile s/2
-        const float mref_c = m_ref * a.c_soft;
         uint32_t pw[4][4];
+        // the tile's weights summed on their own first (fp32 partial sums for lse, fp16
+        // dot products for out's divisor): the running sums take one addition per tile,
+        // so their rounding does not grow with the number of keys
+        float lp[4] = {0.f, 0.f, 0.f, 0.f};
+        float lhp[2] = {0.f, 0.f};
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
             for (int j = 0; j < 16; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(g[mt][j], a.c_soft, -mref_c));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(g[mt][j + 1], a.c_soft, -mref_c));
-                l_run += p0 + p1;
+                const float p0 = __builtin_amdgcn_exp2f(g[mt][j]);
+                const float p1 = __builtin_amdgcn_exp2f(g[mt][j + 1]);
+                lp[(j >> 1) & 3] += p0 + p1;
                 const uint32_t pk = pack_f16(p0, p1);
-                lh_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, lh_run, false);
+                lhp[(j >> 1) & 1] =
+                    __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones, lhp[(j >> 1) & 1], false);
                 pw[mt * 2 + j / 8][(j % 8) / 2] = pk;
             }
         }
+        l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+        lh_run += lhp[0] + lhp[1];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const f16x8 pB = __builtin_bit_cast(f16x8, make_uint4(pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]));
@@ -320,7 +357,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
     // the two halves of a query's keys meet
     const float l_tot = half_pair_sum(l_run);
     const float lh_tot = half_pair_sum(lh_run);  // >= 1 once a key is visible (its max weighs 1)
-    const float gs_tot = GSUM ? half_pair_sum(g_sum) : 0.f;
+    const float gs_tot = GSUM ? (HARD ? half_pair_sum(g_sum) : half_pair_sum(g_sum) * a.inv_c) : 0.f;
     if (qi < a.T_q) {
         const size_t uq = (size_t)bh * a.T_q + qi;
         const float inv = l_tot > 0.f ? 1.f / lh_tot : 0.f;
@@ -336,7 +373,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
             }
         }
         if (hl == 0) {
-            if (a.lse) a.lse[uq] = l_tot > 0.f ? a.s * m_run + __logf(l_tot) : -INFINITY;
+            if (a.lse) a.lse[uq] = l_tot > 0.f ? (mref + __log2f(l_tot)) * kLn2 : -INFINITY;
             if (GSUM) a.gate_sum[uq] = gs_tot;
         }
     }
@@ -456,6 +493,7 @@ hipError_t launch_prefill_t(const PrefillGeometry &g, const void *Q, const void 
     a.s = 1.0f / sqrtf((float)D);
     a.c_gate = -gate_beta * kLog2e * a.s;
     a.c_soft = kLog2e * a.s;
+    a.inv_c = 1.0f / a.c_soft;
     a.Q = static_cast<const uint16_t *>(Q);
     a.K = static_cast<const uint16_t *>(K);
     a.V = static_cast<const uint16_t *>(V);

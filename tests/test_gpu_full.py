@@ -104,7 +104,8 @@ def test_full_size(name):
 def test_prefill_full_size(name):
     """The training-time forward at the benchmark's sizes and launch configuration
     (Eq. 1 per token on the GPU, then the gated forward): a seeded sample of
-    (row, head, query) triples, spread over early, middle and last positions, is
+    (row, head, query) triples, spread over early, middle and last positions (16 of
+    them among the last 2048), is
     compared with the oracle (its own Eq. 1 for tau, a one-query call over the
     query's causal window)."""
     from oracle import oracle as oracle_mod
@@ -129,6 +130,10 @@ def test_prefill_full_size(name):
     picks = [(0, 0, 0), (B - 1, H - 1, T - 1)]
     picks += [(int(rng.integers(B)), int(rng.integers(H)), int(t))
               for t in np.concatenate([rng.integers(0, 256, 4), rng.integers(256, T, 10)])]
+    # the last queries see the most keys: lse there shows any rounding that grows
+    # with the number of keys summed
+    picks += [(int(rng.integers(B)), int(rng.integers(H)), int(t))
+              for t in rng.integers(max(0, T - 2048), T, 16)]
     Wn = data["W"].cpu().numpy()
     bn = bias.cpu().numpy()
     worst = 0.0
