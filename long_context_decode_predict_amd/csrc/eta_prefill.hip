@@ -31,9 +31,9 @@
 // needs no rescaling of the output and the sums.
 //
 // Workgroup = 4 waves = 128 consecutive queries of one (row, head); wave w owns
-// queries 32w .. 32w + 31. Key tiles of 64 are staged into LDS (K row-major,
-// V^T), the next tile's global loads are in flight while the current one is
-// computed. Causal: query i sits at position T_k - T_q + i and sees keys at or
+// queries 32w .. 32w + 31. Key tiles of 64 are staged into LDS (K row-major by
+// direct global-to-LDS loads, V^T through registers), the next tile's global
+// loads are in flight while the current one is computed. Causal: query i sits at position T_k - T_q + i and sees keys at or
 // before it. Grid x = (row, head), y = query block, heaviest blocks first; all
 // query blocks of one head share an XCD when B * H is a multiple of 8.
 #include "eta_device.hpp"
@@ -55,13 +55,16 @@ constexpr float kPfSlack = 8.f;      // log2 units the weight reference may trai
 
 template <int D>
 struct PfShared {
-    static constexpr int KS = D + 8;        // bf16 per K row (16 bytes of padding)
+    static constexpr int KCH = D / 8;       // 16-byte chunks per K row
     static constexpr int VS = kPfKeys + 4;  // fp16 per V^T row (8 bytes of padding)
+    // K rows unpadded; chunk c of row r sits at chunk c ^ (r % KCH) of its row, so
+    // the 32 rows an MFMA operand read touches hit distinct banks. Written by the
+    // direct global-to-LDS loads (64 lanes x 16 contiguous bytes per instruction).
+    alignas(16) uint16_t k[2][kPfKeys * D];  // double buffered: one barrier per tile
     // V^T row r keeps key k at column k ^ swz(r): 16-key groups are permuted by the
     // row's 32-dimension tile, so the transposing writes (8 bytes per lane, rows
     // 8 apart across lanes) spread over the banks; a reading wave works on one
     // 32-row tile at a time, so its reads are only shifted.
-    alignas(16) uint16_t k[2][kPfKeys * KS];  // double buffered: one barrier per tile
     alignas(16) uint16_t vt[2][D * VS];
 };
 
@@ -103,18 +106,35 @@ struct StageShape {
 // Key swizzle of V^T row r (see PfShared): flips the 16-key group by r / 32.
 __device__ __forceinline__ int vt_swz(int r) { return ((r >> 5) & 3) << 4; }
 
+// K rows of one key tile straight into LDS (no registers): instruction i of wave w
+// fills chunk positions (w * KLD + i) * 64 + lane of the swizzled buffer; rows past
+// T_k are clamped (their keys are masked later).
 template <int D>
-__device__ __forceinline__ void stage_load(const PfArgs &a, const uint16_t *Kh, const uint16_t *Vh,
-                                           int k0, uint4 (&kr)[StageShape<D>::KLD],
+__device__ __forceinline__ void stage_k_lds(const PfArgs &a, const uint16_t *Kh, int k0,
+                                            uint16_t *kbuf) {
+    using S = StageShape<D>;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int i = 0; i < S::KLD; ++i) {
+        const int ins = wave * S::KLD + i;
+        const int p = ins * kWave + lane;  // chunk position in the tile
+        const int r = p / S::KCH;
+        const int c = (p % S::KCH) ^ (r % S::KCH);
+        const int row = min(k0 + r, a.T_k - 1);
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void *>(Kh + (size_t)row * D + c * 8),
+            reinterpret_cast<__attribute__((address_space(3))) void *>(
+                reinterpret_cast<uintptr_t>(kbuf + ins * kWave * 8)),
+            16, 0, 0);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_load(const PfArgs &a, const uint16_t *Vh, int k0,
                                            uint4 (&vr)[StageShape<D>::KPT]) {
     using S = StageShape<D>;
     const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < S::KLD; ++i) {
-        const int c = tid + i * kPfWaves * kWave;
-        const int row = min(k0 + c / S::KCH, a.T_k - 1);  // rows past T_k: clamped, masked later
-        kr[i] = *reinterpret_cast<const uint4 *>(Kh + (size_t)row * D + (c % S::KCH) * 8);
-    }
     const int ka = tid / S::KCH;  // key group
     const int db = tid % S::KCH;  // 8-dimension chunk
 #pragma unroll
@@ -126,16 +146,9 @@ __device__ __forceinline__ void stage_load(const PfArgs &a, const uint16_t *Kh, 
 
 template <int D>
 __device__ __forceinline__ void stage_store(PfShared<D> &sm, int buf,
-                                            const uint4 (&kr)[StageShape<D>::KLD],
                                             const uint4 (&vr)[StageShape<D>::KPT]) {
     using S = StageShape<D>;
     const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < S::KLD; ++i) {
-        const int c = tid + i * kPfWaves * kWave;
-        *reinterpret_cast<uint4 *>(&sm.k[buf][(c / S::KCH) * PfShared<D>::KS + (c % S::KCH) * 8]) =
-            kr[i];
-    }
     const int ka = tid / S::KCH;
     const int db = tid % S::KCH;
 #pragma unroll
@@ -200,7 +213,7 @@ __device__ __forceinline__ float gate_tile(const PfArgs &a, const float (&acc)[2
 template <int D, bool HARD, bool GSUM>
 __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs a) {
     __shared__ PfShared<D> sm;
-    constexpr int KS = PfShared<D>::KS;
+    constexpr int KCH = PfShared<D>::KCH;
     constexpr int VS = PfShared<D>::VS;
     constexpr int NKS = D / 16;  // k-steps of the S product
     constexpr int NMD = D / 32;  // head-dimension tiles of the O product
@@ -256,17 +269,19 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
     float lh_run = 0.f;  // sum of the weights as rounded to fp16 for P.V: out's divisor
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-    uint4 kr[StageShape<D>::KLD], vr[StageShape<D>::KPT];
-    stage_load<D>(a, Kh, Vh, 0, kr, vr);
-    stage_store<D>(sm, 0, kr, vr);
+    uint4 vr[StageShape<D>::KPT];
+    stage_k_lds<D>(a, Kh, 0, sm.k[0]);
+    stage_load<D>(a, Vh, 0, vr);
+    stage_store<D>(sm, 0, vr);
+    __builtin_amdgcn_s_waitcnt(0);  // the K rows have landed in LDS
     __syncthreads();
     for (int tt = 0; tt < ntiles; ++tt) {
         const int k0 = tt * kPfKeys;
         const int buf = tt & 1;
-        // the next tile's loads are in flight during this one (issued unconditionally:
-        // rows are clamped, so the load past the last tile stays in bounds and keeps
-        // the staging registers out of scratch memory)
-        stage_load<D>(a, Kh, Vh, k0 + kPfKeys, kr, vr);
+        // the next tile's V rows are in flight during this one (issued
+        // unconditionally: rows are clamped, so the load past the last tile stays in
+        // bounds and keeps the staging registers out of scratch memory)
+        stage_load<D>(a, Vh, k0 + kPfKeys, vr);
 
         // S^T for keys k0 .. k0 + 63 (two 32-key tiles) against the wave's 32 queries
         f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -274,12 +289,17 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
+                const int r = mt * 32 + col;
                 const uint4 raw = *reinterpret_cast<const uint4 *>(
-                    &sm.k[buf][(mt * 32 + col) * KS + ks * 16 + hl * 8]);
+                    &sm.k[buf][r * D + (((ks * 2 + hl) ^ (r % KCH)) * 8)]);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
                                                                 qB[ks], s[mt], 0, 0, 0);
             }
         }
+        // the next tile's K rows go straight into the other buffer once this tile's
+        // K reads are issued (that buffer's last readers finished before the barrier
+        // that ended the previous iteration)
+        if (tt + 1 < ntiles) stage_k_lds<D>(a, Kh, k0 + kPfKeys, sm.k[buf ^ 1]);
         float acc[2][16];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -350,7 +370,8 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
         }
         // next tile into the other buffer: its last readers finished before the
         // barrier that ended the previous iteration
-        if (tt + 1 < ntiles) stage_store<D>(sm, buf ^ 1, kr, vr);
+        if (tt + 1 < ntiles) stage_store<D>(sm, buf ^ 1, vr);
+        __builtin_amdgcn_s_waitcnt(0);  // the next tile's K rows have landed in LDS
         __syncthreads();
     }
 
