@@ -380,7 +380,8 @@ typedef struct {
                       {1, 2, 4, 8}                                           */
     int d;         /* head dimension: 64 or 128                              */
     int T_q, T_k;  /* queries and keys per row; 0 <= T_q <= T_k; at most
-                      65535 * 128 queries                                    */
+                      65535 * 128 queries; T_k * d * 2 < 2^31 (one row's K
+                      or V of one head under 2 GiB)                          */
 } eta_prefill_shape;
 
 /*

@@ -410,6 +410,9 @@ eta_status eta_prefill_attn(const eta_prefill_shape *s, const void *Q, const voi
     eta::PrefillGeometry g;
     eta_status st = check_prefill(s, &g);
     if (st != ETA_OK) return st;
+    // the forward addresses one (row, key/value head) slab of K or V through a
+    // buffer resource with a 31-bit byte range
+    if ((long long)s->T_k * s->d * 2 >= (1ll << 31)) return ETA_ERR_INVALID_ARG;
     if ((st = check_params(p)) != ETA_OK) return st;
     if (Q == nullptr || K == nullptr || V == nullptr || tau == nullptr || out == nullptr)
         return ETA_ERR_INVALID_ARG;

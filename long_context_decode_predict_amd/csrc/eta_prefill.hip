@@ -57,8 +57,8 @@ template <int D>
 struct PfShared {
     static constexpr int KCH = D / 8;       // 16-byte chunks per K row
     static constexpr int VS = kPfKeys + 4;  // fp16 per V^T row (8 bytes of padding)
-    // K rows unpadded; chunk c of row r sits at chunk c ^ (r % KCH) of its row, so
-    // the 32 rows an MFMA operand read touches hit distinct banks. Written by the
+    // K rows unpadded; chunk c of row r sits at chunk c ^ (r % 8) of its row, so
+    // the rows an MFMA operand read touches together hit distinct banks. Written by the
     // direct global-to-LDS loads (64 lanes x 16 contiguous bytes per instruction).
     alignas(16) uint16_t k[2][kPfKeys * D];  // double buffered: one barrier per tile
     // V^T row r keeps key k at column k ^ swz(r): 16-key groups are permuted by the
@@ -103,45 +103,67 @@ struct StageShape {
     static constexpr int KPT = D / 32;                              // V keys per thread
 };
 
+// Chunk swizzle of K row r (see PfShared): the eight rows a reading lane group
+// touches at one logical chunk land on eight different 16-byte bank groups.
+__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+
 // Key swizzle of V^T row r (see PfShared): flips the 16-key group by r / 32.
 __device__ __forceinline__ int vt_swz(int r) { return ((r >> 5) & 3) << 4; }
 
-// K rows of one key tile straight into LDS (no registers): instruction i of wave w
-// fills chunk positions (w * KLD + i) * 64 + lane of the swizzled buffer; rows past
-// T_k are clamped (their keys are masked later).
+// Buffer resource over the rows [k0, T_k) of one (row, key/value head) slab of K or
+// V: reads at or past T_k return zeros (hardware range check), so a tile that
+// runs past the end needs no clamping, and the tile's base lives in scalar
+// registers (lanes add only their constant 32-bit offsets). The slab is at most
+// 2^31 bytes (checked on the host).
+#define ETA_TILE_RSRC(slab, k0, T_k)                                                     \
+    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>((slab) + (size_t)(k0) * D), \
+                                      (short)0, max((T_k) - (k0), 0) * D * 2, 0x00020000)
+
+// Byte offsets of a lane's K chunks within a tile: instruction i of wave w fills
+// chunk positions (w * KLD + i) * 64 + lane of the swizzled LDS buffer.
 template <int D>
-__device__ __forceinline__ void stage_k_lds(const PfArgs &a, const uint16_t *Kh, int k0,
-                                            uint16_t *kbuf) {
+__device__ __forceinline__ uint32_t k_lane_off(int wave, int lane, int i) {
     using S = StageShape<D>;
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int i = 0; i < S::KLD; ++i) {
-        const int ins = wave * S::KLD + i;
-        const int p = ins * kWave + lane;  // chunk position in the tile
-        const int r = p / S::KCH;
-        const int c = (p % S::KCH) ^ (r % S::KCH);
-        const int row = min(k0 + r, a.T_k - 1);
-        __builtin_amdgcn_global_load_lds(
-            static_cast<const void *>(Kh + (size_t)row * D + c * 8),
-            reinterpret_cast<__attribute__((address_space(3))) void *>(
-                reinterpret_cast<uintptr_t>(kbuf + ins * kWave * 8)),
-            16, 0, 0);
-    }
+    const int p = (wave * S::KLD + i) * kWave + lane;
+    const int r = p / S::KCH;
+    const int c = (p % S::KCH) ^ k_swz(r);
+    return (uint32_t)(r * D * 2 + c * 16);
 }
 
+// K rows of one key tile straight into LDS (no registers).
 template <int D>
-__device__ __forceinline__ void stage_load(const PfArgs &a, const uint16_t *Vh, int k0,
-                                           uint4 (&vr)[StageShape<D>::KPT]) {
+__device__ __forceinline__ void stage_k_lds(const uint16_t *Kh, int k0, int T_k, int wave_u,
+                                            const uint32_t (&koff)[StageShape<D>::KLD],
+                                            uint16_t *kbuf) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer-resource type exists for the device only
     using S = StageShape<D>;
-    const int tid = threadIdx.x;
-    const int ka = tid / S::KCH;  // key group
-    const int db = tid % S::KCH;  // 8-dimension chunk
+    const auto rs = ETA_TILE_RSRC(Kh, k0, T_k);
+#pragma unroll
+    for (int i = 0; i < S::KLD; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs,
+            reinterpret_cast<__attribute__((address_space(3))) void *>(
+                reinterpret_cast<uintptr_t>(kbuf + (wave_u * S::KLD + i) * kWave * 8)),
+            16, koff[i], 0, 0, 0);
+    }
+#endif
+}
+
+// V rows of one key tile into registers: KPT consecutive keys x 8 dimensions per
+// thread (rows past T_k read as zeros).
+template <int D>
+__device__ __forceinline__ void stage_load(const uint16_t *Vh, int k0, int T_k, uint32_t voff,
+                                           uint4 (&vr)[StageShape<D>::KPT]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using S = StageShape<D>;
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const auto rs = ETA_TILE_RSRC(Vh, k0, T_k);
 #pragma unroll
     for (int r = 0; r < S::KPT; ++r) {
-        const int row = min(k0 + ka * S::KPT + r, a.T_k - 1);
-        vr[r] = *reinterpret_cast<const uint4 *>(Vh + (size_t)row * D + db * 8);
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + r * D * 2, 0, 0);
+        vr[r] = make_uint4(x.x, x.y, x.z, x.w);
     }
+#endif
 }
 
 template <int D>
@@ -213,7 +235,6 @@ __device__ __forceinline__ float gate_tile(const PfArgs &a, const float (&acc)[2
 template <int D, bool HARD, bool GSUM>
 __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs a) {
     __shared__ PfShared<D> sm;
-    constexpr int KCH = PfShared<D>::KCH;
     constexpr int VS = PfShared<D>::VS;
     constexpr int NKS = D / 16;  // k-steps of the S product
     constexpr int NMD = D / 32;  // head-dimension tiles of the O product
@@ -269,9 +290,16 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
     float lh_run = 0.f;  // sum of the weights as rounded to fp16 for P.V: out's divisor
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
+    // staging offsets of this lane (constant over the key tiles)
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t koff[StageShape<D>::KLD];
+#pragma unroll
+    for (int i = 0; i < StageShape<D>::KLD; ++i) koff[i] = k_lane_off<D>(wave_u, lane, i);
+    const uint32_t voff = (uint32_t)((tid / StageShape<D>::KCH) * StageShape<D>::KPT * D * 2 +
+                                     (tid % StageShape<D>::KCH) * 16);
     uint4 vr[StageShape<D>::KPT];
-    stage_k_lds<D>(a, Kh, 0, sm.k[0]);
-    stage_load<D>(a, Vh, 0, vr);
+    stage_k_lds<D>(Kh, 0, a.T_k, wave_u, koff, sm.k[0]);
+    stage_load<D>(Vh, 0, a.T_k, voff, vr);
     stage_store<D>(sm, 0, vr);
     __builtin_amdgcn_s_waitcnt(0);  // the K rows have landed in LDS
     __syncthreads();
@@ -279,9 +307,9 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
         const int k0 = tt * kPfKeys;
         const int buf = tt & 1;
         // the next tile's V rows are in flight during this one (issued
-        // unconditionally: rows are clamped, so the load past the last tile stays in
-        // bounds and keeps the staging registers out of scratch memory)
-        stage_load<D>(a, Vh, k0 + kPfKeys, vr);
+        // unconditionally: past the last tile every row reads as zero, and the
+        // staging registers stay out of scratch memory)
+        stage_load<D>(Vh, k0 + kPfKeys, a.T_k, voff, vr);
 
         // S^T for keys k0 .. k0 + 63 (two 32-key tiles) against the wave's 32 queries
         f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -291,7 +319,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
             for (int mt = 0; mt < 2; ++mt) {
                 const int r = mt * 32 + col;
                 const uint4 raw = *reinterpret_cast<const uint4 *>(
-                    &sm.k[buf][r * D + (((ks * 2 + hl) ^ (r % KCH)) * 8)]);
+                    &sm.k[buf][r * D + (((ks * 2 + hl) ^ k_swz(r)) * 8)]);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
                                                                 qB[ks], s[mt], 0, 0, 0);
             }
@@ -299,7 +327,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
         // the next tile's K rows go straight into the other buffer once this tile's
         // K reads are issued (that buffer's last readers finished before the barrier
         // that ended the previous iteration)
-        if (tt + 1 < ntiles) stage_k_lds<D>(a, Kh, k0 + kPfKeys, sm.k[buf ^ 1]);
+        if (tt + 1 < ntiles) stage_k_lds<D>(Kh, k0 + kPfKeys, a.T_k, wave_u, koff, sm.k[buf ^ 1]);
         float acc[2][16];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)

@@ -362,6 +362,16 @@ def test_prefill_shape_errors(L, kw, st):
     assert L.eta_prefill_predict_tau(BY(pshape(**kw)), FAKE, FAKE, FAKE, FAKE, None) == st
 
 
+@pytest.mark.parametrize("d,T_k", [(128, 1 << 23), (64, 1 << 24), (128, (1 << 31) - 1)])
+def test_prefill_slab_limit(L, d, T_k):
+    """One row's K (or V) of one head must stay under 2^31 bytes for the forward (it
+    is addressed through a buffer resource); the predictor does not read K and takes
+    the shape."""
+    s = BY(pshape(d=d, T_q=100, T_k=T_k))
+    assert L.eta_prefill_attn(s, FAKE, FAKE, FAKE, FAKE, BY(params()), FAKE, None, None,
+                              None) == INV
+
+
 def test_prefill_pointer_errors(L):
     s, p = BY(pshape()), BY(params())
     call = lambda **kw: L.eta_prefill_attn(s, kw.get("Q", FAKE), kw.get("K", FAKE),
