@@ -57,7 +57,7 @@ template <int D>
 struct PfShared {
     static constexpr int KCH = D / 8;       // 16-byte chunks per K row
     static constexpr int VS = kPfKeys + 4;  // fp16 per V^T row (8 bytes of padding)
-    // K rows unpadded; chunk c of row r sits at chunk c ^ (r % 8) of its row, so
+    // K rows unpadded; chunk c of row r sits at chunk c ^ (r % KCH) of its row, so
     // the rows an MFMA operand read touches together hit distinct banks. Written by the
     // direct global-to-LDS loads (64 lanes x 16 contiguous bytes per instruction).
     alignas(16) uint16_t k[2][kPfKeys * D];  // double buffered: one barrier per tile
@@ -103,9 +103,10 @@ struct StageShape {
     static constexpr int KPT = D / 32;                              // V keys per thread
 };
 
-// Chunk swizzle of K row r (see PfShared): the eight rows a reading lane group
-// touches at one logical chunk land on eight different 16-byte bank groups.
-__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+// Chunk swizzle of K row r (see PfShared): the 16 rows (8 at d = 64) a reading
+// lane group touches at one logical chunk land on distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return r & (D / 8 - 1); }
 
 // Key swizzle of V^T row r (see PfShared): flips the 16-key group by r / 32.
 __device__ __forceinline__ int vt_swz(int r) { return ((r >> 5) & 3) << 4; }
@@ -126,7 +127,7 @@ __device__ __forceinline__ uint32_t k_lane_off(int wave, int lane, int i) {
     using S = StageShape<D>;
     const int p = (wave * S::KLD + i) * kWave + lane;
     const int r = p / S::KCH;
-    const int c = (p % S::KCH) ^ k_swz(r);
+    const int c = (p % S::KCH) ^ k_swz<D>(r);
     return (uint32_t)(r * D * 2 + c * 16);
 }
 
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
             for (int mt = 0; mt < 2; ++mt) {
                 const int r = mt * 32 + col;
                 const uint4 raw = *reinterpret_cast<const uint4 *>(
-                    &sm.k[buf][r * D + (((ks * 2 + hl) ^ k_swz(r)) * 8)]);
+                    &sm.k[buf][r * D + (((ks * 2 + hl) ^ k_swz<D>(r)) * 8)]);
                 s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
                                                                 qB[ks], s[mt], 0, 0, 0);
             }
