@@ -431,90 +431,89 @@ __global__ __launch_bounds__(kPfWaves *kWave, 2) void prefill_attn_kernel(PfArgs
 
 // Eq. 1 for every query token of a prefill: tau[b, h, t] = bias[h] + sum over the
 // token's queries of all heads g and dimensions i of Q[b, g, t, i] * W[g*d + i, h].
-// Workgroup = 64 consecutive tokens (one per lane) x up to 16 heads per pass;
-// wave w sums the query heads g = w, w + 4, ... . In each round the workgroup
-// stages the four W slices W[g*d .. g*d + d)[h0 .. h0 + 16) in LDS; a wave reads
-// its slice with broadcast loads (the same address in every lane) and every
-// lane does 16 FMAs per query element. The four partial sums meet in LDS and
-// are added in wave order (fixed order, deterministic).
+// Workgroup = 64 consecutive tokens (one per lane) x 16 waves, up to 16 output
+// heads per pass; wave w sums the query heads g = w, w + 16, ... . A row of W is
+// the same for every lane of a wave: it is read through the scalar cache into
+// scalar registers and enters the FMAs as their scalar operand, so each query
+// element costs 16 FMAs and no LDS traffic or barrier. The sixteen partial sums
+// meet in LDS and are added in wave order (fixed order, deterministic), wave k
+// finishing output head k. Each lane reads its own token's query rows, 16 bytes
+// at a time (one row per lane, rows 2d bytes apart).
 constexpr int kTauTokens = 64;
-constexpr int kTauWaves = 4;
+constexpr int kTauWaves = 16;
 constexpr int kTauHeads = 16;
+
+// One query head g of a token against rows W[g*d .. g*d + d)[h0 .. h0 + 16): FULL
+// when all 16 columns exist and the rows are 16-byte aligned (four 16-byte scalar
+// loads per row); otherwise column by column, the missing ones skipped.
+template <int D, bool FULL>
+__device__ __forceinline__ void tau_rows(const uint16_t *__restrict__ qrow,
+                                         const float *__restrict__ wg, int H, int nh,
+                                         float (&acc)[kTauHeads]) {
+    for (int i0 = 0; i0 < D; i0 += 8) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(qrow + i0);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float qv = (e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1]);
+            const float *wr = wg + (size_t)(i0 + e) * H;  // wave-uniform row
+            if (FULL) {
+#pragma unroll
+                for (int k4 = 0; k4 < kTauHeads / 4; ++k4) {
+                    const float4 w = reinterpret_cast<const float4 *>(wr)[k4];
+                    acc[4 * k4] = fmaf(qv, w.x, acc[4 * k4]);
+                    acc[4 * k4 + 1] = fmaf(qv, w.y, acc[4 * k4 + 1]);
+                    acc[4 * k4 + 2] = fmaf(qv, w.z, acc[4 * k4 + 2]);
+                    acc[4 * k4 + 3] = fmaf(qv, w.w, acc[4 * k4 + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < kTauHeads; ++k) {
+                    if (k < nh) acc[k] = fmaf(qv, wr[k], acc[k]);
+                }
+            }
+            // one row's scalar registers at a time (scalar loads return out of order,
+            // so rows loaded ahead would only hold registers)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(kTauWaves *kWave) void prefill_tau_kernel(
     const uint16_t *__restrict__ Q, const float *__restrict__ W, const float *__restrict__ bias,
-    float *__restrict__ tau, int H, int T, int vec) {
-    __shared__ float4 wsl[kTauWaves][D][kTauHeads / 4];
+    float *__restrict__ tau, int H, int T, int wvec) {
     __shared__ float part[kTauWaves][kTauHeads][kTauTokens];
     const int b = blockIdx.y;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = threadIdx.x & (kWave - 1);
     const int tok = blockIdx.x * kTauTokens + lane;
     const int tc = min(tok, T - 1);
     for (int h0 = 0; h0 < H; h0 += kTauHeads) {
+        const int nh = min(kTauHeads, H - h0);
+        const bool full = nh == kTauHeads && wvec;
         float acc[kTauHeads];
 #pragma unroll
         for (int k = 0; k < kTauHeads; ++k) acc[k] = 0.f;
         if (W != nullptr) {
-            for (int g0 = 0; g0 < H; g0 += kTauWaves) {
-                __syncthreads();  // the previous round's slices are consumed
-                // stage W[(g0 + w)*d + i][h0 .. h0 + 16) for w < 4, i < d (zeros outside)
-                for (int c = threadIdx.x; c < kTauWaves * D * (kTauHeads / 4); c += kTauWaves * kWave) {
-                    const int w = c / (D * (kTauHeads / 4));
-                    const int i = (c / (kTauHeads / 4)) % D;
-                    const int q4 = c % (kTauHeads / 4);
-                    const int g = g0 + w;
-                    const int h = h0 + q4 * 4;
-                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (g < H) {
-                        const float *src = W + (size_t)(g * D + i) * H + h;
-                        if (vec && h + 4 <= H) {
-                            v = *reinterpret_cast<const float4 *>(src);
-                        } else {
-                            v.x = h < H ? src[0] : 0.f;
-                            v.y = h + 1 < H ? src[1] : 0.f;
-                            v.z = h + 2 < H ? src[2] : 0.f;
-                            v.w = h + 3 < H ? src[3] : 0.f;
-                        }
-                    }
-                    wsl[w][i][q4] = v;
-                }
-                __syncthreads();
-                const int g = g0 + wave;
-                if (g < H) {
-                    const uint16_t *qrow = Q + (((size_t)b * H + g) * T + tc) * D;
-                    for (int i0 = 0; i0 < D; i0 += 8) {
-                        const uint4 raw = *reinterpret_cast<const uint4 *>(qrow + i0);
-                        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float qv = (e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1]);
-#pragma unroll
-                            for (int q4 = 0; q4 < kTauHeads / 4; ++q4) {
-                                const float4 wv = wsl[wave][i0 + e][q4];
-                                acc[4 * q4] = fmaf(qv, wv.x, acc[4 * q4]);
-                                acc[4 * q4 + 1] = fmaf(qv, wv.y, acc[4 * q4 + 1]);
-                                acc[4 * q4 + 2] = fmaf(qv, wv.z, acc[4 * q4 + 2]);
-                                acc[4 * q4 + 3] = fmaf(qv, wv.w, acc[4 * q4 + 3]);
-                            }
-                        }
-                    }
+            for (int g = wave; g < H; g += kTauWaves) {
+                const uint16_t *qrow = Q + (((size_t)b * H + g) * T + tc) * D;
+                const float *wg = W + (size_t)g * D * H + h0;
+                if (full) {
+                    tau_rows<D, true>(qrow, wg, H, nh, acc);
+                } else {
+                    tau_rows<D, false>(qrow, wg, H, nh, acc);
                 }
             }
         }
 #pragma unroll
         for (int k = 0; k < kTauHeads; ++k) part[wave][k][lane] = acc[k];
         __syncthreads();
-        if (wave == 0 && tok < T) {
+        if (wave < nh && tok < T) {
+            float sum = part[0][wave][lane];
 #pragma unroll
-            for (int k = 0; k < kTauHeads; ++k) {
-                if (h0 + k < H) {
-                    const float sum = ((part[0][k][lane] + part[1][k][lane]) + part[2][k][lane]) +
-                                      part[3][k][lane];
-                    tau[((size_t)b * H + h0 + k) * T + tok] = bias[h0 + k] + sum;
-                }
-            }
+            for (int w = 1; w < kTauWaves; ++w) sum += part[w][wave][lane];
+            tau[((size_t)b * H + h0 + wave) * T + tok] = bias[h0 + wave] + sum;
         }
         __syncthreads();  // part is rewritten by the next pass
     }
@@ -566,14 +565,14 @@ hipError_t launch_prefill_tau(const PrefillGeometry &g, const void *Q, const flo
                               const float *bias, float *tau, hipStream_t st) {
     if (g.T_q == 0) return hipSuccess;
     const dim3 grid((unsigned)((g.T_q + kTauTokens - 1) / kTauTokens), (unsigned)g.B);
-    // float4 slices of W rows need 16-byte aligned rows
-    const int vec = (g.H % 4 == 0 && (reinterpret_cast<uintptr_t>(W) % 16) == 0) ? 1 : 0;
+    // 16-byte rows of W for the four-column loads: H a multiple of 4, W 16-byte aligned
+    const int wvec = (g.H % 4 == 0 && (reinterpret_cast<uintptr_t>(W) % 16) == 0) ? 1 : 0;
     if (g.d == 128) {
         hipLaunchKernelGGL((prefill_tau_kernel<128>), grid, dim3(kTauWaves * kWave), 0, st,
-                           static_cast<const uint16_t *>(Q), W, bias, tau, g.H, g.T_q, vec);
+                           static_cast<const uint16_t *>(Q), W, bias, tau, g.H, g.T_q, wvec);
     } else {
         hipLaunchKernelGGL((prefill_tau_kernel<64>), grid, dim3(kTauWaves * kWave), 0, st,
-                           static_cast<const uint16_t *>(Q), W, bias, tau, g.H, g.T_q, vec);
+                           static_cast<const uint16_t *>(Q), W, bias, tau, g.H, g.T_q, wvec);
     }
     return hipGetLastError();
 }
