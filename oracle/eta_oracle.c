@@ -142,6 +142,61 @@ void eta_oracle_bounds(int nblk, int d, const float *q_unit, const double *centr
     }
 }
 
+/* Centroid-relative geometric bound (abstract: cached geometric bounds; review
+ * "Summary": centroid and max-norm metadata), the reading of "max-norm" as the
+ * largest distance of a block's keys from its centroid.
+ * Per block: the centroid c is the mean key (first pass), then
+ *   maxdev = max over the block's tokens of |k - c|      (second pass).
+ * Same block ranges as eta_oracle_block_meta. */
+int eta_oracle_block_maxdev(int T, int d, int bs, int kv_dtype, const void *K, double *maxdev) {
+    int nblk = (T + bs - 1) / bs;
+    double *c = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int blk = 0; blk < nblk; ++blk) {
+        long t0 = (long)blk * bs;
+        long t1 = t0 + bs;
+        if (t1 > T) t1 = T;
+        double n = (double)(t1 - t0);
+        for (int i = 0; i < d; ++i) c[i] = 0.0;
+        for (long t = t0; t < t1; ++t)
+            for (int i = 0; i < d; ++i) c[i] += kv_at(K, kv_dtype, d, t, i);
+        for (int i = 0; i < d; ++i) c[i] /= n;
+        double best = 0.0;
+        for (long t = t0; t < t1; ++t) {
+            double dist2 = 0.0;
+            for (int i = 0; i < d; ++i) {
+                double dev = kv_at(K, kv_dtype, d, t, i) - c[i];
+                dist2 += dev * dev;
+            }
+            double dist = sqrt(dist2);
+            if (dist > best) best = dist;
+        }
+        maxdev[blk] = best;
+    }
+    free(c);
+    return nblk;
+}
+
+/* The centered bound: every key k of the block has q.k = q.c + q.(k - c) <=
+ * q.c + |q| * |k - c| (Cauchy-Schwarz), so
+ *   U_cen = s * (q.c + |q| * maxdev)
+ * is never below the block's best score; it is taken together with the
+ * max-norm bound, U = min(U_geo, U_cen), and like U_geo alone it can miss no
+ * block whose best key reaches tau. */
+void eta_oracle_bounds_centered(int nblk, int d, const float *q_unit, const double *centroid,
+                                const double *maxnorm, const double *maxdev, double *U) {
+    double s = 1.0 / sqrt((double)d);
+    double qn2 = 0.0;
+    for (int i = 0; i < d; ++i) qn2 += (double)q_unit[i] * (double)q_unit[i];
+    double qn = sqrt(qn2);
+    for (int blk = 0; blk < nblk; ++blk) {
+        double u_geo = s * qn * maxnorm[blk];
+        double qc = 0.0;
+        for (int i = 0; i < d; ++i) qc += (double)q_unit[i] * centroid[(long)blk * d + i];
+        double u_cen = s * (qc + qn * maxdev[blk]);
+        U[blk] = (u_cen < u_geo) ? u_cen : u_geo;
+    }
+}
+
 /* Hard skip (Q&A "What is ETA?"): a block whose bound is below tau is not
  * loaded at all. Reading: admit iff U >= tau (a tie is kept); NaN admits
  * nothing. The list is ascending. */

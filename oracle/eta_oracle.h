@@ -51,6 +51,15 @@ void eta_oracle_bounds(int nblk, int d, const float *q_unit, const double *centr
                        const double *var, const double *maxnorm, double z, int mode,
                        double *U);
 
+/* Largest distance of a block's keys from the block's centroid, per block (two
+ * passes: centroid, then max |k - centroid|). Returns nblk. */
+int eta_oracle_block_maxdev(int T, int d, int bs, int kv_dtype, const void *K, double *maxdev);
+
+/* Centered bound: min(s*|q|*maxnorm, s*(q.centroid + |q|*maxdev)), both sides
+ * guaranteed (Cauchy-Schwarz about the origin and about the centroid). */
+void eta_oracle_bounds_centered(int nblk, int d, const float *q_unit, const double *centroid,
+                                const double *maxnorm, const double *maxdev, double *U);
+
 /* Admission: block b is admitted iff U[b] >= tau. Writes the admitted block
  * ids in ascending order to idx (room for nblk) and returns their count. */
 int eta_oracle_screen(int nblk, const double *U, double tau, int32_t *idx);

@@ -68,6 +68,12 @@ class OracleLib:
         L.eta_oracle_bounds.restype = None
         L.eta_oracle_bounds.argtypes = [ctypes.c_int, ctypes.c_int, _fp, _dp, _dp, _dp,
                                         ctypes.c_double, ctypes.c_int, _dp]
+        L.eta_oracle_block_maxdev.restype = ctypes.c_int
+        L.eta_oracle_block_maxdev.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _vp, _dp]
+        L.eta_oracle_bounds_centered.restype = None
+        L.eta_oracle_bounds_centered.argtypes = [ctypes.c_int, ctypes.c_int, _fp, _dp, _dp, _dp,
+                                                 _dp]
         L.eta_oracle_screen.restype = ctypes.c_int
         L.eta_oracle_screen.argtypes = [ctypes.c_int, _dp, ctypes.c_double, _ip]
         L.eta_oracle_union.restype = ctypes.c_int
@@ -128,6 +134,31 @@ class OracleLib:
         self.L.eta_oracle_bounds(nblk, d, q.ctypes.data_as(_fp), centroid.ctypes.data_as(_dp),
                                  var.ctypes.data_as(_dp), maxnorm.ctypes.data_as(_dp),
                                  float(z), int(mode), U.ctypes.data_as(_dp))
+        return U[:nblk]
+
+    def block_maxdev(self, K, T: int, bs: int = 64) -> np.ndarray:
+        """K [T_cap,d] (float32, or uint16 bf16 bits) -> per block, the largest
+        distance of a key from the block's centroid [nblk]."""
+        K, kvd = _kv(K)
+        d = K.shape[1]
+        assert 0 <= T <= K.shape[0]
+        nblk = (T + bs - 1) // bs
+        out = np.empty(max(nblk, 1), dtype=np.float64)
+        self.L.eta_oracle_block_maxdev(T, d, bs, kvd, K.ctypes.data, out.ctypes.data_as(_dp))
+        return out[:nblk]
+
+    def bounds_centered(self, q, centroid, maxnorm, maxdev) -> np.ndarray:
+        """min(s|q|maxnorm, s(q.c + |q| maxdev)) per block."""
+        q = _c(q, np.float32)
+        centroid = _c(centroid, np.float64)
+        maxnorm = _c(maxnorm, np.float64)
+        maxdev = _c(maxdev, np.float64)
+        nblk, d = centroid.shape
+        U = np.empty(max(nblk, 1), dtype=np.float64)
+        self.L.eta_oracle_bounds_centered(nblk, d, q.ctypes.data_as(_fp),
+                                          centroid.ctypes.data_as(_dp),
+                                          maxnorm.ctypes.data_as(_dp),
+                                          maxdev.ctypes.data_as(_dp), U.ctypes.data_as(_dp))
         return U[:nblk]
 
     def screen(self, U, tau: float) -> np.ndarray:

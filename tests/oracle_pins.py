@@ -256,6 +256,76 @@ def check_bound_worked_example(O):
         np.testing.assert_allclose(U[0], want, rtol=0, atol=1e-14, err_msg=str((q, z, mode)))
 
 
+def check_maxdev_library(O):
+    """Largest distance from the centroid against numpy (mean, then the row norms of
+    the deviations), with a ragged last block and bf16 input."""
+    rng = np.random.default_rng(31)
+    d, T = 24, 3 * 64 + 11
+    K = (rng.standard_normal((T + 5, d)) * 2.0).astype(np.float32)
+    md = O.block_maxdev(K, T)
+    assert md.shape == (4,)
+    for blk in range(4):
+        X = K[blk * 64:min(T, blk * 64 + 64)].astype(np.float64)
+        want = np.max(np.linalg.norm(X - X.mean(axis=0), axis=1))
+        np.testing.assert_allclose(md[blk], want, rtol=1e-13)
+    Kb = f32_to_bf16_bits(K)
+    mdb = O.block_maxdev(Kb, T)
+    X = bf16_bits_to_f64(Kb[:64])
+    np.testing.assert_allclose(mdb[0], np.max(np.linalg.norm(X - X.mean(axis=0), axis=1)),
+                               rtol=1e-13)
+
+
+def check_bound_centered_guarantee(O):
+    """Centered bound: brute force -- no key scores above min(U_geo, U_cen), so the
+    screen keeps every block holding a key that reaches tau; never above U_geo; a
+    one-token block bounds to its key's exact score; a block whose farthest key
+    lies from the centroid along q is bounded exactly by that key."""
+    rng = np.random.default_rng(32)
+    d, nblk = 16, 12
+    K = _clustered(rng, nblk, d, sigma=0.4)
+    K[7 * 64 + 40] = 5.0 * rng.standard_normal(d)  # an outlier (a needle-like key)
+    c, v, m = O.block_meta(K, nblk * 64)
+    md = O.block_maxdev(K, nblk * 64)
+    for trial in range(20):
+        q = (rng.standard_normal(d) * (1 + trial % 3)).astype(np.float32)
+        U = O.bounds_centered(q, c, m, md)
+        Ug = O.bounds(q, c, v, m, mode=1)
+        assert np.all(U <= Ug)
+        for blk in range(nblk):
+            S, _ = _scores(q, K, [blk], nblk * 64)
+            assert S.max() <= U[blk] + 1e-12, (trial, blk)
+            assert blk in O.screen(U, float(S.max()) - 1e-9)
+    q = rng.standard_normal(d).astype(np.float32)
+    c1, _, m1 = O.block_meta(K, 1)
+    U = O.bounds_centered(q, c1, m1, O.block_maxdev(K, 1))
+    S, _ = _scores(q, K, [0], 1)
+    np.testing.assert_allclose(U[0], S[0], rtol=0, atol=1e-13)
+    base = rng.standard_normal(d)
+    qh = q.astype(np.float64) / np.linalg.norm(q.astype(np.float64))
+    K2 = np.stack([base + 1.5 * qh, base - 1.5 * qh, base]).astype(np.float32)
+    c2, v2, m2 = O.block_meta(K2, 3)
+    U = O.bounds_centered(q, c2, m2, O.block_maxdev(K2, 3))
+    S, _ = _scores(q, K2, [0], 3)
+    np.testing.assert_allclose(U[0], min(S.max(), O.bounds(q, c2, v2, m2, mode=1)[0]),
+                               rtol=0, atol=1e-6)
+
+
+def check_bound_centered_worked_example(O):
+    """Hand-worked d=2 block {(2,1), (0,1)}: centroid (1,1), both keys at distance 1
+    from it, max-norm sqrt(5), s = 1/sqrt(2). q = (1,0): U_cen = (1 + 1)/sqrt(2) =
+    sqrt(2), the score of (2,1) exactly, below U_geo = sqrt(5/2); q = (0,-2): U_cen =
+    (-2 + 2)/sqrt(2) = 0; q = (3,0): U_cen = (3 + 3)/sqrt(2), U_geo = 3 sqrt(5/2),
+    the smaller is U_cen."""
+    K = np.array([[2.0, 1.0], [0.0, 1.0]], np.float32)
+    c, _, m = O.block_meta(K, 2)
+    md = O.block_maxdev(K, 2)
+    np.testing.assert_allclose(md[0], 1.0, rtol=0, atol=1e-15)
+    r2 = math.sqrt(2.0)
+    for q, want in [((1.0, 0.0), r2), ((0.0, -2.0), 0.0), ((3.0, 0.0), 6.0 / r2)]:
+        U = O.bounds_centered(np.array(q, np.float32), c, m, md)
+        np.testing.assert_allclose(U[0], want, rtol=0, atol=1e-14, err_msg=str(q))
+
+
 # ----------------------------------------------------------------------------------------
 # Screen
 # ----------------------------------------------------------------------------------------

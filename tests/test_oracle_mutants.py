@@ -57,6 +57,13 @@ MUTANTS = [
     ("gate_sum_unscaled", "gs += eta_oracle_gate(s * dot, tau[t], gate_beta, gate_hard);",
      "gs += eta_oracle_gate(dot, tau[t], gate_beta, gate_hard);"),
     ("union_skips_first_head", "for (int j = 0; j < g && !hit; ++j)", "for (int j = 1; j < g && !hit; ++j)"),
+    ("maxdev_from_origin", "double dev = kv_at(K, kv_dtype, d, t, i) - c[i];",
+     "double dev = kv_at(K, kv_dtype, d, t, i);"),
+    ("maxdev_squared", "double dist = sqrt(dist2);", "double dist = dist2;"),
+    ("centered_drops_qnorm", "double u_cen = s * (qc + qn * maxdev[blk]);",
+     "double u_cen = s * (qc + maxdev[blk]);"),
+    ("centered_minus", "qc + qn * maxdev[blk]", "qc - qn * maxdev[blk]"),
+    ("centered_takes_max", "(u_cen < u_geo) ? u_cen : u_geo", "(u_cen > u_geo) ? u_cen : u_geo"),
 ]
 
 
