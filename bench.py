@@ -515,7 +515,8 @@ def bias_by_bisection(step, data, w, meta, W, lens, target, iters=32):
     return torch.full((w.H,), 0.5 * (lo + hi), dtype=torch.float32, device="cuda")
 
 
-def screen_frontier(step, data, w, meta, W, bias, params, lens, steps, fused):
+def screen_frontier(step, data, w, meta, W, bias, params, lens, steps, fused, K0=None,
+                    layout=None):
     """What the screen's bound costs and keeps, beyond the default z = 4: for the
     combined bound at several z and for the max-norm (GEO) bound alone, the admitted
     density, the step time (median of `steps`), the planted-needle block recall and
@@ -524,7 +525,10 @@ def screen_frontier(step, data, w, meta, W, bias, params, lens, steps, fused):
     "density_held" re-calibrates the bias by bisection on the screen so that every
     setting admits the workload's target density (what the bound's ranking keeps at
     equal cost). z = sqrt(63 * d) is Samuelson's bound for 64-token blocks: with it
-    the combined bound is never below a full block's best score."""
+    the combined bound is never below a full block's best score. The centered bound
+    (the largest key distance from the block centroid, also a guarantee) is measured
+    in both families too, after a metadata build that adds those distances (its
+    time is reported)."""
     if W is None or w.static_tau:
         return None
     rows_nblk = np.array([max((t + 63) // 64, 1) for t in lens], dtype=np.float64)
@@ -537,7 +541,8 @@ def screen_frontier(step, data, w, meta, W, bias, params, lens, steps, fused):
         cnt = step.adm_cnt.cpu().numpy()
         ucnt = step.uni_cnt.cpu().numpy()
         miss = screen_misses(step, data, w, lens)
-        pt = {"bound": "geo" if mode == 1 else "combined", "z": None if mode == 1 else z,
+        pt = {"bound": {0: "combined", 1: "geo", 2: "centered"}[mode],
+              "z": z if mode == 0 else None,
               "bias": float(b[0]),
               "density": float((cnt / rows_nblk[:, None]).mean()),
               "loaded_density": float((ucnt / rows_nblk[:, None]).mean()),
@@ -550,16 +555,29 @@ def screen_frontier(step, data, w, meta, W, bias, params, lens, steps, fused):
         return pt
 
     out = {"tau_fixed": [], "density_held": [], "samuelson_z": sam}
+    centered = K0 is not None
     try:
-        for z, mode in [(2.0, 0), (4.0, 0), (6.0, 0), (8.0, 0), (16.0, 0), (z0, 1)]:
+        if centered:  # the distances from the centroid, built once for both families
+            meta.maxdev2 = torch.empty_like(meta.var)
+            _lib.eta_build_block_meta(K0, w.T, meta, layout=layout)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                _lib.eta_build_block_meta(K0, w.T, meta, layout=layout)
+            e1.record()
+            torch.cuda.synchronize()
+            out["centered_meta_build_ms"] = e0.elapsed_time(e1) / 3
+        for z, mode in [(2.0, 0), (4.0, 0), (6.0, 0), (8.0, 0), (16.0, 0), (z0, 1)] + \
+                ([(z0, 2)] if centered else []):
             out["tau_fixed"].append(measure(z, mode, bias))
         for z, mode in [(2.0, 0), (4.0, 0), (8.0, 0), (16.0, 0), (32.0, 0), (64.0, 0),
-                        (sam, 0), (z0, 1)]:
+                        (sam, 0), (z0, 1)] + ([(z0, 2)] if centered else []):
             step.params.z, step.params.bound_mode = z, mode
             b = bias_by_bisection(step, data, w, meta, W, lens, w.density)
             out["density_held"].append(measure(z, mode, b))
     finally:
         step.params.z, step.params.bound_mode = z0, mode0
+        meta.maxdev2 = None
     return out
 
 
@@ -886,7 +904,7 @@ def main():
 
     if not args.no_frontier:
         extra["screen_frontier"] = screen_frontier(step, data, w, meta, W, bias, params, lens,
-                                                   10, fused)
+                                                   10, fused, K0=K0, layout=layout)
 
     if not args.no_dense:
         dense_bias = torch.full((w.H,), -math.inf, device="cuda")

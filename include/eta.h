@@ -88,6 +88,7 @@ typedef enum { ETA_F32 = 0, ETA_BF16 = 1, ETA_DTYPE_MAX_ENUM = 0x7fffffff } eta_
 typedef enum {
     ETA_BOUND_COMBINED = 0,
     ETA_BOUND_GEO = 1,
+    ETA_BOUND_CENTERED = 2,  /* needs eta_meta.maxdev2                          */
     ETA_BOUND_MAX_ENUM = 0x7fffffff
 } eta_bound_mode;
 
@@ -138,8 +139,12 @@ typedef struct {
     float *centroid;    /* [B][H][d][nblk_cap]                                 */
     float *var;         /* [B][H][nblk_cap]                                    */
     float *maxnorm;     /* [B][H][nblk_cap]                                    */
-    int nblk_cap;       /* must equal eta_nblk_cap(T_cap); the three pointers
-                           are 16-byte aligned                                 */
+    int nblk_cap;       /* must equal eta_nblk_cap(T_cap); the pointers are
+                           16-byte aligned                                     */
+    float *maxdev2;     /* [B][H][nblk_cap] or NULL: the largest squared
+                           distance of a block's keys from its centroid,
+                           written by the build and append when not NULL and
+                           read by ETA_BOUND_CENTERED                         */
 } eta_meta;
 
 typedef struct {
@@ -213,7 +218,11 @@ eta_status eta_predict_tau(int B, int H, int d, const float *q, const float *W,
  * can reach tau is skipped). With s = 1/sqrt(d), per block:
  *   U_geo  = s * |q| * maxnorm                        (Cauchy-Schwarz)
  *   U_prob = s * (q . centroid + z * |q| * sqrt(var)) (centroid + z std devs)
- *   U = min(U_geo, U_prob)  (ETA_BOUND_COMBINED)  or  U_geo (ETA_BOUND_GEO)
+ *   U_cen  = s * (q . centroid + |q| * sqrt(maxdev2)) (Cauchy-Schwarz about
+ *                                                      the centroid)
+ *   U = min(U_geo, U_prob)  (ETA_BOUND_COMBINED),  U_geo (ETA_BOUND_GEO), or
+ *   min(U_geo, U_cen) (ETA_BOUND_CENTERED: like U_geo it never skips a block
+ *   holding a key that reaches tau; z is not used; m->maxdev2 must be set).
  * Block beta < ceil(T/64) is admitted iff U >= tau[b][h] (a NaN tau admits
  * nothing). Writes the admitted ids in ascending order to adm_idx[u][0..cnt)
  * and cnt to adm_cnt[u]; entries past cnt are left untouched. bound_out

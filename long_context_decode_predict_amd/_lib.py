@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 from dataclasses import dataclass
+from typing import Optional
 
 import torch
 
@@ -26,6 +27,7 @@ ETA_F32 = 0
 ETA_BF16 = 1
 ETA_BOUND_COMBINED = 0
 ETA_BOUND_GEO = 1
+ETA_BOUND_CENTERED = 2
 BLOCK = 64
 
 
@@ -45,7 +47,8 @@ class eta_shape(ctypes.Structure):
 
 class eta_meta(ctypes.Structure):
     _fields_ = [("centroid", ctypes.c_void_p), ("var", ctypes.c_void_p),
-                ("maxnorm", ctypes.c_void_p), ("nblk_cap", ctypes.c_int)]
+                ("maxnorm", ctypes.c_void_p), ("nblk_cap", ctypes.c_int),
+                ("maxdev2", ctypes.c_void_p)]
 
 
 class eta_prefill_shape(ctypes.Structure):
@@ -274,17 +277,21 @@ class Meta:
     var: torch.Tensor       # [B,H,nblk_cap] float32
     maxnorm: torch.Tensor   # [B,H,nblk_cap] float32
     nblk_cap: int
+    maxdev2: Optional[torch.Tensor] = None  # [B,H,nblk_cap] float32, for the centered bound
 
     @staticmethod
-    def alloc(B, H, d, T_cap, device="cuda") -> "Meta":
+    def alloc(B, H, d, T_cap, device="cuda", centered: bool = False) -> "Meta":
         n = nblk_cap(T_cap)
         return Meta(torch.empty((B, H, d, n), dtype=torch.float32, device=device),
                     torch.empty((B, H, n), dtype=torch.float32, device=device),
-                    torch.empty((B, H, n), dtype=torch.float32, device=device), n)
+                    torch.empty((B, H, n), dtype=torch.float32, device=device), n,
+                    torch.empty((B, H, n), dtype=torch.float32, device=device)
+                    if centered else None)
 
     def c(self) -> eta_meta:
         return eta_meta(self.centroid.data_ptr(), self.var.data_ptr(), self.maxnorm.data_ptr(),
-                        self.nblk_cap)
+                        self.nblk_cap,
+                        self.maxdev2.data_ptr() if self.maxdev2 is not None else None)
 
 
 def _check_meta(meta: Meta, B, H, d, T_cap):
@@ -292,6 +299,8 @@ def _check_meta(meta: Meta, B, H, d, T_cap):
     _need(meta.centroid, "centroid", torch.float32, (B, H, d, n))
     _need(meta.var, "var", torch.float32, (B, H, n))
     _need(meta.maxnorm, "maxnorm", torch.float32, (B, H, n))
+    if meta.maxdev2 is not None:
+        _need(meta.maxdev2, "maxdev2", torch.float32, (B, H, n))
 
 
 def _check_kv(K: torch.Tensor, name="K"):

@@ -45,6 +45,15 @@ def _bisect(f, target: float, lo=-50.0, hi=50.0, iters=200) -> float:
     return 0.5 * (lo + hi)
 
 
+def centered_z(d: int) -> float:
+    """The z at which the combined model above stands in for the centered bound
+    s (q.c + |q| max|k - c|): under the generator a block's largest key distance
+    from its centroid is about sigma (sqrt(d) + 1.7) (the largest of 64 norms of
+    N(0, sigma^2 I_d) noise, whose spread is about sigma / sqrt(2)), i.e. z ~=
+    sqrt(d) + 1.7 in-block standard deviations."""
+    return math.sqrt(d) + 1.7
+
+
 def bias_for(w: Workload, q: torch.Tensor, W, z: float = 4.0, device="cuda") -> torch.Tensor:
     """float32 [H] bias: frozen per-head thresholds for a workload without a predictor,
     else one predictor bias shared by all heads."""

@@ -66,8 +66,28 @@ eta_status check_meta(const eta_shape *s, const eta_meta *m) {
     if (m == nullptr || m->centroid == nullptr || m->var == nullptr || m->maxnorm == nullptr)
         return ETA_ERR_INVALID_ARG;
     if (m->nblk_cap != nblk_cap_of(s->T_cap)) return ETA_ERR_INVALID_ARG;
-    if (!aligned(m->centroid, 16) || !aligned(m->var, 16) || !aligned(m->maxnorm, 16))
+    if (!aligned(m->centroid, 16) || !aligned(m->var, 16) || !aligned(m->maxnorm, 16) ||
+        !aligned(m->maxdev2, 16))
         return ETA_ERR_INVALID_ARG;
+    return ETA_OK;
+}
+
+// What a screen call reads for the bound's second term: the centered bound is the
+// combined formula with z = 1 over the squared largest distance from the centroid
+// (s (q.c + |q| sqrt(maxdev2)), then the minimum with the max-norm bound).
+struct BoundInputs {
+    const float *spread;
+    float z;
+    bool geo_only;
+};
+
+eta_status bound_inputs(const eta_meta *m, const eta_params *p, BoundInputs *bi) {
+    if (p->bound_mode == ETA_BOUND_CENTERED) {
+        if (m->maxdev2 == nullptr) return ETA_ERR_INVALID_ARG;
+        *bi = {m->maxdev2, 1.0f, false};
+    } else {
+        *bi = {m->var, p->z, p->bound_mode == ETA_BOUND_GEO};
+    }
     return ETA_OK;
 }
 
@@ -103,7 +123,8 @@ eta_status check_params(const eta_params *p) {
     if (p == nullptr) return ETA_ERR_INVALID_ARG;
     if (!p->gate_hard && !(p->gate_beta > 0.f && isfinite(p->gate_beta))) return ETA_ERR_INVALID_ARG;
     if (!(p->z >= 0.f && isfinite(p->z))) return ETA_ERR_INVALID_ARG;
-    if (p->bound_mode != ETA_BOUND_COMBINED && p->bound_mode != ETA_BOUND_GEO)
+    if (p->bound_mode != ETA_BOUND_COMBINED && p->bound_mode != ETA_BOUND_GEO &&
+        p->bound_mode != ETA_BOUND_CENTERED)
         return ETA_ERR_INVALID_ARG;
     if (p->split_blocks < 0 || p->split_blocks > kMaxSplit) return ETA_ERR_INVALID_ARG;
     return ETA_OK;
@@ -245,7 +266,8 @@ eta_status eta_build_block_meta(const eta_shape *s, const void *K, const eta_met
     if ((st = check_meta(s, m)) != ETA_OK) return st;
     if (K == nullptr || !kv_aligned(s, K)) return ETA_ERR_INVALID_ARG;
     const eta::Geometry g = geometry(s, m->nblk_cap);
-    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, 0, g.nblk, 0, stream));
+    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, m->maxdev2, 0,
+                                           g.nblk, 0, stream));
 }
 
 eta_status eta_append_meta(const eta_shape *s, int n_new, const void *K, const eta_meta *m,
@@ -258,7 +280,8 @@ eta_status eta_append_meta(const eta_shape *s, int n_new, const void *K, const e
     // the layout keeps the lengths before the append; each row's blocks from the one
     // holding its first new token through the one holding its last are rebuilt
     const eta::Geometry g = geometry(s, m->nblk_cap);
-    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, 0, 0, n_new, stream));
+    return from_hip(eta::launch_block_meta(g, K, m->centroid, m->var, m->maxnorm, m->maxdev2, 0, 0,
+                                           n_new, stream));
 }
 
 eta_status eta_predict_tau(int B, int H, int d, const float *q, const float *W,
@@ -280,11 +303,12 @@ eta_status eta_screen(const eta_shape *s, const float *q, const float *tau, cons
     if (q == nullptr || tau == nullptr || adm_idx == nullptr || adm_cnt == nullptr)
         return ETA_ERR_INVALID_ARG;
     if (bound_out != nullptr && !aligned(bound_out, 16)) return ETA_ERR_INVALID_ARG;
+    BoundInputs bi;
+    if ((st = bound_inputs(m, p, &bi)) != ETA_OK) return st;
     const eta::Geometry g = geometry(s, m->nblk_cap);
     return from_hip(eta::launch_screen(g, s->H, q, const_cast<float *>(tau), nullptr, nullptr,
-                                       false, m->centroid, m->var, m->maxnorm, p->z,
-                                       p->bound_mode == ETA_BOUND_GEO, adm_idx, adm_cnt,
-                                       bound_out, stream));
+                                       false, m->centroid, bi.spread, m->maxnorm, bi.z,
+                                       bi.geo_only, adm_idx, adm_cnt, bound_out, stream));
 }
 
 eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W,
@@ -299,10 +323,12 @@ eta_status eta_predict_screen(const eta_shape *s, const float *q, const float *W
         adm_cnt == nullptr)
         return ETA_ERR_INVALID_ARG;
     if (bound_out != nullptr && !aligned(bound_out, 16)) return ETA_ERR_INVALID_ARG;
+    BoundInputs bi;
+    if ((st = bound_inputs(m, p, &bi)) != ETA_OK) return st;
     const eta::Geometry g = geometry(s, m->nblk_cap);
-    return from_hip(eta::launch_screen(g, s->H, q, tau, W, bias, true, m->centroid, m->var,
-                                       m->maxnorm, p->z, p->bound_mode == ETA_BOUND_GEO, adm_idx,
-                                       adm_cnt, bound_out, stream));
+    return from_hip(eta::launch_screen(g, s->H, q, tau, W, bias, true, m->centroid, bi.spread,
+                                       m->maxnorm, bi.z, bi.geo_only, adm_idx, adm_cnt, bound_out,
+                                       stream));
 }
 
 eta_status eta_predict_screen_union(const eta_shape *s, const float *q, const float *W,
@@ -319,10 +345,12 @@ eta_status eta_predict_screen_union(const eta_shape *s, const float *q, const fl
         return ETA_ERR_INVALID_ARG;
     if (kv_heads_of(s) == s->H) return ETA_ERR_INVALID_ARG;  // grouped heads only
     if (bound_out != nullptr && !aligned(bound_out, 16)) return ETA_ERR_INVALID_ARG;
+    BoundInputs bi;
+    if ((st = bound_inputs(m, p, &bi)) != ETA_OK) return st;
     const eta::Geometry g = geometry(s, m->nblk_cap);
-    return from_hip(eta::launch_screen(g, s->H, q, tau, W, bias, true, m->centroid, m->var,
-                                       m->maxnorm, p->z, p->bound_mode == ETA_BOUND_GEO, adm_idx,
-                                       adm_cnt, bound_out, stream, uni_idx, uni_cnt));
+    return from_hip(eta::launch_screen(g, s->H, q, tau, W, bias, true, m->centroid, bi.spread,
+                                       m->maxnorm, bi.z, bi.geo_only, adm_idx, adm_cnt, bound_out,
+                                       stream, uni_idx, uni_cnt));
 }
 
 eta_status eta_admit_union(const eta_shape *s, const int32_t *adm_idx, const int32_t *adm_cnt,

@@ -26,10 +26,11 @@ struct Geometry {
 
 // Metadata of blocks [blk_begin, blk_end) of every row (clipped to the row's
 // length); with n_new > 0, of the blocks each row's next n_new tokens touch
-// (the layout's lengths are then the lengths before those tokens).
+// (the layout's lengths are then the lengths before those tokens). maxdev2 may be
+// null (not computed).
 hipError_t launch_block_meta(const Geometry &g, const void *K, float *centroid, float *var,
-                             float *maxnorm, int blk_begin, int blk_end, int n_new,
-                             hipStream_t st);
+                             float *maxnorm, float *maxdev2, int blk_begin, int blk_end,
+                             int n_new, hipStream_t st);
 
 hipError_t launch_predict_tau(int B, int H, int d, const float *q, const float *W,
                               const float *bias, float *tau, hipStream_t st);

@@ -1,4 +1,5 @@
-// eta_meta.hip -- per-block key metadata (centroid, variance, max key norm).
+// eta_meta.hip -- per-block key metadata (centroid, variance, max key norm, and
+// optionally the largest squared key distance from the centroid).
 //
 // The cached block metadata is what makes the screen O(1) per block
 // (arXiv:2609.20888 abstract; evolve.pub review "Summary": centroid /
@@ -52,10 +53,13 @@ __device__ __forceinline__ float bcast_row0(float x) {
 
 // Statistics of the block at Kb (its first token row) holding n >= 1 tokens,
 // computed by the calling wave. cen: the lane's EPL centroid dimensions
-// (identical in all four rows); var and maxnorm are wave-uniform.
-template <typename KV, int D>
+// (identical in all four rows); var and maxnorm are wave-uniform. With DEV the
+// wave also returns maxdev2, the largest squared distance of a key from the
+// centroid, from a second pass over the rows still held in registers.
+template <typename KV, int D, bool DEV>
 __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
-                                            float (&cen)[D / 16], float &var, float &maxnorm) {
+                                            float (&cen)[D / 16], float &var, float &maxnorm,
+                                            float &maxdev2) {
     constexpr int EPL = D / 16;
     const int lane = threadIdx.x & (kWave - 1);
     const int row = lane >> 4;
@@ -103,6 +107,23 @@ __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
     m2 = row_sum16(m2);
     var = fmaxf(q - fn * m2, 0.f) / (fn * (float)D);
     maxnorm = sqrtf(xrow_max(nmax));
+    if (DEV) {
+        // rows past the end repeat token 0, whose distance is already among them
+        float dmax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float x[EPL];
+            ld[i].widen(x);
+            float dist2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const float dv = x[e] - cen[e];
+                dist2 = fmaf(dv, dv, dist2);
+            }
+            dmax = fmaxf(dmax, row_sum16(dist2));
+        }
+        maxdev2 = xrow_max(dmax);
+    }
 }
 
 // One workgroup per (key/value unit, group of 256 blocks). Build (n_new = 0):
@@ -110,15 +131,16 @@ __device__ __forceinline__ void block_stats(const KV *__restrict__ Kb, int n,
 // the blocks touched by tokens [T_b, T_b + n_new) of row b, counted from the
 // block holding token T_b. A block whose page id is out of range gets zero
 // metadata.
-template <typename KV, int D>
+template <typename KV, int D, bool DEV>
 __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
     const KV *__restrict__ K, float *__restrict__ centroid, float *__restrict__ var,
-    float *__restrict__ maxnorm, KVLayout lay, int nblk_cap, int blk_begin, int blk_end,
-    int n_new, int groups_per_unit) {
+    float *__restrict__ maxnorm, float *__restrict__ maxdev2, KVLayout lay, int nblk_cap,
+    int blk_begin, int blk_end, int n_new, int groups_per_unit) {
     constexpr int EPL = D / 16;
     __shared__ float tile_c[D][kMetaBlocksPerGroup + 1];  // +1: no bank conflicts
     __shared__ float tile_v[kMetaBlocksPerGroup];
     __shared__ float tile_m[kMetaBlocksPerGroup];
+    __shared__ float tile_d[DEV ? kMetaBlocksPerGroup : 1];
 
     const int u = blockIdx.x / groups_per_unit;
     const int grp = blockIdx.x - u * groups_per_unit;
@@ -142,10 +164,11 @@ __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
     for (int j = wave; j < count; j += kMetaWaves) {
         const int blk = first + j;
         float cen[EPL];
-        float v = 0.f, m = 0.f;
+        float v = 0.f, m = 0.f, dv2 = 0.f;
         const long long off = lay.block_offset(b, k, blk);
         if (off >= 0) {
-            block_stats<KV, D>(K + off, min(len - blk * kBlockTokens, kBlockTokens), cen, v, m);
+            block_stats<KV, D, DEV>(K + off, min(len - blk * kBlockTokens, kBlockTokens), cen, v,
+                                    m, dv2);
         } else {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) cen[e] = 0.f;
@@ -157,6 +180,7 @@ __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
         if (lane == 0) {
             tile_v[j] = v;
             tile_m[j] = m;
+            if (DEV) tile_d[j] = dv2;
         }
     }
     __syncthreads();
@@ -183,34 +207,41 @@ __global__ __launch_bounds__(kMetaWaves *kWave) void block_meta_kernel(
     for (int j = threadIdx.x; j < count; j += kMetaWaves * kWave) {
         __builtin_nontemporal_store(tile_v[j], var + (size_t)u * nblk_cap + first + j);
         __builtin_nontemporal_store(tile_m[j], maxnorm + (size_t)u * nblk_cap + first + j);
+        if (DEV) __builtin_nontemporal_store(tile_d[j], maxdev2 + (size_t)u * nblk_cap + first + j);
     }
 }
 
 template <typename KV, int D>
 hipError_t launch_meta_t(const Geometry &g, const void *K, float *c, float *v, float *m,
-                         int blk_begin, int blk_end, int n_new, hipStream_t st) {
+                         float *dev2, int blk_begin, int blk_end, int n_new, hipStream_t st) {
     // blocks per row: the range, or at most ceil(n_new / 64) + 1 for an append
     const int span = n_new > 0 ? (n_new + kBlockTokens - 1) / kBlockTokens + 1 : blk_end - blk_begin;
     const int groups = (span + kMetaBlocksPerGroup - 1) / kMetaBlocksPerGroup;
     const dim3 grid((unsigned)((long long)g.kv_units * groups));
-    hipLaunchKernelGGL((block_meta_kernel<KV, D>), grid, dim3(kMetaWaves * kWave), 0, st,
-                       static_cast<const KV *>(K), c, v, m, g.lay, g.nblk_cap, blk_begin, blk_end,
-                       n_new, groups);
+    if (dev2 != nullptr) {
+        hipLaunchKernelGGL((block_meta_kernel<KV, D, true>), grid, dim3(kMetaWaves * kWave), 0, st,
+                           static_cast<const KV *>(K), c, v, m, dev2, g.lay, g.nblk_cap, blk_begin,
+                           blk_end, n_new, groups);
+    } else {
+        hipLaunchKernelGGL((block_meta_kernel<KV, D, false>), grid, dim3(kMetaWaves * kWave), 0, st,
+                           static_cast<const KV *>(K), c, v, m, dev2, g.lay, g.nblk_cap, blk_begin,
+                           blk_end, n_new, groups);
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_block_meta(const Geometry &g, const void *K, float *centroid, float *var,
-                             float *maxnorm, int blk_begin, int blk_end, int n_new,
-                             hipStream_t st) {
+                             float *maxnorm, float *maxdev2, int blk_begin, int blk_end,
+                             int n_new, hipStream_t st) {
     if (g.kv_units == 0 || (n_new <= 0 && blk_end <= blk_begin)) return hipSuccess;
     if (g.bf16) {
-        return g.d == 128 ? launch_meta_t<uint16_t, 128>(g, K, centroid, var, maxnorm, blk_begin, blk_end, n_new, st)
-                          : launch_meta_t<uint16_t, 64>(g, K, centroid, var, maxnorm, blk_begin, blk_end, n_new, st);
+        return g.d == 128 ? launch_meta_t<uint16_t, 128>(g, K, centroid, var, maxnorm, maxdev2, blk_begin, blk_end, n_new, st)
+                          : launch_meta_t<uint16_t, 64>(g, K, centroid, var, maxnorm, maxdev2, blk_begin, blk_end, n_new, st);
     }
-    return g.d == 128 ? launch_meta_t<float, 128>(g, K, centroid, var, maxnorm, blk_begin, blk_end, n_new, st)
-                      : launch_meta_t<float, 64>(g, K, centroid, var, maxnorm, blk_begin, blk_end, n_new, st);
+    return g.d == 128 ? launch_meta_t<float, 128>(g, K, centroid, var, maxnorm, maxdev2, blk_begin, blk_end, n_new, st)
+                      : launch_meta_t<float, 64>(g, K, centroid, var, maxnorm, maxdev2, blk_begin, blk_end, n_new, st);
 }
 
 }  // namespace eta

@@ -57,7 +57,9 @@ class Case:
         if bias is not None:
             self.bias = bias.to("cuda", torch.float32)
         elif tau_mode in ("predictor", "static"):
-            self.bias = calibrate.bias_for(w, d["q"], d["W"], z=self.params.z)
+            z = (calibrate.centered_z(w.d) if self.params.bound_mode == _lib.ETA_BOUND_CENTERED
+                 else self.params.z)
+            self.bias = calibrate.bias_for(w, d["q"], d["W"], z=z)
         else:
             val = {"neg_inf": -math.inf, "pos_inf": math.inf, "nan": math.nan}[tau_mode]
             self.bias = torch.full((w.H,), val, dtype=torch.float32, device="cuda")
@@ -75,7 +77,8 @@ class Case:
                 table, d["Kp"], d["Vp"] = workloads.page_pool(
                     d["K"], d["V"], self.row_T or [self.T] * w.B, w.seed, all_blocks=all_pages)
             self.layout = _lib.KVLayout(lens, table)
-        self.meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, self.T_cap)
+        self.meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, self.T_cap,
+                                    centered=self.params.bound_mode == _lib.ETA_BOUND_CENTERED)
         self.step = DecodeStep(w.B, w.H, w.d, self.T_cap, w.kv_dtype, self.params,
                                with_bounds=True, H_kv=w.kv_heads, layout=self.layout)
 
@@ -106,7 +109,7 @@ class Case:
                 "uni_cnt": s.uni_cnt.cpu().numpy(), "out": s.out.cpu().numpy(),
                 "lse": s.lse.cpu().numpy(), "U": s.bounds.cpu().numpy(),
                 "centroid": self.meta.centroid, "var": self.meta.var,
-                "maxnorm": self.meta.maxnorm}
+                "maxnorm": self.meta.maxnorm, "maxdev2": self.meta.maxdev2}
 
     def free(self):
         for k in list(self.data):
@@ -136,12 +139,20 @@ def _check_unit(O, p, u, b, h, T, nblk, Kh, Vh, meta_g, qv, t, U_g, idx_g, out_g
     so units can be checked on a pool of threads: the oracle's C calls release
     the interpreter lock). Returns the unit's figures; raises on a mismatch."""
     c, v, m = O.block_meta(Kh, T)
+    centered = p.bound_mode == _lib.ETA_BOUND_CENTERED
+    md = O.block_maxdev(Kh, T) if centered else None
     if meta_g is not None:
-        cg, vg, mg = meta_g
+        cg, vg, mg = meta_g[:3]
         assert np.max(np.abs(cg - c)) <= 1e-5, (u, np.max(np.abs(cg - c)))
         assert np.all(np.abs(vg - v) <= 1e-5 * np.maximum(v, 1e-30) + 1e-12), u
         assert np.all(np.abs(mg - m) <= 1e-5 * m + 1e-12), u
-    U = O.bounds(qv, c, v, m, z=p.z, mode=p.bound_mode)
+        if centered:
+            # fp32 squared distances from the fp32 centroid: relative 1e-5 of the
+            # distance, or 1e-5 of the block's key norm when the distance is small
+            dg = np.sqrt(meta_g[3].astype(np.float64))
+            assert np.all(np.abs(dg - md) <= 1e-5 * md + 1e-5 * m + 1e-12), (u, np.max(np.abs(dg - md)))
+    U = (O.bounds_centered(qv, c, m, md) if centered
+         else O.bounds(qv, c, v, m, z=p.z, mode=p.bound_mode))
     assert np.all(np.abs(U_g - U) <= 1e-5 * np.maximum(1.0, np.abs(U))), (u, np.max(np.abs(U_g - U)))
     mask_o = U >= t
     mask_g = np.zeros(nblk, bool)
@@ -209,6 +220,8 @@ def compare_units(case: Case, units, O=None, check_meta=True, workers: int = 8):
                 meta_g = (g["centroid"][b, h, :, :nblk].cpu().numpy().T,
                           g["var"][b, h, :nblk].cpu().numpy(),
                           g["maxnorm"][b, h, :nblk].cpu().numpy())
+                if g["maxdev2"] is not None:
+                    meta_g += (g["maxdev2"][b, h, :nblk].cpu().numpy(),)
             cnt = int(g["cnt"][b, h])
             pending.append(pool.submit(
                 _check_unit, O, p, u, b, h, T, nblk, Kh, Vh, meta_g, q[b, h],
@@ -247,10 +260,12 @@ def compare_gqa_units(case: Case, kv_units, O=None):
         Kh = kv_host(case.data["K"][b, k])
         Vh = kv_host(case.data["V"][b, k])
         c, v, m = O.block_meta(Kh, T)
+        md = O.block_maxdev(Kh, T) if p.bound_mode == _lib.ETA_BOUND_CENTERED else None
         masks, outs = [], []
         for j in range(G):
             h = k * G + j
-            U = O.bounds(q[b, h], c, v, m, z=p.z, mode=p.bound_mode)
+            U = (O.bounds_centered(q[b, h], c, m, md) if md is not None
+                 else O.bounds(q[b, h], c, v, m, z=p.z, mode=p.bound_mode))
             Ug = g["U"][b, h, :nblk]
             assert np.all(np.abs(Ug - U) <= 1e-5 * np.maximum(1.0, np.abs(U)))
             t = float(tau_o[b, h])

@@ -119,11 +119,24 @@ def params(**kw):
 
 @pytest.mark.parametrize("kw", [dict(gate_beta=0.0), dict(gate_beta=float("inf")),
                                 dict(gate_beta=float("nan")), dict(z=-1.0), dict(z=float("inf")),
-                                dict(bound_mode=2), dict(split_blocks=-1),
+                                dict(bound_mode=3), dict(bound_mode=-1), dict(split_blocks=-1),
                                 dict(split_blocks=5000)])
 def test_screen_param_errors(L, kw):
     p = params(**kw)
     assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(meta()), BY(p), FAKE, FAKE, None, None) == INV
+
+
+def test_centered_bound_needs_distances(L):
+    """ETA_BOUND_CENTERED reads eta_meta.maxdev2: rejected before any launch when it is
+    NULL or not 16-byte aligned (the other modes ignore a NULL maxdev2)."""
+    p = BY(params(bound_mode=2))
+    assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(meta()), p, FAKE, FAKE, None, None) == INV
+    m = meta()
+    m.maxdev2 = FAKE + 4
+    assert L.eta_screen(BY(shape()), FAKE, FAKE, BY(m), p, FAKE, FAKE, None, None) == INV
+    assert L.eta_predict_screen(BY(shape()), FAKE, None, FAKE, BY(meta()), p, FAKE, FAKE, FAKE,
+                                None, None) == INV
+    assert L.eta_build_block_meta(BY(shape()), FAKE, BY(m), None) == INV
 
 
 def test_screen_other_errors(L):

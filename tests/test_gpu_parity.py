@@ -64,6 +64,13 @@ SMALL = [
                                         seed=18), "predictor", {"gate_hard": 1}, None),
     ("bf16_geo_bound", workloads.custom("r9", B=2, H=4, d=128, T=3000, kv_dtype=torch.bfloat16,
                                         seed=19), "predictor", {"bound_mode": 1}, None),
+    # the centered bound (largest key distance from the centroid): needles, a ragged
+    # tail and fp32 d = 64
+    ("bf16_centered_needles", workloads.custom("r17", B=2, H=4, d=128, T=8192 - 37,
+                                               kv_dtype=torch.bfloat16, needle_frac=0.02,
+                                               seed=28), "predictor", {"bound_mode": 2}, 8192),
+    ("f32_d64_centered", workloads.custom("r18", B=2, H=3, d=64, T=1000, kv_dtype=torch.float32,
+                                          seed=29), "predictor", {"bound_mode": 2}, 1088),
     ("bf16_beta1_z2", workloads.custom("r10", B=2, H=4, d=128, T=3000, kv_dtype=torch.bfloat16,
                                        seed=20), "predictor", {"gate_beta": 1.0, "z": 2.0}, None),
     ("bf16_dense_tau_neg_inf", workloads.custom("r11", B=2, H=4, d=128, T=2500,
@@ -133,7 +140,8 @@ def test_parity_needles_at_z16():
 
 FUSED = [c for c in SMALL if c[0] in ("tiny_config", "bf16_d128_ragged", "f32_d128_ragged",
                                       "bf16_static_heads", "bf16_two_screen_passes",
-                                      "bf16_geo_bound", "bf16_tau_nan", "f32_d64_many_units")]
+                                      "bf16_geo_bound", "bf16_tau_nan", "f32_d64_many_units",
+                                      "bf16_centered_needles")]
 
 
 @pytest.mark.parametrize("name,w,mode,pkw,T_cap", FUSED, ids=[c[0] for c in FUSED])
@@ -328,8 +336,9 @@ def test_append_equals_rebuild_bitwise(dtype, d):
     w = workloads.custom("ap", B=2, H=3, d=d, T=5000, kv_dtype=dtype, seed=51)
     data = workloads.generate(w, "cuda", T_cap=5120)
     K = data["K"]
-    built = _lib.Meta.alloc(w.B, w.H, d, 5120)
-    grown = _lib.Meta.alloc(w.B, w.H, d, 5120)
+    built = _lib.Meta.alloc(w.B, w.H, d, 5120, centered=True)
+    grown = _lib.Meta.alloc(w.B, w.H, d, 5120, centered=True)
+    plain = _lib.Meta.alloc(w.B, w.H, d, 5120)  # without the centroid distances
     T0 = 4000 - 7
     _lib.eta_build_block_meta(K, T0, grown)
     T = T0
@@ -337,11 +346,17 @@ def test_append_equals_rebuild_bitwise(dtype, d):
         _lib.eta_append_meta(K, T, n, grown)
         T += n
         _lib.eta_build_block_meta(K, T, built)
+        _lib.eta_build_block_meta(K, T, plain)
         nb = (T + 63) // 64
         torch.cuda.synchronize()
         assert torch.equal(built.centroid[..., :nb], grown.centroid[..., :nb]), T
         assert torch.equal(built.var[..., :nb], grown.var[..., :nb]), T
         assert torch.equal(built.maxnorm[..., :nb], grown.maxnorm[..., :nb]), T
+        assert torch.equal(built.maxdev2[..., :nb], grown.maxdev2[..., :nb]), T
+        # the distances' second pass leaves the other statistics as they are
+        assert torch.equal(built.centroid[..., :nb], plain.centroid[..., :nb]), T
+        assert torch.equal(built.var[..., :nb], plain.var[..., :nb]), T
+        assert torch.equal(built.maxnorm[..., :nb], plain.maxnorm[..., :nb]), T
     assert T == 5000
 
 
