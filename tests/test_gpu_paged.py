@@ -38,7 +38,8 @@ def _results(case):
     s = case.step
     return {"tau": s.tau, "cnt": s.adm_cnt, "idx": s.adm_idx, "ucnt": s.uni_cnt,
             "uidx": s.uni_idx, "out": s.out, "lse": s.lse, "U": s.bounds,
-            "c": case.meta.centroid, "v": case.meta.var, "m": case.meta.maxnorm}
+            "c": case.meta.centroid, "v": case.meta.var, "m": case.meta.maxnorm,
+            "d": case.meta.maxdev2}
 
 
 def _assert_same(a, b, case):
@@ -49,7 +50,7 @@ def _assert_same(a, b, case):
         nb = (case.row_len(bi) + 63) // 64
         for k in ("c",):
             assert torch.equal(a[k][bi, ..., :nb], b[k][bi, ..., :nb]), (k, bi)
-        for k in ("v", "m", "U"):
+        for k in ("v", "m", "U") + (("d",) if a["d"] is not None else ()):
             assert torch.equal(a[k][bi, :, :nb], b[k][bi, :, :nb]), (k, bi)
         for k, ck in (("idx", "cnt"), ("uidx", "ucnt")):
             for h in range(a[k].shape[1]):
@@ -67,6 +68,8 @@ MHA = [
      [3000, 129, 1500], {"split_blocks": 1, "gate_hard": 1}),
     ("bf16_d128_two_passes", dict(B=2, H=1, d=128, T=300_000, kv_dtype=torch.bfloat16,
                                   seed=204), [300_000, 170_001], {}),
+    ("bf16_d128_centered", dict(B=3, H=2, d=128, T=3000, kv_dtype=torch.bfloat16, seed=205),
+     [3000, 65, 1900], {"bound_mode": 2}),
 ]
 
 
@@ -84,7 +87,7 @@ def test_varlen_and_paged_parity(name, kw, lens, pkw, fused):
         if t == 0:  # an empty row attends to nothing
             assert torch.all(dense.step.adm_cnt[b] == 0)
             assert torch.all(dense.step.out[b] == 0) and torch.all(torch.isneginf(dense.step.lse[b]))
-    ref = {k: v.clone() for k, v in _results(dense).items()}
+    ref = {k: (v.clone() if v is not None else None) for k, v in _results(dense).items()}
     dense.free()
 
     _announce(f"paged {name}")
@@ -101,6 +104,8 @@ GQA = [
                               seed=212), [999, 1000, 1], {"gate_hard": 1}),
     ("g8_bf16_d64", dict(B=2, H=16, H_kv=2, d=64, T=2600, kv_dtype=torch.bfloat16,
                          group_corr=0.8, seed=213), [2600, 1900], {}),
+    ("g4_bf16_d128_centered", dict(B=2, H=8, H_kv=2, d=128, T=2000, kv_dtype=torch.bfloat16,
+                                   group_corr=0.9, seed=214), [2000, 700], {"bound_mode": 2}),
 ]
 
 
@@ -113,7 +118,7 @@ def test_grouped_varlen_and_paged_parity(name, kw, lens, pkw):
     st = compare_gqa_units(dense, range(w.B * w.kv_heads))
     assert st["kv_units"] == w.B * w.kv_heads
     assert st["band_mismatch_units"] <= 1, st
-    ref = {k: v.clone() for k, v in _results(dense).items()}
+    ref = {k: (v.clone() if v is not None else None) for k, v in _results(dense).items()}
     dense.free()
     paged = Case(w, params=params, seq_lens=lens, paged=True, fused=True).run()
     _assert_same(ref, _results(paged), paged)
@@ -230,7 +235,7 @@ def test_interleaved_pages_in_one_buffer(G):
                          seed=251 + G)
     lens = [5000, 1, 3333]
     case = Case(w, seq_lens=lens, paged=True, fused=True).run()
-    ref = {k: v.clone() for k, v in _results(case).items()}
+    ref = {k: (v.clone() if v is not None else None) for k, v in _results(case).items()}
     Kp, Vp = case.kv()
     P = Kp.shape[0]
     buf = torch.empty((2 * P + 1,) + tuple(Kp.shape[1:]), dtype=Kp.dtype, device="cuda")
@@ -264,7 +269,7 @@ def test_block_interleaved_dense_layout(name, kw, lens):
     _announce(f"block-interleaved {name}")
     w = workloads.custom(name, seed=261, **kw)
     case = Case(w, seq_lens=lens, fused=True).run()
-    ref = {k: v.clone() for k, v in _results(case).items()}
+    ref = {k: (v.clone() if v is not None else None) for k, v in _results(case).items()}
     K, V = case.data["K"], case.data["V"]
     B, Hk, Tc, d = K.shape
     nb = Tc // 64
@@ -313,7 +318,7 @@ def test_block_interleaved_page_pool(G, dtype):
                          seed=271 + G)
     lens = [4500, 65, 2000]
     case = Case(w, seq_lens=lens, paged=True, fused=True).run()
-    ref = {k: v.clone() for k, v in _results(case).items()}
+    ref = {k: (v.clone() if v is not None else None) for k, v in _results(case).items()}
     table, Kp, Vp = workloads.page_pool(case.data["K"], case.data["V"], lens, w.seed,
                                         interleaved=True)
     assert torch.equal(table, case.layout.page_table)

@@ -211,6 +211,8 @@ GQA = [
                               seed=104), "predictor", {}),
     ("g4_tau_neg_inf", dict(B=1, H=8, H_kv=2, d=128, T=2000, kv_dtype=torch.bfloat16, seed=98),
      "neg_inf", {}),
+    ("g4_bf16_d128_centered", dict(B=2, H=8, H_kv=2, d=128, T=3000, kv_dtype=torch.bfloat16,
+                                   group_corr=0.9, seed=105), "predictor", {"bound_mode": 2}),
     ("g4_tau_pos_inf", dict(B=1, H=8, H_kv=2, d=128, T=2000, kv_dtype=torch.bfloat16, seed=99),
      "pos_inf", {}),
 ]
