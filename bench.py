@@ -263,6 +263,9 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, lens, max_units=256, thr
     threads = threads or host_threads()
     with ThreadPoolExecutor(threads) as ex:
         metas = list(ex.map(lambda s: O.block_meta(s[2], s[2].shape[0]), slabs))
+        centered = params.bound_mode == _lib.ETA_BOUND_CENTERED
+        devs = (list(ex.map(lambda s: O.block_maxdev(s[2], s[2].shape[0]), slabs))
+                if centered else None)
         rows = sorted({s[0] for s in slabs})
         taus = {}
 
@@ -271,7 +274,11 @@ def cpu_baseline(w, data, W, bias, step_gpu_ms, params, lens, max_units=256, thr
             lists = []
             for j in range(G):
                 h = k * G + j
-                U = O.bounds(q[b, h], *metas[i], z=params.z, mode=params.bound_mode)
+                if centered:
+                    c, _, m = metas[i]
+                    U = O.bounds_centered(q[b, h], c, m, devs[i])
+                else:
+                    U = O.bounds(q[b, h], *metas[i], z=params.z, mode=params.bound_mode)
                 lists.append(O.screen(U, taus[b][h]))
             adm = lists[0] if G == 1 else O.union(lists, (Kh.shape[0] + 63) // 64)
             for j in range(G):
@@ -372,13 +379,21 @@ def screen_misses(step, data, w, lens, n_units=16):
             "rate": missed / reach if reach else 0.0, "sampled_query_heads": len(units)}
 
 
+def calib_z(params, w) -> float:
+    """The z the closed-form calibration takes for the step's bound."""
+    if params.bound_mode == _lib.ETA_BOUND_CENTERED:
+        return calibrate.centered_z(w.d)
+    return params.z
+
+
 def density_sweep(step, data, w, meta, W, params, lens, steps, fused):
     """Step time against the admitted fraction: the predictor bias is re-calibrated
     for each target density, everything else fixed."""
     rows_nblk = np.array([(t + 63) // 64 for t in lens], dtype=np.float64)
     out = []
     for rho in (0.05, 0.1, 0.2, 0.3, 0.4, 0.5, 0.6, 0.7, 0.8, 0.9):
-        bias = calibrate.bias_for(dataclasses.replace(w, density=rho), data["q"], W, z=params.z)
+        bias = calibrate.bias_for(dataclasses.replace(w, density=rho), data["q"], W,
+                                  z=calib_z(params, w))
         t = time_steps(step, data, w, meta, W, bias, steps, 2, fused)
         ms, attn_ms = t.ms, t.attn_ms
         cnt = step.adm_cnt.cpu().numpy()
@@ -556,9 +571,11 @@ def screen_frontier(step, data, w, meta, W, bias, params, lens, steps, fused, K0
 
     out = {"tau_fixed": [], "density_held": [], "samuelson_z": sam}
     centered = K0 is not None
+    own = meta.maxdev2 is None  # a run with the centered bound built them already
     try:
         if centered:  # the distances from the centroid, built once for both families
-            meta.maxdev2 = torch.empty_like(meta.var)
+            if own:
+                meta.maxdev2 = torch.empty_like(meta.var)
             _lib.eta_build_block_meta(K0, w.T, meta, layout=layout)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -577,7 +594,8 @@ def screen_frontier(step, data, w, meta, W, bias, params, lens, steps, fused, K0
             out["density_held"].append(measure(z, mode, b))
     finally:
         step.params.z, step.params.bound_mode = z0, mode0
-        meta.maxdev2 = None
+        if own:
+            meta.maxdev2 = None
     return out
 
 
@@ -757,6 +775,10 @@ def main():
                          "separate buffers / pools")
     ap.add_argument("--hard", action="store_true",
                     help="the hard gate (step at tau) instead of the sigmoid")
+    ap.add_argument("--bound", choices=("combined", "centered"), default="combined",
+                    help="the screen's bound: centroid score + z in-block standard deviations "
+                         "capped by the max-norm bound (default), or the bound about the "
+                         "block centroid (largest key distance from it; a guarantee)")
     ap.add_argument("--unfused", action="store_true",
                     help="separate eta_predict_tau + eta_screen launches instead of "
                          "eta_predict_screen")
@@ -779,13 +801,15 @@ def main():
         bench_prefill(args, workloads.PREFILL_WORKLOADS[args.workload])
         return
     w = workloads.WORKLOADS[args.workload]
-    params = _lib.default_params(split_blocks=args.split, gate_hard=1 if args.hard else 0)
+    params = _lib.default_params(split_blocks=args.split, gate_hard=1 if args.hard else 0,
+                                 bound_mode=_lib.ETA_BOUND_CENTERED if args.bound == "centered"
+                                 else _lib.ETA_BOUND_COMBINED)
 
     log(f"[bench] generating {w.name}: B={w.B} H={w.H} d={w.d} T={w.T} {w.kv_dtype}")
     t0 = time.time()
     data = workloads.generate(w, "cuda")
     W = data["W"]
-    bias = calibrate.bias_for(w, data["q"], W, z=params.z)
+    bias = calibrate.bias_for(w, data["q"], W, z=calib_z(params, w))
     lens = workloads.row_lengths(w)
     layout = None
     if w.var_len > 0 or w.paged:
@@ -806,7 +830,8 @@ def main():
     log(f"[bench] generated in {time.time() - t0:.1f}s")
     K0 = kv_of(data)[0]
 
-    meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, w.T_cap)
+    meta = _lib.Meta.alloc(w.B, w.kv_heads, w.d, w.T_cap,
+                           centered=params.bound_mode == _lib.ETA_BOUND_CENTERED)
     append_ms = None
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if w.append:
@@ -966,7 +991,9 @@ def main():
                    "kv_dtype": "bf16" if w.kv_dtype == torch.bfloat16 else "f32",
                    "block": 64, "target_density": w.density if not w.static_tau else "per-head",
                    "split_blocks": _lib.split_blocks(w.B, w.H, w.kv_heads, w.T_cap, params),
-                   "gate": "hard" if params.gate_hard else "sigmoid", "parallelism": "single GPU"},
+                   "gate": "hard" if params.gate_hard else "sigmoid",
+                   "bound": "centered" if params.bound_mode == _lib.ETA_BOUND_CENTERED
+                   else "combined z=%g" % params.z, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -125,6 +125,10 @@ class OracleLib:
 
     def bounds(self, q, centroid, var, maxnorm, z: float = 4.0,
                mode: int = BOUND_COMBINED) -> np.ndarray:
+        """The combined (mode 0) or max-norm (mode 1) bound per block; the centered
+        bound has its own call (bounds_centered)."""
+        if mode not in (BOUND_COMBINED, BOUND_GEO):
+            raise ValueError(f"bound mode {mode}: use bounds_centered for the centered bound")
         q = _c(q, np.float32)
         centroid = _c(centroid, np.float64)
         var = _c(var, np.float64)
